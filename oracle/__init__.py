@@ -1,0 +1,46 @@
+"""Plain fp64 CPU oracle for one GPU's share of Ring Attention.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or call anything in this package.  The HIP library never routes through
+it, and it imports nothing from the HIP side (no kernels, headers, tables or
+helpers are shared).
+
+What it computes, and the passage each function follows:
+
+* ``attention.attention_fwd`` -- exact softmax attention of query rows over the
+  unchunked key/value sequence.  Ring Attention is exact: after the walk every
+  query block has attended to the whole global sequence ("Training Long-Context
+  Models Without OOM: Ring Attention", section "Ring Attention Demystified",
+  item 5 "Ring Completion"; "Context Parallelism", section 2 "Ring Attention",
+  "How It Works").  The oracle therefore is the plain definition, not the ring.
+* ``attention.attention_bwd`` / ``attention_bwd_key_rows`` -- the textbook
+  gradient of softmax attention.  The pages give no backward formula; the
+  reading (recompute P from the final log-sum-exp) is listed in the design doc.
+* ``attention.lse_merge`` / ``ring_fwd_chunked`` -- the online-softmax merge of
+  partial results ("Training Long-Context Models Without OOM: Ring
+  Attention", "Ring Attention Demystified", paragraph on running softmax
+  statistics; "Context Parallelism", 2 "How It Works", last sentence).  Used by
+  the tests only to check invariants of the method, never as the expected
+  value of a GPU output.
+* ``schedule.ring_schedule`` -- which KV chunk a rank uses at each step
+  ("Context Parallelism", 2 "How It Works": step s uses K_{i-s}, V_{i-s};
+  "Training Long-Context Models Without OOM", "Ring Attention Demystified",
+  items 2-5).
+* ``schedule.kv_bytes_per_step`` -- KV rotation bytes ("Context Parallelism",
+  2 "Communication" and "Worked Example").
+
+Every function here is pinned by ``tests/test_oracle.py`` against something
+other than itself (a library routine, brute force, closed forms, invariants,
+or numbers the pages print).  No function is "parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    attention_fwd,
+    attention_bwd,
+    attention_bwd_key_rows,
+    lse_merge,
+    step_partial,
+    ring_fwd_chunked,
+)
+from .schedule import ring_schedule, kv_bytes_per_step, visible_pairs  # noqa: F401
