@@ -1,0 +1,185 @@
+/*
+ * ra.h -- one GPU's share of Ring Attention, hand-written HIP for MI355X
+ * (gfx950).  C ABI: plain pointers, sizes and status codes; no C++ or torch
+ * types cross it.
+ *
+ * The method.  The sequence is split into P equal contiguous chunks; the GPU
+ * of rank r keeps its query chunk Q_r while the key/value chunks travel round
+ * a ring.  At step s it computes exact attention of Q_r against chunk
+ * j = (r - s) mod P and folds the result into running softmax statistics, so
+ * after P - 1 rotations Q_r has attended to the whole sequence without the
+ * global score matrix ever being formed ("Training Long-Context Models
+ * Without OOM: Ring Attention", section "Ring Attention Demystified", items
+ * 1-5; "Context Parallelism", section 2 "Ring Attention", "How It Works").
+ * The per-step kernel is FlashAttention-style tiling: scores live only in
+ * on-chip tiles, with a running row maximum and running sum of exponentials
+ * (same section of the first page).  On one GPU the rotation is emulated: all
+ * P chunks are resident and the ring walk is a double-buffered copy into a
+ * two-slot staging area.
+ *
+ * Conventions shared by every entry point.
+ *   Layout: q, k, v, dO are bf16 [B, H, S, d] contiguous ("BHSD"), the
+ *     d values of one token adjacent.  o, o_partial, dq, dk, dv are fp32 in
+ *     the same layout; lse and lse_partial are fp32 [B, H, S].
+ *   lse is the natural logarithm of sum_k exp(scale * q . k_k) over the keys
+ *     a row has seen; o is normalised (the softmax-weighted mean of v).  A
+ *     row that has seen no key has o = 0 and lse = -inf.
+ *   d must be 64 or 128; B, H and every sequence length must be >= 1 (any
+ *     length: ragged tails are masked in the kernels).
+ *   Every device pointer must be 16-byte aligned.
+ *   Causality is over global positions with the diagonal included: query at
+ *     global position p sees key positions <= p.  Chunk j holds global
+ *     tokens [j*C, (j+1)*C).  So under causal masking chunk j < r is fully
+ *     visible to rank r, chunk r is lower-triangular, chunks j > r are
+ *     skipped.
+ *   stream / copy_stream: a hipStream_t passed as void* (NULL = the null
+ *     stream).  Work is enqueued asynchronously on it; device faults surface
+ *     at the caller's next synchronisation.
+ *   Ownership: the caller owns every buffer.  Hot calls allocate no device
+ *     memory; they only read and write the buffers passed in.
+ *   Errors: arguments are validated on the host before anything is
+ *     enqueued; on any non-zero status nothing has been enqueued, except
+ *     RA_ERR_HIP which reports a failed launch or runtime call (work
+ *     enqueued before it may still run).  ra_last_error() then holds a
+ *     message for the calling thread.  No C++ exception crosses the ABI.
+ *   Thread safety: calls on distinct streams may run concurrently.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RA_VERSION 1
+
+enum ra_status {
+  RA_OK = 0,
+  RA_ERR_NULL = 1,        /* a required pointer is NULL */
+  RA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  RA_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned */
+  RA_ERR_UNSUPPORTED = 4, /* d is not 64 or 128, or an unknown mode */
+  RA_ERR_RANK = 5,        /* rank outside [0, P) */
+  RA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
+  RA_ERR_HIP = 7          /* a HIP runtime call or launch failed */
+};
+
+enum ra_ring_mode {
+  RA_RING_RESIDENT = 0,     /* walk the resident chunks in ring order, no copies */
+  RA_RING_DOUBLE_BUFFER = 1 /* stage each chunk into a 2-slot buffer first (the
+                               emulated receive), overlapped with the previous
+                               step's compute when copy_stream is given */
+};
+
+/* Library version (RA_VERSION). */
+int ra_version(void);
+
+/* Human-readable name of a status code; never NULL. */
+const char* ra_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* ra_last_error(void);
+
+/*
+ * ra_step_fwd -- one ring step's attention partial.
+ *
+ * Exact attention of the query block q [B,H,Sq,d] against one KV chunk
+ * k, v [B,H,Sk,d] ("Context Parallelism", 2 "How It Works": at step s GPU i
+ * computes attention(Q_i, K_{i-s}, V_{i-s})).  Writes the normalised partial
+ * o_partial [B,H,Sq,d] and its log-sum-exp lse_partial [B,H,Sq] (both fp32,
+ * overwritten).  scale multiplies q . k before the softmax.
+ *
+ * The diagonal mask (local query t sees local keys <= t) applies iff
+ * causal != 0 and step == 0; that case needs Sq == Sk.  Every other call is
+ * unmasked: skipping chunks in the future of the query block is the
+ * caller's business (ra_ring_fwd does it).  step < 0 is RA_ERR_SHAPE.
+ */
+int ra_step_fwd(const void* q, const void* k, const void* v,
+                float* o_partial, float* lse_partial,
+                int B, int H, int Sq, int Sk, int d,
+                float scale, int step, int causal, void* stream);
+
+/*
+ * ra_lse_merge -- fold a partial into a running result, in place.
+ *
+ * With lse' = ln(e^lse + e^lse_p):
+ *   o <- e^(lse - lse') o + e^(lse_p - lse') o_partial,  lse <- lse'
+ * This is the online-softmax update that lets partial outputs against
+ * separate KV chunks be combined incrementally ("Training Long-Context Models
+ * Without OOM: Ring Attention", "Ring Attention Demystified"; "Context
+ * Parallelism", 2 "How It Works").  An operand with lse = -inf contributes
+ * nothing; both -inf leaves o = 0, lse = -inf.  o, o_partial [B,H,S,d],
+ * lse, lse_partial [B,H,S], fp32.  o/lse may not alias the partial.
+ */
+int ra_lse_merge(float* o, float* lse, const float* o_partial,
+                 const float* lse_partial, int B, int H, int S, int d,
+                 void* stream);
+
+/*
+ * Device workspace bytes ra_ring_fwd (bwd == 0) or ra_ring_bwd (bwd != 0)
+ * needs for these sizes.  Double-buffer forward: two slots of one K and one
+ * V chunk, 4 * B*H*C*d * 2 bytes.  Resident forward: 0.  Backward: the
+ * per-row term rowsum(dO * O), B*H*C * 4 bytes.  Returns 0 for invalid sizes.
+ */
+size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d,
+                               int ring_mode, int bwd);
+
+/*
+ * ra_ring_fwd -- rank `rank`'s whole ring walk, forward.
+ *
+ * q [B,H,C,d] is the local query chunk (global tokens [rank*C, (rank+1)*C)).
+ * k_chunks and v_chunks are HOST arrays of P device pointers, chunk j at
+ * index j, each [B,H,C,d] bf16.  Step s = 0..P-1 uses chunk
+ * j = (rank - s) mod P ("Context Parallelism", 2 "How It Works").  Under
+ * causal masking step 0 is the diagonal chunk and chunks j > rank are skipped
+ * (no copy, no launch).  Each visible step runs one kernel that computes the
+ * step's partial in on-chip tiles and merges it with the running (o, lse) in
+ * its epilogue, so only o and lse touch memory between steps.
+ * o [B,H,C,d] and lse [B,H,C] (fp32) are overwritten with the final result.
+ *
+ * ring_mode RA_RING_DOUBLE_BUFFER needs ra_ring_workspace_bytes(...) of
+ * workspace: the chunk of step s >= 1 is copied into slot (s-1) & 1 on
+ * copy_stream (or on stream when copy_stream is NULL) while step s-1
+ * computes, with events ordering slot reuse -- the stand-in for the ring's
+ * receive from the left neighbour ("Training Long-Context Models Without
+ * OOM: Ring Attention", "Ring Attention Demystified", items 3-4).
+ * RA_RING_RESIDENT reads the chunks in place and needs no workspace.
+ * When the call returns, all work is ordered on `stream` (copy_stream work
+ * is joined back into it).
+ */
+int ra_ring_fwd(const void* q, const void* const* k_chunks,
+                const void* const* v_chunks, int P, float* o, float* lse,
+                int rank, int causal, float scale, int B, int H, int C, int d,
+                int ring_mode, void* workspace, size_t workspace_bytes,
+                void* stream, void* copy_stream);
+
+/*
+ * ra_ring_bwd -- rank `rank`'s ring walk, backward.
+ *
+ * Gradient of L = sum(dO * o) for the o that ra_ring_fwd produced.  The pages
+ * give no backward; this is the textbook softmax-attention gradient with the
+ * probabilities recomputed from the final lse (no merge is needed):
+ *   P = exp(scale q k^T - lse), dV_j += P^T dO, dP = dO v_j^T,
+ *   D = rowsum(dO * o), dS = P (dP - D), dq += scale dS k_j,
+ *   dK_j += scale dS^T q.
+ * q, dO [B,H,C,d] bf16; o [B,H,C,d] and lse [B,H,C] fp32 from the forward;
+ * dq [B,H,C,d] fp32 is overwritten.  dk_chunks and dv_chunks are HOST arrays
+ * of P device pointers to fp32 [B,H,C,d] accumulators that are ADDED TO
+ * (the caller zeroes them once), so walking every rank's share accumulates
+ * the full-sequence gradient.  Skipped chunks are not touched.  workspace
+ * must hold ra_ring_workspace_bytes(P,B,H,C,d,0,1) bytes.
+ */
+int ra_ring_bwd(const void* q, const void* const* k_chunks,
+                const void* const* v_chunks, int P, const float* o,
+                const float* lse, const void* dO, float* dq,
+                float* const* dk_chunks, float* const* dv_chunks, int rank,
+                int causal, float scale, int B, int H, int C, int d,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

@@ -1,0 +1,185 @@
+"""One GPU's share of Ring Attention on MI355X (gfx950): Python binding.
+
+Thin ctypes marshalling over libra.so (include/ra.h).  Every step of the
+path runs in the library's HIP kernels; this module only turns torch tensors
+into device pointers and streams.  There is no fallback: if libra.so is
+missing, every call raises.
+
+    import long_context_exact_step_amd as ra
+    ra.ring_fwd(q, k_chunks, v_chunks, o, lse, rank=3, causal=True)
+"""
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "RAError", "lib", "version", "step_fwd", "lse_merge", "ring_fwd", "ring_bwd",
+    "workspace_bytes", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
+RING_RESIDENT = 0
+RING_DOUBLE_BUFFER = 1
+_MODES = {"resident": RING_RESIDENT, "double_buffer": RING_DOUBLE_BUFFER,
+          RING_RESIDENT: RING_RESIDENT, RING_DOUBLE_BUFFER: RING_DOUBLE_BUFFER}
+
+_lib = None
+
+
+class RAError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+        self.detail = detail
+
+
+def lib():
+    """The loaded libra.so (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m long_context_exact_step_amd.build` "
+                "(or __graft_entry__.build()) first. There is no CPU fallback.")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        vpp = ctypes.POINTER(ctypes.c_void_p)
+        L.ra_version.restype = i
+        L.ra_version.argtypes = []
+        L.ra_status_string.restype = ctypes.c_char_p
+        L.ra_status_string.argtypes = [i]
+        L.ra_last_error.restype = ctypes.c_char_p
+        L.ra_last_error.argtypes = []
+        L.ra_step_fwd.restype = i
+        L.ra_step_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.ra_lse_merge.restype = i
+        L.ra_lse_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+        L.ra_ring_workspace_bytes.restype = sz
+        L.ra_ring_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.ra_ring_fwd.restype = i
+        L.ra_ring_fwd.argtypes = [vp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, i, vp, sz, vp, vp]
+        L.ra_ring_bwd.restype = i
+        L.ra_ring_bwd.argtypes = [vp, vpp, vpp, i, vp, vp, vp, vp, vpp, vpp, i, i, f, i, i, i, i, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        L = lib()
+        raise RAError(status, f"{L.ra_status_string(status).decode()}: {L.ra_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))()
+    for n, t in enumerate(ts):
+        arr[n] = None if t is None else t.data_ptr()
+    return arr
+
+
+def _stream(stream, like):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(like.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if t.dim() != (3 if name.startswith("lse") else 4):
+        raise ValueError(f"{name}: wrong rank {t.dim()}")
+
+
+def version():
+    return lib().ra_version()
+
+
+def step_fwd(q, k, v, o_partial, lse_partial, step, causal, scale=None, stream=None):
+    """ra_step_fwd: one ring step's normalised partial and its lse."""
+    import torch
+    _need(q, torch.bfloat16, "q"); _need(k, torch.bfloat16, "k"); _need(v, torch.bfloat16, "v")
+    _need(o_partial, torch.float32, "o_partial"); _need(lse_partial, torch.float32, "lse_partial")
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().ra_step_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o_partial), _ptr(lse_partial),
+                             B, H, Sq, Sk, d, scale, int(step), int(bool(causal)), _stream(stream, q)))
+
+
+def lse_merge(o, lse, o_partial, lse_partial, stream=None):
+    """ra_lse_merge: fold (o_partial, lse_partial) into (o, lse) in place."""
+    import torch
+    for t, n in ((o, "o"), (o_partial, "o_partial")):
+        _need(t, torch.float32, n)
+    for t, n in ((lse, "lse"), (lse_partial, "lse_partial")):
+        _need(t, torch.float32, n)
+    B, H, S, d = o.shape
+    _check(lib().ra_lse_merge(_ptr(o), _ptr(lse), _ptr(o_partial), _ptr(lse_partial),
+                              B, H, S, d, _stream(stream, o)))
+
+
+def workspace_bytes(P, B, H, C, d, ring_mode="double_buffer", bwd=False):
+    return int(lib().ra_ring_workspace_bytes(P, B, H, C, d, _MODES[ring_mode], int(bool(bwd))))
+
+
+def ring_fwd(q, k_chunks, v_chunks, o, lse, rank, causal, scale=None, ring_mode="double_buffer",
+             workspace=None, stream=None, copy_stream=None):
+    """ra_ring_fwd: rank's whole ring walk; overwrites (o, lse).
+
+    workspace: a uint8 GPU tensor of at least workspace_bytes(...) bytes (only
+    for ring_mode "double_buffer"); allocated here if not given.
+    """
+    import torch
+    _need(q, torch.bfloat16, "q")
+    _need(o, torch.float32, "o")
+    _need(lse, torch.float32, "lse")
+    for n, t in enumerate(list(k_chunks) + list(v_chunks)):
+        _need(t, torch.bfloat16, f"chunk{n}")
+    B, H, C, d = q.shape
+    P = len(k_chunks)
+    mode = _MODES[ring_mode]
+    need = workspace_bytes(P, B, H, C, d, mode, False)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ka, va = _ptr_array(k_chunks), _ptr_array(v_chunks)
+    cs = None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+    _check(lib().ra_ring_fwd(_ptr(q), ka, va, P, _ptr(o), _ptr(lse), int(rank), int(bool(causal)), scale,
+                             B, H, C, d, mode, _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _stream(stream, q), cs))
+    return workspace
+
+
+def ring_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, causal, scale=None,
+             workspace=None, stream=None):
+    """ra_ring_bwd: rank's backward walk; dq overwritten, dk/dv chunks += ."""
+    import torch
+    _need(q, torch.bfloat16, "q"); _need(dO, torch.bfloat16, "dO")
+    _need(o, torch.float32, "o"); _need(lse, torch.float32, "lse"); _need(dq, torch.float32, "dq")
+    for n, t in enumerate(list(k_chunks) + list(v_chunks)):
+        _need(t, torch.bfloat16, f"chunk{n}")
+    for n, t in enumerate(list(dk_chunks) + list(dv_chunks)):
+        if t is not None:
+            _need(t, torch.float32, f"grad_chunk{n}")
+    B, H, C, d = q.shape
+    P = len(k_chunks)
+    need = workspace_bytes(P, B, H, C, d, "resident", True)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().ra_ring_bwd(_ptr(q), _ptr_array(k_chunks), _ptr_array(v_chunks), P, _ptr(o), _ptr(lse),
+                             _ptr(dO), _ptr(dq), _ptr_array(dk_chunks), _ptr_array(dv_chunks), int(rank),
+                             int(bool(causal)), scale, B, H, C, d, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream, q)))
+    return workspace

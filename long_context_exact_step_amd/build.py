@@ -1,0 +1,69 @@
+"""Builds libra.so (the HIP kernels and the C-ABI) in-tree for gfx950.
+
+    python -m long_context_exact_step_amd.build
+
+Each HIP source is compiled to an object under <repo>/_build/ in parallel and
+linked into long_context_exact_step_amd/libra.so.  Always rebuilds.
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libra.so")
+SOURCES = ["ra_api.hip", "ra_fwd.hip", "ra_merge.hip", "ra_bwd.hip"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    p = os.path.join(rocm, "bin", "hipcc")
+    return p if os.path.exists(p) else "hipcc"
+
+
+def common_flags(extra=()):
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        # No packed-fp32 VALU instructions in any kernel.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I" + INCLUDE, "-I" + CSRC, *extra,
+    ]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless.
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(verbose=False, extra_flags=(), out=LIB):
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([hipcc(), *common_flags(extra_flags), "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
+        for err in ex.map(_run, cmds):
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+    tmp = out + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, out)
+    if verbose:
+        print(f"built {out}", file=sys.stderr)
+    return out
+
+
+if __name__ == "__main__":
+    build(verbose=True)

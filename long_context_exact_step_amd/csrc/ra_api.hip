@@ -1,0 +1,292 @@
+// C-ABI of the ring-attention library: host-side validation, the ring walk
+// (schedule, causal skip, double-buffered staging of KV chunks) and kernel
+// dispatch.  See include/ra.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <vector>
+
+#include "ra.h"
+#include "ra_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return RA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Sizes of one [B, H, S, d] tensor must fit the kernels' 32-bit row indices
+// (rows = B*H*S) and size_t byte counts.
+int check_dims(int B, int H, int S, int d, const char* what) {
+  if (d != 64 && d != 128) return fail(RA_ERR_UNSUPPORTED, "%s: d=%d (supported: 64, 128)", what, d);
+  if (B < 1 || H < 1 || S < 1) return fail(RA_ERR_SHAPE, "%s: B=%d H=%d S=%d must all be >= 1", what, B, H, S);
+  const long long rows = (long long)B * H * S;
+  if (rows > 0x7fffffffLL) return fail(RA_ERR_SHAPE, "%s: B*H*S=%lld exceeds 2^31-1", what, rows);
+  return RA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// One visible ring step: which chunk, and whether it is the masked diagonal.
+struct Step {
+  int s, j;
+  bool diag;
+};
+
+// Step s of rank `rank` uses chunk j = (rank - s) mod P ("Context
+// Parallelism", 2 "How It Works"); under causal masking step 0 is the
+// diagonal chunk and chunks j > rank are skipped.
+std::vector<Step> visible_steps(int rank, int P, bool causal) {
+  std::vector<Step> out;
+  for (int s = 0; s < P; ++s) {
+    const int j = ((rank - s) % P + P) % P;
+    if (causal && s > 0 && j > rank) continue;
+    out.push_back(Step{s, j, causal && s == 0});
+  }
+  return out;
+}
+
+// Events for ordering slot reuse between the compute and copy streams,
+// created once per (thread, device) and reused.
+struct RingEvents {
+  int device = -1;
+  hipEvent_t start = nullptr, copied[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr};
+};
+thread_local RingEvents t_events;
+
+hipError_t ring_events(RingEvents** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  RingEvents& ev = t_events;
+  if (ev.device != dev) {
+    hipEvent_t* all[5] = {&ev.start, &ev.copied[0], &ev.copied[1], &ev.consumed[0], &ev.consumed[1]};
+    for (hipEvent_t* p : all) {
+      if (*p != nullptr && ev.device >= 0) (void)hipEventDestroy(*p);
+      *p = nullptr;
+      e = hipEventCreateWithFlags(p, hipEventDisableTiming);
+      if (e != hipSuccess) {
+        ev.device = -1;
+        return e;
+      }
+    }
+    ev.device = dev;
+  }
+  *out = &ev;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_version(void) { return RA_VERSION; }
+
+const char* ra_status_string(int status) {
+  switch (status) {
+    case RA_OK: return "RA_OK";
+    case RA_ERR_NULL: return "RA_ERR_NULL";
+    case RA_ERR_SHAPE: return "RA_ERR_SHAPE";
+    case RA_ERR_ALIGN: return "RA_ERR_ALIGN";
+    case RA_ERR_UNSUPPORTED: return "RA_ERR_UNSUPPORTED";
+    case RA_ERR_RANK: return "RA_ERR_RANK";
+    case RA_ERR_WORKSPACE: return "RA_ERR_WORKSPACE";
+    case RA_ERR_HIP: return "RA_ERR_HIP";
+    default: return "RA_ERR_UNKNOWN";
+  }
+}
+
+const char* ra_last_error(void) { return g_err; }
+
+int ra_step_fwd(const void* q, const void* k, const void* v, float* o_partial, float* lse_partial, int B, int H,
+                int Sq, int Sk, int d, float scale, int step, int causal, void* stream) {
+  if (!q || !k || !v || !o_partial || !lse_partial) return fail(RA_ERR_NULL, "ra_step_fwd: NULL pointer");
+  int st = check_dims(B, H, Sq, d, "ra_step_fwd(q)");
+  if (st) return st;
+  st = check_dims(B, H, Sk, d, "ra_step_fwd(k)");
+  if (st) return st;
+  if (step < 0) return fail(RA_ERR_SHAPE, "ra_step_fwd: step=%d < 0", step);
+  const bool diag = causal != 0 && step == 0;
+  if (diag && Sq != Sk) return fail(RA_ERR_SHAPE, "ra_step_fwd: diagonal step needs Sq == Sk (%d vs %d)", Sq, Sk);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_partial) || !aligned16(lse_partial))
+    return fail(RA_ERR_ALIGN, "ra_step_fwd: device pointers must be 16-byte aligned");
+  ra::FwdStepArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                    static_cast<const uint16_t*>(v), o_partial, lse_partial, B * H, Sq, Sk, d, scale, diag, false};
+  const hipError_t e = ra::launch_fwd_step(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ra_step_fwd launch");
+  return ok();
+}
+
+int ra_lse_merge(float* o, float* lse, const float* o_partial, const float* lse_partial, int B, int H, int S, int d,
+                 void* stream) {
+  if (!o || !lse || !o_partial || !lse_partial) return fail(RA_ERR_NULL, "ra_lse_merge: NULL pointer");
+  int st = check_dims(B, H, S, d, "ra_lse_merge");
+  if (st) return st;
+  if (!aligned16(o) || !aligned16(lse) || !aligned16(o_partial) || !aligned16(lse_partial))
+    return fail(RA_ERR_ALIGN, "ra_lse_merge: device pointers must be 16-byte aligned");
+  if (o == o_partial || lse == lse_partial) return fail(RA_ERR_SHAPE, "ra_lse_merge: output aliases the partial");
+  const hipError_t e = ra::launch_lse_merge(o, lse, o_partial, lse_partial, B * H * S, d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ra_lse_merge launch");
+  return ok();
+}
+
+size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d, int ring_mode, int bwd) {
+  if (P < 1 || B < 1 || H < 1 || C < 1 || (d != 64 && d != 128)) return 0;
+  const size_t elems = (size_t)B * H * C * d;
+  if (bwd) return (size_t)B * H * C * sizeof(float);
+  if (ring_mode == RA_RING_DOUBLE_BUFFER) return 4 * elems * 2;  // 2 slots x (K, V) bf16
+  return 0;
+}
+
+int ra_ring_fwd(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, float* o, float* lse,
+                int rank, int causal, float scale, int B, int H, int C, int d, int ring_mode, void* workspace,
+                size_t workspace_bytes, void* stream, void* copy_stream) {
+  if (!q || !k_chunks || !v_chunks || !o || !lse) return fail(RA_ERR_NULL, "ra_ring_fwd: NULL pointer");
+  if (P < 1) return fail(RA_ERR_SHAPE, "ra_ring_fwd: P=%d < 1", P);
+  int st = check_dims(B, H, C, d, "ra_ring_fwd");
+  if (st) return st;
+  if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "ra_ring_fwd: rank=%d outside [0, %d)", rank, P);
+  if (ring_mode != RA_RING_RESIDENT && ring_mode != RA_RING_DOUBLE_BUFFER)
+    return fail(RA_ERR_UNSUPPORTED, "ra_ring_fwd: ring_mode=%d", ring_mode);
+  for (int j = 0; j < P; ++j) {
+    if (!k_chunks[j] || !v_chunks[j]) return fail(RA_ERR_NULL, "ra_ring_fwd: chunk %d pointer is NULL", j);
+    if (!aligned16(k_chunks[j]) || !aligned16(v_chunks[j]))
+      return fail(RA_ERR_ALIGN, "ra_ring_fwd: chunk %d pointer not 16-byte aligned", j);
+  }
+  if (!aligned16(q) || !aligned16(o) || !aligned16(lse))
+    return fail(RA_ERR_ALIGN, "ra_ring_fwd: device pointers must be 16-byte aligned");
+  const size_t need = ra_ring_workspace_bytes(P, B, H, C, d, ring_mode, 0);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(RA_ERR_WORKSPACE, "ra_ring_fwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  if (need > 0 && !aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_ring_fwd: workspace not 16-byte aligned");
+
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
+  const std::vector<Step> steps = visible_steps(rank, P, causal != 0);
+  const size_t chunk_bytes = (size_t)B * H * C * d * 2;
+  const uint16_t* qh = static_cast<const uint16_t*>(q);
+  auto step_args = [&](const void* kp, const void* vp, bool diag, bool merge) {
+    return ra::FwdStepArgs{qh, static_cast<const uint16_t*>(kp), static_cast<const uint16_t*>(vp), o, lse, B * H,
+                           C, C, d, scale, diag, merge};
+  };
+
+  if (ring_mode == RA_RING_RESIDENT) {
+    for (size_t i = 0; i < steps.size(); ++i) {
+      const Step& sp = steps[i];
+      const hipError_t e = ra::launch_fwd_step(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, i > 0), cs);
+      if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd step launch");
+    }
+    return ok();
+  }
+
+  // Double buffer: step 0 reads the local chunk in place; the chunk of
+  // visible step i >= 1 is staged into slot (i-1) & 1 while step i-1 runs.
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  auto slot_k = [&](int slot) { return ws + (size_t)slot * 2 * chunk_bytes; };
+  auto slot_v = [&](int slot) { return ws + (size_t)slot * 2 * chunk_bytes + chunk_bytes; };
+  RingEvents* ev = nullptr;
+  hipError_t e = hipSuccess;
+  const bool two_streams = xs != cs;
+  if (two_streams) {
+    e = ring_events(&ev);
+    if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd events");
+    // Copies may start only after everything already queued on the compute
+    // stream (the inputs, and any earlier user of the workspace).
+    if ((e = hipEventRecord(ev->start, cs)) != hipSuccess) return hip_fail(e, "ra_ring_fwd record");
+    if ((e = hipStreamWaitEvent(xs, ev->start, 0)) != hipSuccess) return hip_fail(e, "ra_ring_fwd wait");
+  }
+  const int n = (int)steps.size();
+  for (int i = 0; i < n; ++i) {
+    // Stage the chunk for step i+1 (slot i & 1); that slot was last read by
+    // step i-1 (step 0 reads the local chunk in place), so from i = 2 on the
+    // copy waits for that step.
+    if (i + 1 < n) {
+      const int slot = i & 1;
+      const int j = steps[i + 1].j;
+      if (two_streams && i >= 2) {
+        if ((e = hipStreamWaitEvent(xs, ev->consumed[slot], 0)) != hipSuccess) return hip_fail(e, "ra_ring_fwd wait");
+      }
+      if ((e = hipMemcpyAsync(slot_k(slot), k_chunks[j], chunk_bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess)
+        return hip_fail(e, "ra_ring_fwd stage K");
+      if ((e = hipMemcpyAsync(slot_v(slot), v_chunks[j], chunk_bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess)
+        return hip_fail(e, "ra_ring_fwd stage V");
+      if (two_streams && (e = hipEventRecord(ev->copied[slot], xs)) != hipSuccess)
+        return hip_fail(e, "ra_ring_fwd record");
+    }
+    const Step& sp = steps[i];
+    if (i == 0) {
+      e = ra::launch_fwd_step(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, false), cs);
+    } else {
+      const int slot = (i - 1) & 1;
+      if (two_streams && (e = hipStreamWaitEvent(cs, ev->copied[slot], 0)) != hipSuccess)
+        return hip_fail(e, "ra_ring_fwd wait");
+      e = ra::launch_fwd_step(step_args(slot_k(slot), slot_v(slot), sp.diag, true), cs);
+      if (e == hipSuccess && two_streams) e = hipEventRecord(ev->consumed[slot], cs);
+    }
+    if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd step");
+  }
+  return ok();
+}
+
+int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,
+                const float* lse, const void* dO, float* dq, float* const* dk_chunks, float* const* dv_chunks,
+                int rank, int causal, float scale, int B, int H, int C, int d, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (!q || !k_chunks || !v_chunks || !o || !lse || !dO || !dq || !dk_chunks || !dv_chunks)
+    return fail(RA_ERR_NULL, "ra_ring_bwd: NULL pointer");
+  if (P < 1) return fail(RA_ERR_SHAPE, "ra_ring_bwd: P=%d < 1", P);
+  int st = check_dims(B, H, C, d, "ra_ring_bwd");
+  if (st) return st;
+  if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "ra_ring_bwd: rank=%d outside [0, %d)", rank, P);
+  const std::vector<Step> steps = visible_steps(rank, P, causal != 0);
+  for (const Step& sp : steps) {
+    const int j = sp.j;
+    if (!k_chunks[j] || !v_chunks[j] || !dk_chunks[j] || !dv_chunks[j])
+      return fail(RA_ERR_NULL, "ra_ring_bwd: chunk %d pointer is NULL", j);
+    if (!aligned16(k_chunks[j]) || !aligned16(v_chunks[j]) || !aligned16(dk_chunks[j]) || !aligned16(dv_chunks[j]))
+      return fail(RA_ERR_ALIGN, "ra_ring_bwd: chunk %d pointer not 16-byte aligned", j);
+  }
+  if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || !aligned16(dO) || !aligned16(dq))
+    return fail(RA_ERR_ALIGN, "ra_ring_bwd: device pointers must be 16-byte aligned");
+  const size_t need = ra_ring_workspace_bytes(P, B, H, C, d, 0, 1);
+  if (!workspace || workspace_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "ra_ring_bwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  if (!aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_ring_bwd: workspace not 16-byte aligned");
+
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  float* Dbuf = static_cast<float*>(workspace);
+  const int rows = B * H * C;
+  hipError_t e = ra::launch_bwd_rowdot(static_cast<const uint16_t*>(dO), o, Dbuf, rows, d, cs);
+  if (e == hipSuccess) e = ra::launch_zero_f32(dq, (size_t)rows * d, cs);
+  if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd preprocess");
+  for (const Step& sp : steps) {
+    ra::BwdStepArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_chunks[sp.j]),
+                      static_cast<const uint16_t*>(v_chunks[sp.j]), static_cast<const uint16_t*>(dO), lse, Dbuf, dq,
+                      dk_chunks[sp.j], dv_chunks[sp.j], B * H, C, C, d, scale, sp.diag};
+    e = ra::launch_bwd_step(a, cs);
+    if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd step");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Host-visible launch interface of the ring-attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// One ring step, forward: query block [BH, Sq, d] against one KV chunk
+// [BH, Sk, d] (bf16), written into (o, lse) fp32 -- overwritten when
+// merge == false, folded into the running values when merge == true.
+struct FwdStepArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* o;
+  float* lse;
+  int BH, Sq, Sk, d;
+  float scale;
+  bool diag;   // diagonal mask: local query t sees local keys <= t (Sq == Sk)
+  bool merge;  // fold into the running (o, lse) instead of overwriting
+};
+hipError_t launch_fwd_step(const FwdStepArgs& a, hipStream_t stream);
+
+// Row-wise online-softmax merge of a partial into (o, lse), in place.
+hipError_t launch_lse_merge(float* o, float* lse, const float* op, const float* lp,
+                            int rows, int d, hipStream_t stream);
+
+// Backward: D = rowsum(dO * O) per row.
+hipError_t launch_bwd_rowdot(const uint16_t* dO, const float* o, float* D, int rows, int d,
+                             hipStream_t stream);
+
+// Backward of one ring step against one KV chunk.  Uses the final lse and D.
+struct BwdStepArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dO;
+  const float* lse;
+  const float* D;
+  float* dq;   // accumulated (+=)
+  float* dk;   // accumulated (+=)
+  float* dv;   // accumulated (+=)
+  int BH, Sq, Sk, d;
+  float scale;
+  bool diag;
+};
+hipError_t launch_bwd_step(const BwdStepArgs& a, hipStream_t stream);
+
+// dq <- 0 over n floats (a small fill kernel, safe under graph capture).
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream);
+
+}  // namespace ra

@@ -1,0 +1,128 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/ra.h
+declares, and rejects bad arguments with the documented status codes before
+touching the GPU (validation is pure host code; no call here launches work).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_exact_step_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+
+RA_OK, RA_ERR_NULL, RA_ERR_SHAPE, RA_ERR_ALIGN, RA_ERR_UNSUPPORTED, RA_ERR_RANK, RA_ERR_WORKSPACE = range(7)
+
+FAKE = 0x10000  # an aligned, never-dereferenced address
+MIS = 0x10008   # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ra.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"ra_step_fwd", "ra_lse_merge", "ra_ring_fwd", "ra_ring_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in ra.h but not exported"
+
+
+def test_version_and_status_strings(L):
+    assert L.ra_version() == 1
+    assert L.ra_status_string(RA_OK) == b"RA_OK"
+    assert L.ra_status_string(RA_ERR_WORKSPACE) == b"RA_ERR_WORKSPACE"
+    assert L.ra_status_string(12345) == b"RA_ERR_UNKNOWN"
+
+
+def vp(x):
+    return ctypes.c_void_p(x)
+
+
+def step(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Sq=64, Sk=64, d=128, step=1, causal=0):
+    return L.ra_step_fwd(vp(q), vp(k), vp(v), vp(o), vp(lse), B, H, Sq, Sk, d, 0.125, step, causal, None)
+
+
+def test_step_fwd_validation(L):
+    assert step(L, q=0) == RA_ERR_NULL
+    assert step(L, lse=0) == RA_ERR_NULL
+    assert step(L, d=96) == RA_ERR_UNSUPPORTED
+    assert step(L, d=256) == RA_ERR_UNSUPPORTED
+    assert step(L, B=0) == RA_ERR_SHAPE
+    assert step(L, Sk=0) == RA_ERR_SHAPE
+    assert step(L, step=-1) == RA_ERR_SHAPE
+    assert step(L, step=0, causal=1, Sq=64, Sk=65) == RA_ERR_SHAPE
+    assert step(L, v=MIS) == RA_ERR_ALIGN
+    assert step(L, B=1 << 16, H=1 << 16, Sq=1) == RA_ERR_SHAPE  # rows overflow 32 bits
+    assert b"d=96" in (step(L, d=96), L.ra_last_error())[1]
+
+
+def test_lse_merge_validation(L):
+    m = lambda o=FAKE, lse=FAKE, op=FAKE + 4096, lp=FAKE + 8192, d=64: L.ra_lse_merge(
+        vp(o), vp(lse), vp(op), vp(lp), 1, 1, 8, d, None)
+    assert m(o=0) == RA_ERR_NULL
+    assert m(d=32) == RA_ERR_UNSUPPORTED
+    assert m(lse=MIS) == RA_ERR_ALIGN
+    assert m(op=FAKE) == RA_ERR_SHAPE  # output aliases the partial
+
+
+def ring_fwd(L, P=4, rank=3, mode=1, ws=FAKE, ws_bytes=None, chunks=None, d=128, C=64):
+    arr = (ctypes.c_void_p * P)(*([FAKE] * P if chunks is None else chunks))
+    need = L.ra_ring_workspace_bytes(P, 1, 2, C, d, mode, 0)
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.ra_ring_fwd(vp(FAKE), arr, arr, P, vp(FAKE), vp(FAKE), rank, 1, 0.1, 1, 2, C, d, mode,
+                         vp(ws), wsb, None, None)
+
+
+def test_ring_fwd_validation(L):
+    assert ring_fwd(L, rank=4) == RA_ERR_RANK
+    assert ring_fwd(L, rank=-1) == RA_ERR_RANK
+    assert ring_fwd(L, mode=7) == RA_ERR_UNSUPPORTED
+    assert ring_fwd(L, chunks=[FAKE, 0, FAKE, FAKE]) == RA_ERR_NULL
+    assert ring_fwd(L, chunks=[FAKE, MIS, FAKE, FAKE]) == RA_ERR_ALIGN
+    assert ring_fwd(L, ws=0) == RA_ERR_WORKSPACE
+    need = L.ra_ring_workspace_bytes(4, 1, 2, 64, 128, 1, 0)
+    assert ring_fwd(L, ws_bytes=need - 1) == RA_ERR_WORKSPACE
+    assert ring_fwd(L, d=80) == RA_ERR_UNSUPPORTED
+    assert ring_fwd(L, P=0, rank=0) == RA_ERR_SHAPE
+
+
+def test_ring_bwd_validation(L):
+    P, C, d = 4, 64, 128
+    arr = (ctypes.c_void_p * P)(*([FAKE] * P))
+    need = L.ra_ring_workspace_bytes(P, 1, 2, C, d, 0, 1)
+    args = lambda rank=3, ws=FAKE, wsb=need: L.ra_ring_bwd(
+        vp(FAKE), arr, arr, P, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), arr, arr, rank, 1, 0.1,
+        1, 2, C, d, vp(ws), wsb, None)
+    assert args(rank=5) == RA_ERR_RANK
+    assert args(ws=0) == RA_ERR_WORKSPACE
+    assert args(wsb=need - 4) == RA_ERR_WORKSPACE
+    assert L.ra_ring_bwd(None, arr, arr, P, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), arr, arr, 0, 1, 0.1,
+                         1, 2, C, d, vp(FAKE), need, None) == RA_ERR_NULL
+
+
+def test_workspace_sizes(L):
+    # Double buffer: 2 slots x (K + V) x B*H*C*d bf16.
+    assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 1, 0) == 2 * 2 * 32 * 32768 * 128 * 2
+    assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 0, 0) == 0
+    assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 128, 0, 1) == 32 * 16384 * 4
+    assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 96, 0, 1) == 0
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    o = torch.zeros(1, 1, 8, 64)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        ra.step_fwd(q, q, q, o, lse, 1, False)

@@ -1,0 +1,219 @@
+"""GPU parity at sizes the oracle finishes in seconds: several tiles, ragged
+tails, both head dims, every rank, both ring modes.  HIP outputs are compared
+element by element with the fp64 CPU oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_exact_step_amd as ra
+import oracle
+from long_context_exact_step_amd import inputs
+from parity import (TOL_GRAD, TOL_LSE, TOL_O, assert_close, dev, f64, gen, ring_tensors)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_step(q, k, v, step, causal, scale):
+    B, H, Sq, d = q.shape
+    o = torch.full((B, H, Sq, d), float("nan"), device=dev())
+    lse = torch.full((B, H, Sq), float("nan"), device=dev())
+    ra.step_fwd(q.to(dev()), k.to(dev()), v.to(dev()), o, lse, step, causal, scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,d,diag", [
+    (1, 1, 1, 1, 64, True),
+    (1, 2, 3, 3, 128, True),
+    (2, 2, 100, 100, 128, True),
+    (1, 2, 129, 129, 64, True),
+    (1, 3, 293, 293, 128, True),
+    (1, 2, 100, 37, 128, False),
+    (2, 1, 293, 517, 64, False),
+    (1, 2, 1, 700, 128, False),
+    (1, 1, 256, 256, 128, False),
+])
+def test_step_fwd_matches_oracle(B, H, Sq, Sk, d, diag):
+    print(f"step_fwd B={B} H={H} Sq={Sq} Sk={Sk} d={d} diag={diag}", flush=True)
+    q = gen(101, inputs.Q, 0, B, H, Sq, d)
+    k = gen(101, inputs.K, 0, B, H, Sk, d)
+    v = gen(101, inputs.V, 0, B, H, Sk, d)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_step(q, k, v, 0 if diag else 2, diag, scale)
+    ro, rl = oracle.step_partial(f64(q), f64(k), f64(v), scale, diagonal=diag)
+    assert_close(f64(o), ro, TOL_O, "o_partial")
+    assert_close(f64(lse), rl, TOL_LSE, "lse_partial", rel=None)
+
+
+def test_lse_merge_matches_oracle():
+    print("lse_merge", flush=True)
+    g = torch.Generator().manual_seed(5)
+    B, H, S, d = 2, 3, 77, 128
+    o = torch.randn(B, H, S, d, generator=g)
+    op = torch.randn(B, H, S, d, generator=g)
+    lse = torch.randn(B, H, S, generator=g) * 4
+    lp = torch.randn(B, H, S, generator=g) * 4
+    lse[0, 0, :5] = -math.inf
+    lp[0, 0, 3:9] = -math.inf
+    o[0, 0, :5] = 0
+    op[0, 0, 3:9] = 0
+    ro, rl = oracle.lse_merge(f64(o), f64(lse), f64(op), f64(lp))
+    go, gl, gop, glp = (t.to(dev()) for t in (o, lse, op, lp))
+    ra.lse_merge(go, gl, gop, glp)
+    torch.cuda.synchronize()
+    got_l = f64(gl)
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert np.abs(got_l[fin] - rl[fin]).max() < 1e-5
+    assert_close(f64(go), ro, 1e-5, "merged o")
+
+
+@pytest.mark.parametrize("P,C,d,causal", [
+    (1, 100, 128, True), (2, 3, 64, True), (4, 100, 128, True), (3, 129, 64, False),
+    (4, 64, 128, False), (2, 200, 128, True),
+])
+@pytest.mark.parametrize("mode", ["resident", "double_buffer"])
+def test_ring_fwd_every_rank(P, C, d, causal, mode):
+    B, H = 1, 2
+    q, k, v, _ = ring_tensors(102, B, H, P, C, d)
+    kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    scale = 1 / math.sqrt(d)
+    copy_stream = torch.cuda.Stream() if mode == "double_buffer" else None
+    for rank in range(P):
+        print(f"ring_fwd P={P} C={C} d={d} causal={causal} mode={mode} rank={rank}", flush=True)
+        o = torch.full((B, H, C, d), float("nan"), device=dev())
+        lse = torch.full((B, H, C), float("nan"), device=dev())
+        ra.ring_fwd(q[rank].to(dev()), kd, vd, o, lse, rank, causal, scale, ring_mode=mode,
+                    copy_stream=copy_stream)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attention_fwd(f64(q[rank]), kf, vf, scale, causal, q_pos=rank * C + np.arange(C))
+        assert_close(f64(o), ro, TOL_O, f"o rank {rank}")
+        assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)
+
+
+def test_steps_plus_merge_equal_fused_ring():
+    """The unfused path (ra_step_fwd per chunk + ra_lse_merge) and the fused
+    ring walk agree, and merge order does not matter."""
+    print("steps+merge vs fused ring", flush=True)
+    B, H, P, C, d, rank = 1, 2, 4, 160, 128, 3
+    q, k, v, _ = ring_tensors(103, B, H, P, C, d, ranks=[rank])
+    qd = q[rank].to(dev())
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    o = torch.empty(B, H, C, d, device=dev())
+    lse = torch.empty(B, H, C, device=dev())
+    ra.ring_fwd(qd, kd, vd, o, lse, rank, True, ring_mode="resident")
+    parts = []
+    for s in range(P):
+        j = (rank - s) % P
+        op = torch.empty(B, H, C, d, device=dev())
+        lp = torch.empty(B, H, C, device=dev())
+        ra.step_fwd(qd, kd[j], vd[j], op, lp, s, True)
+        parts.append((op, lp))
+    results = []
+    for order in ([0, 1, 2, 3], [3, 1, 0, 2], [2, 3, 1, 0]):
+        mo, ml = parts[order[0]][0].clone(), parts[order[0]][1].clone()
+        for n in order[1:]:
+            ra.lse_merge(mo, ml, parts[n][0], parts[n][1])
+        results.append((mo, ml))
+    torch.cuda.synchronize()
+    for mo, ml in results:
+        assert_close(f64(mo), f64(o), 1e-5, "unfused vs fused o", rel=None)
+        assert_close(f64(ml), f64(lse), 1e-5, "unfused vs fused lse", rel=None)
+
+
+def test_future_chunks_do_not_matter():
+    """Causal: contents of chunks j > rank leave the outputs bit-identical."""
+    print("skip invariance", flush=True)
+    B, H, P, C, d, rank = 1, 2, 4, 96, 128, 1
+    q, k, v, _ = ring_tensors(104, B, H, P, C, d, ranks=[rank])
+    outs = []
+    for trial in range(2):
+        kk = [t.clone() for t in k]
+        vv = [t.clone() for t in v]
+        if trial:
+            for j in range(rank + 1, P):
+                kk[j] = gen(999, inputs.K, j, B, H, C, d)
+                vv[j] = gen(999, inputs.V, j, B, H, C, d)
+        o = torch.empty(B, H, C, d, device=dev())
+        lse = torch.empty(B, H, C, device=dev())
+        ra.ring_fwd(q[rank].to(dev()), [t.to(dev()) for t in kk], [t.to(dev()) for t in vv], o, lse, rank, True)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def _bwd_case(P, C, d, causal, rank, B=1, H=2, wid=105):
+    q, k, v, do = ring_tensors(wid, B, H, P, C, d, with_do=True, ranks=[rank])
+    scale = 1 / math.sqrt(d)
+    qd, dod = q[rank].to(dev()), do[rank].to(dev())
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    o = torch.empty(B, H, C, d, device=dev())
+    lse = torch.empty(B, H, C, device=dev())
+    ra.ring_fwd(qd, kd, vd, o, lse, rank, causal, scale, ring_mode="resident")
+    dq = torch.full((B, H, C, d), float("nan"), device=dev())
+    dk = [torch.zeros(B, H, C, d, device=dev()) for _ in range(P)]
+    dv = [torch.zeros(B, H, C, d, device=dev()) for _ in range(P)]
+    ra.ring_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, rank, causal, scale)
+    torch.cuda.synchronize()
+    return q, k, v, do, scale, dq, dk, dv
+
+
+@pytest.mark.parametrize("P,C,d,causal", [(3, 100, 128, True), (2, 129, 64, True), (3, 64, 128, False),
+                                          (1, 200, 128, True)])
+def test_ring_bwd_matches_oracle(P, C, d, causal):
+    for rank in range(P):
+        print(f"ring_bwd P={P} C={C} d={d} causal={causal} rank={rank}", flush=True)
+        q, k, v, do, scale, dq, dk, dv = _bwd_case(P, C, d, causal, rank)
+        kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
+        rq, rk, rv = oracle.attention_bwd(f64(q[rank]), kf, vf, f64(do[rank]), scale, causal,
+                                          q_pos=rank * C + np.arange(C))
+        assert_close(f64(dq), rq, TOL_GRAD, "dq")
+        for j in range(P):
+            sl = slice(j * C, (j + 1) * C)
+            if causal and j > rank:
+                assert not dk[j].any() and not dv[j].any(), "skipped chunk was touched"
+                continue
+            assert_close(f64(dk[j]), rk[:, :, sl], TOL_GRAD, f"dk chunk {j}")
+            assert_close(f64(dv[j]), rv[:, :, sl], TOL_GRAD, f"dv chunk {j}")
+
+
+def test_ring_bwd_accumulates_over_ranks():
+    """Walking every rank's share into the same dK_j/dV_j accumulators gives
+    the full-sequence gradient."""
+    print("ring_bwd accumulation over ranks", flush=True)
+    B, H, P, C, d = 1, 2, 3, 80, 128
+    q, k, v, do = ring_tensors(106, B, H, P, C, d, with_do=True)
+    scale = 1 / math.sqrt(d)
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    dk = [torch.zeros(B, H, C, d, device=dev()) for _ in range(P)]
+    dv = [torch.zeros(B, H, C, d, device=dev()) for _ in range(P)]
+    for rank in range(P):
+        o = torch.empty(B, H, C, d, device=dev())
+        lse = torch.empty(B, H, C, device=dev())
+        dq = torch.empty(B, H, C, d, device=dev())
+        ra.ring_fwd(q[rank].to(dev()), kd, vd, o, lse, rank, True, scale)
+        ra.ring_bwd(q[rank].to(dev()), kd, vd, o, lse, do[rank].to(dev()), dq, dk, dv, rank, True, scale)
+    torch.cuda.synchronize()
+    qa = f64(torch.cat([q[r] for r in range(P)], dim=2))
+    doa = f64(torch.cat([do[r] for r in range(P)], dim=2))
+    _, rk, rv = oracle.attention_bwd(qa, f64(torch.cat(k, 2)), f64(torch.cat(v, 2)), doa, scale, True)
+    assert_close(f64(torch.cat(dk, 2)), rk, TOL_GRAD, "dk accumulated")
+    assert_close(f64(torch.cat(dv, 2)), rv, TOL_GRAD, "dv accumulated")
+
+
+def test_repeat_runs_bit_identical():
+    print("determinism", flush=True)
+    outs = []
+    for _ in range(2):
+        q, k, v, do, scale, dq, dk, dv = _bwd_case(2, 150, 128, True, 1, wid=107)
+        outs.append([t.cpu() for t in [dq, *dk, *dv]])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
