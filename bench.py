@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of Ring Attention on one MI355X.
+
+Default workload: the 128K-token sequence at CP=4, local share of rank 3
+(C = 32768 query tokens, P = 4 KV chunks of 32768, H = 32, d = 128, causal),
+forward ring walk in double-buffer mode.  One step = one ra_ring_fwd call:
+the ring schedule, the staged (emulated) KV receives, one fused step kernel
+per visible chunk with the log-sum-exp merge in its epilogue.  Inputs are
+seeded synthetic bf16 N(0,1) tensors resident in HBM before timing starts.
+
+Also reported (unless --no-train): the training share (C = 16384, P = 4,
+rank 3, H = 32, d = 128, causal), one step = forward walk + backward walk.
+
+Prints ONE JSON line: throughput in algorithmic TFLOP/s (4*d flops per
+visible (query, key) pair forward, 10*d backward), tokens/s, the roofline of
+the dominant kernel timed live with HIP events on its own stream, and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-train] [--no-cpu]
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ring-attention fwd/bwd TFLOP/s and tokens/s on 1 MI355X (% of bf16 MFMA peak)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fwd_step_full_128k_cp4_counters.json")
+FWD_KERNEL_SOURCES = ["long_context_exact_step_amd/csrc/ra_fwd.hip", "long_context_exact_step_amd/csrc/ra_device.h"]
+
+
+def fwd_kernel_sha():
+    h = hashlib.sha256()
+    for p in FWD_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Timing-enabled hipEvent_t handles made through the HIP runtime."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.start, self.end = [], []
+        for lst in (self.start, self.end):
+            for _ in range(n):
+                e = ctypes.c_void_p()
+                rc = self.hip.hipEventCreate(ctypes.byref(e))
+                if rc != 0:
+                    raise RuntimeError(f"hipEventCreate failed ({rc})")
+                lst.append(e.value)
+
+    def elapsed_ms(self, i):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.end[i])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.start + self.end:
+            self.hip.hipEventDestroy(e)
+
+
+def pairs_of_kind(kind, w):
+    """Visible (query, key) pairs one traced launch processes."""
+    C, BH = w.C, w.B * w.H
+    if kind in ("fwd_diag", "bwd_dq_diag", "bwd_dkdv_diag"):
+        return BH * C * (C + 1) // 2
+    if kind in ("fwd_full", "bwd_dq_full", "bwd_dkdv_full"):
+        return BH * C * C
+    return 0
+
+
+def timed_steps(step_fn, n_launch_per_step, steps, warmup):
+    """Runs warmup, then exactly `steps` timed steps with per-launch tracing.
+    Returns (seconds, [(kind, ms), ...])."""
+    import torch
+    import long_context_exact_step_amd as ra
+
+    for _ in range(warmup):
+        step_fn()
+    torch.cuda.synchronize()
+    cap = steps * n_launch_per_step
+    ev = HipEvents(cap)
+    kinds = (ctypes.c_int * cap)()
+    keep = ra.trace_begin(ev.start, ev.end, kinds)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step_fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n = ra.trace_end()
+    del keep
+    rec = [(ra.TRACE_KINDS[kinds[i]], ev.elapsed_ms(i)) for i in range(min(n, cap))]
+    ev.close()
+    return t1 - t0, rec
+
+
+def kernel_stats(rec, w, kind_flops):
+    """Per kind: launches, average ms, algorithmic TFLOP/s."""
+    out = {}
+    for kind in sorted({k for k, _ in rec}):
+        ms = [m for k, m in rec if k == kind]
+        avg = sum(ms) / len(ms)
+        fl = kind_flops(kind) * pairs_of_kind(kind, w)
+        out[kind] = {"launches": len(ms), "avg_ms": round(avg, 4),
+                     "tflops": round(fl / (avg * 1e-3) / 1e12, 2) if fl else None}
+    return out
+
+
+def run_fwd(w, steps, warmup, ring_mode):
+    import torch
+    import long_context_exact_step_amd as ra
+    from long_context_exact_step_amd import inputs
+    from long_context_exact_step_amd.workloads import fwd_flops, step_kinds
+
+    dev = torch.device("cuda", 0)
+    B, H, C, d, P = w.B, w.H, w.C, w.d, w.P
+    qs = {r: inputs.chunk(w.id, inputs.Q, r, B, H, C, d).to(dev) for r in w.ranks}
+    ks = [inputs.chunk(w.id, inputs.K, j, B, H, C, d).to(dev) for j in range(P)]
+    vs = [inputs.chunk(w.id, inputs.V, j, B, H, C, d).to(dev) for j in range(P)]
+    o = {r: torch.empty(B, H, C, d, device=dev) for r in w.ranks}
+    lse = {r: torch.empty(B, H, C, device=dev) for r in w.ranks}
+    ws = torch.empty(max(1, ra.workspace_bytes(P, B, H, C, d, ring_mode)), dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream(dev) if ring_mode == "double_buffer" else None
+    n_launch = sum(sum(k != "skip" for *_, k in step_kinds(r, P, w.causal)) for r in w.ranks)
+
+    def step():
+        for r in w.ranks:
+            ra.ring_fwd(qs[r], ks, vs, o[r], lse[r], r, w.causal, w.scale, ring_mode=ring_mode,
+                        workspace=ws, copy_stream=copy_stream)
+
+    secs, rec = timed_steps(step, n_launch, steps, warmup)
+    flops = fwd_flops(w)
+    res = {
+        "secs": secs, "ms_per_step": secs / steps * 1e3,
+        "tflops": flops * steps / secs / 1e12,
+        "tokens_per_s": B * C * len(w.ranks) * steps / secs,
+        "kernels": kernel_stats(rec, w, lambda k: 4 * d),
+        "rec": rec,
+    }
+    return res, (qs, ks, vs, o, lse)
+
+
+def run_train(w, steps, warmup):
+    import torch
+    import long_context_exact_step_amd as ra
+    from long_context_exact_step_amd import inputs
+    from long_context_exact_step_amd.workloads import bwd_flops, fwd_flops, step_kinds
+
+    dev = torch.device("cuda", 0)
+    B, H, C, d, P = w.B, w.H, w.C, w.d, w.P
+    r = w.ranks[0]
+    q = inputs.chunk(w.id, inputs.Q, r, B, H, C, d).to(dev)
+    do = inputs.chunk(w.id, inputs.DO, r, B, H, C, d).to(dev)
+    ks = [inputs.chunk(w.id, inputs.K, j, B, H, C, d).to(dev) for j in range(P)]
+    vs = [inputs.chunk(w.id, inputs.V, j, B, H, C, d).to(dev) for j in range(P)]
+    o = torch.empty(B, H, C, d, device=dev)
+    lse = torch.empty(B, H, C, device=dev)
+    dq = torch.empty(B, H, C, d, device=dev)
+    dk = [torch.zeros(B, H, C, d, device=dev) for _ in range(P)]
+    dv = [torch.zeros(B, H, C, d, device=dev) for _ in range(P)]
+    ws_f = torch.empty(ra.workspace_bytes(P, B, H, C, d, "double_buffer"), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(ra.workspace_bytes(P, B, H, C, d, "resident", bwd=True), dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream(dev)
+    nvis = sum(k != "skip" for *_, k in step_kinds(r, P, w.causal))
+    n_launch = nvis + 2 + 2 * nvis
+
+    def step():
+        for t in dk + dv:
+            t.zero_()
+        ra.ring_fwd(q, ks, vs, o, lse, r, w.causal, w.scale, ring_mode="double_buffer", workspace=ws_f,
+                    copy_stream=copy_stream)
+        ra.ring_bwd(q, ks, vs, o, lse, do, dq, dk, dv, r, w.causal, w.scale, workspace=ws_b)
+
+    secs, rec = timed_steps(step, n_launch, steps, warmup)
+    fl_f, fl_b = fwd_flops(w), bwd_flops(w)
+    kf = {"fwd_diag": 4 * d, "fwd_full": 4 * d, "bwd_dq_diag": 6 * d, "bwd_dq_full": 6 * d,
+          "bwd_dkdv_diag": 8 * d, "bwd_dkdv_full": 8 * d}
+    ks_ = kernel_stats(rec, w, lambda k: kf.get(k, 0))
+    fwd_ms = sum(m for k, m in rec if k.startswith("fwd")) / steps
+    bwd_ms = sum(m for k, m in rec if k.startswith("bwd")) / steps
+    return {
+        "workload": w.name, "steps": steps, "ms_per_step": secs / steps * 1e3,
+        "tflops_fwd_bwd": (fl_f + fl_b) * steps / secs / 1e12,
+        "tokens_per_s": B * C * steps / secs,
+        "fwd_kernels_ms_per_step": round(fwd_ms, 3), "bwd_kernels_ms_per_step": round(bwd_ms, 3),
+        "fwd_tflops_kernels": round(fl_f / (fwd_ms * 1e-3) / 1e12, 1),
+        "bwd_tflops_kernels_algorithmic": round(fl_b / (bwd_ms * 1e-3) / 1e12, 1),
+        "kernels": ks_,
+    }
+
+
+def cpu_baseline(w, tensors, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample: 256 seeded query
+    rows per head of the measured rank, heads taken in order until the time
+    budget is spent.  Returns the baseline record and the GPU-vs-oracle error
+    on those rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from long_context_exact_step_amd import inputs
+
+    qs, ks, vs, o, lse = tensors
+    r = w.ranks[-1]
+    C, d, P = w.C, w.d, w.P
+    f64 = lambda t: t.float().cpu().double().numpy()
+    q_cpu = qs[r].cpu()
+    secs = 0.0
+    pairs = 0
+    rows_done = 0
+    heads = 0
+    err_o = err_l = 0.0
+    for h in range(w.H):
+        rows = inputs.query_row_sample(w.id, h, C)
+        kh = np.concatenate([f64(ks[j][:, h:h + 1]) for j in range(P)], axis=2)
+        vh = np.concatenate([f64(vs[j][:, h:h + 1]) for j in range(P)], axis=2)
+        qh = f64(q_cpu[:, h:h + 1, rows])
+        pos = r * C + rows
+        t0 = time.perf_counter()
+        ro, rl = oracle.attention_fwd(qh, kh, vh, w.scale, w.causal, q_pos=pos)
+        secs += time.perf_counter() - t0
+        pairs += int((pos + 1).sum()) if w.causal else len(rows) * P * C
+        rows_done += len(rows)
+        heads += 1
+        go = f64(o[r][:, h:h + 1, rows])
+        gl = f64(lse[r][:, h:h + 1, rows])
+        err_o = max(err_o, float(np.abs(go - ro).max()))
+        err_l = max(err_l, float(np.abs(gl - rl).max()))
+        if secs >= budget_s:
+            break
+    threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    flops = 4 * d * pairs
+    return {
+        "value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{rows_done} query rows ({heads} heads x 256 seeded rows) of rank {r}, each against its "
+                  f"{'visible' if w.causal else 'whole'} key range of the unchunked sequence; fp64 NumPy",
+        "seconds": round(secs, 2),
+        "tokens_per_s_equiv": round(rows_done / w.H / secs, 3),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }, {"max_abs_err_o": err_o, "max_abs_err_lse": err_l, "rows": rows_done}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--ring-mode", default="double_buffer", choices=["double_buffer", "resident"])
+    ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the ring on a single MI355X; multi-GPU runs "
+              "(--gpus > 1) are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_exact_step_amd.workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    fwd, tensors = run_fwd(w, args.steps, args.warmup, args.ring_mode)
+    print(f"[bench] fwd {w.name}: {fwd['ms_per_step']:.3f} ms/step, {fwd['tflops']:.1f} TFLOP/s", file=sys.stderr,
+          flush=True)
+
+    dom = "fwd_full" if "fwd_full" in fwd["kernels"] else "fwd_diag"
+    dk = fwd["kernels"][dom]
+    dom_flops = 4 * w.d * pairs_of_kind(dom, w)
+    achieved = dom_flops / (dk["avg_ms"] * 1e-3) / 1e12
+    traffic = None
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            prof = json.load(f)
+        if prof.get("source_sha") == fwd_kernel_sha() and prof.get("workload_id") == w.id:
+            traffic = prof.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+        "kernel": f"fwd_step_kernel ({dom}), {dk['launches']} launches, avg {dk['avg_ms']} ms",
+        "flops_per_launch": dom_flops,
+    }
+
+    out = {
+        "metric": METRIC, "value": round(fwd["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(fwd["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "C": w.C, "P": w.P, "rank": list(w.ranks), "d": w.d,
+                   "causal": w.causal, "ring_mode": args.ring_mode},
+        "tokens_per_s": round(fwd["tokens_per_s"], 1),
+        "pct_bf16_dense_peak": round(100 * fwd["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "kernels": fwd["kernels"],
+        "roofline": roofline,
+    }
+    if not args.no_cpu:
+        cb, par = cpu_baseline(w, tensors, args.cpu_seconds)
+        out["cpu_baseline"] = cb
+        out["parity_on_baseline_rows"] = par
+    del tensors
+    torch.cuda.empty_cache()
+    if not args.no_train and w.id != 5:
+        tr = run_train(WORKLOADS[5], max(3, args.steps // 2), max(1, args.warmup))
+        out["train"] = tr
+        print(f"[bench] train: {tr['ms_per_step']:.3f} ms/step, {tr['tflops_fwd_bwd']:.1f} TFLOP/s", file=sys.stderr,
+              flush=True)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -178,6 +178,37 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks,
                 int causal, float scale, int B, int H, int C, int d,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Per-launch tracing, for profiling.  The pages define no such facility; it
+ * exists so that a caller can time each kernel of a ring walk with its own
+ * events, on the stream the kernel runs on.
+ *
+ * ra_trace_begin arms tracing on the calling thread.  Every kernel that
+ * ra_step_fwd, ra_lse_merge, ra_ring_fwd or ra_ring_bwd then launch on their
+ * compute stream is bracketed by hipEventRecord(start_events[n], stream)
+ * and hipEventRecord(end_events[n], stream), and kinds[n] receives its
+ * RA_TRACE_* kind, for the n-th such launch while n < capacity (later
+ * launches run untraced).  The events are hipEvent_t handles (as void*) the
+ * caller created with timing enabled and still owns; kinds may be NULL.
+ * ra_trace_end disarms tracing and returns the number of launches made while
+ * armed (possibly more than capacity).  Staging copies are not traced.
+ * ra_trace_begin returns RA_ERR_NULL for missing arrays with capacity > 0
+ * and RA_ERR_SHAPE for capacity < 0.
+ */
+enum ra_trace_kind {
+  RA_TRACE_FWD_DIAG = 1,       /* forward step, diagonal (masked) chunk */
+  RA_TRACE_FWD_FULL = 2,       /* forward step, fully visible chunk */
+  RA_TRACE_MERGE = 3,          /* standalone lse merge */
+  RA_TRACE_BWD_ROWDOT = 4,     /* backward: D = rowsum(dO * o) */
+  RA_TRACE_BWD_ZERO = 5,       /* backward: dq <- 0 */
+  RA_TRACE_BWD_DQ_DIAG = 6,    /* backward dq kernel, diagonal chunk */
+  RA_TRACE_BWD_DQ_FULL = 7,    /* backward dq kernel, full chunk */
+  RA_TRACE_BWD_DKDV_DIAG = 8,  /* backward dk/dv kernel, diagonal chunk */
+  RA_TRACE_BWD_DKDV_FULL = 9   /* backward dk/dv kernel, full chunk */
+};
+int ra_trace_begin(void* const* start_events, void* const* end_events, int* kinds, int capacity);
+int ra_trace_end(void);
+
 #ifdef __cplusplus
 }
 #endif

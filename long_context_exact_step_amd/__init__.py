@@ -15,8 +15,13 @@ import os
 
 __all__ = [
     "RAError", "lib", "version", "step_fwd", "lse_merge", "ring_fwd", "ring_bwd",
-    "workspace_bytes", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH",
+    "workspace_bytes", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH", "trace_begin", "trace_end",
+    "TRACE_KINDS",
 ]
+
+# ra_trace_kind values (include/ra.h).
+TRACE_KINDS = {1: "fwd_diag", 2: "fwd_full", 3: "merge", 4: "bwd_rowdot", 5: "bwd_zero",
+               6: "bwd_dq_diag", 7: "bwd_dq_full", 8: "bwd_dkdv_diag", 9: "bwd_dkdv_full"}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
 RING_RESIDENT = 0
@@ -61,6 +66,10 @@ def lib():
         L.ra_ring_fwd.argtypes = [vp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, i, vp, sz, vp, vp]
         L.ra_ring_bwd.restype = i
         L.ra_ring_bwd.argtypes = [vp, vpp, vpp, i, vp, vp, vp, vp, vpp, vpp, i, i, f, i, i, i, i, vp, sz, vp]
+        L.ra_trace_begin.restype = i
+        L.ra_trace_begin.argtypes = [vpp, vpp, ctypes.POINTER(ctypes.c_int), i]
+        L.ra_trace_end.restype = i
+        L.ra_trace_end.argtypes = []
         _lib = L
     return _lib
 
@@ -183,3 +192,19 @@ def ring_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, 
                              int(bool(causal)), scale, B, H, C, d, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream, q)))
     return workspace
+
+
+def trace_begin(start_events, end_events, kinds):
+    """ra_trace_begin: start_events/end_events are raw hipEvent_t handles
+    (ints, timing enabled); kinds is a ctypes c_int array of the same length.
+    The arrays must stay alive until trace_end()."""
+    n = len(start_events)
+    sa = (ctypes.c_void_p * n)(*start_events)
+    ea = (ctypes.c_void_p * n)(*end_events)
+    _check(lib().ra_trace_begin(sa, ea, kinds, n))
+    return sa, ea
+
+
+def trace_end():
+    """ra_trace_end: number of launches made while tracing was armed."""
+    return int(lib().ra_trace_end())

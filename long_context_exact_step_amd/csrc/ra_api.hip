@@ -94,9 +94,55 @@ hipError_t ring_events(RingEvents** out) {
   return hipSuccess;
 }
 
+// Per-launch tracing state of the calling thread (see ra_trace_begin).
+struct Trace {
+  void* const* start = nullptr;
+  void* const* end = nullptr;
+  int* kinds = nullptr;
+  int capacity = 0;
+  int count = 0;
+  bool armed = false;
+};
+thread_local Trace t_trace;
+
+// Launches one kernel through `launch`, bracketed by the caller's trace
+// events when tracing is armed.
+template <class F>
+hipError_t traced(int kind, hipStream_t stream, F&& launch) {
+  Trace& tr = t_trace;
+  const bool rec = tr.armed && tr.count < tr.capacity;
+  const int n = tr.count;
+  if (tr.armed) ++tr.count;
+  hipError_t e;
+  if (rec) {
+    if (tr.kinds) tr.kinds[n] = kind;
+    if ((e = hipEventRecord(static_cast<hipEvent_t>(tr.start[n]), stream)) != hipSuccess) return e;
+  }
+  if ((e = launch()) != hipSuccess) return e;
+  if (rec) e = hipEventRecord(static_cast<hipEvent_t>(tr.end[n]), stream);
+  return e;
+}
+
+hipError_t fwd_step(const ra::FwdStepArgs& a, hipStream_t s) {
+  return traced(a.diag ? RA_TRACE_FWD_DIAG : RA_TRACE_FWD_FULL, s, [&] { return ra::launch_fwd_step(a, s); });
+}
+
 }  // namespace
 
 extern "C" {
+
+int ra_trace_begin(void* const* start_events, void* const* end_events, int* kinds, int capacity) {
+  if (capacity < 0) return fail(RA_ERR_SHAPE, "ra_trace_begin: capacity=%d < 0", capacity);
+  if (capacity > 0 && (!start_events || !end_events)) return fail(RA_ERR_NULL, "ra_trace_begin: NULL event array");
+  t_trace = Trace{start_events, end_events, kinds, capacity, 0, true};
+  return ok();
+}
+
+int ra_trace_end(void) {
+  const int n = t_trace.count;
+  t_trace = Trace{};
+  return n;
+}
 
 int ra_version(void) { return RA_VERSION; }
 
@@ -130,7 +176,7 @@ int ra_step_fwd(const void* q, const void* k, const void* v, float* o_partial, f
     return fail(RA_ERR_ALIGN, "ra_step_fwd: device pointers must be 16-byte aligned");
   ra::FwdStepArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                     static_cast<const uint16_t*>(v), o_partial, lse_partial, B * H, Sq, Sk, d, scale, diag, false};
-  const hipError_t e = ra::launch_fwd_step(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = fwd_step(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ra_step_fwd launch");
   return ok();
 }
@@ -143,7 +189,10 @@ int ra_lse_merge(float* o, float* lse, const float* o_partial, const float* lse_
   if (!aligned16(o) || !aligned16(lse) || !aligned16(o_partial) || !aligned16(lse_partial))
     return fail(RA_ERR_ALIGN, "ra_lse_merge: device pointers must be 16-byte aligned");
   if (o == o_partial || lse == lse_partial) return fail(RA_ERR_SHAPE, "ra_lse_merge: output aliases the partial");
-  const hipError_t e = ra::launch_lse_merge(o, lse, o_partial, lse_partial, B * H * S, d, static_cast<hipStream_t>(stream));
+  hipStream_t st_ = static_cast<hipStream_t>(stream);
+  const hipError_t e = traced(RA_TRACE_MERGE, st_, [&] {
+    return ra::launch_lse_merge(o, lse, o_partial, lse_partial, B * H * S, d, st_);
+  });
   if (e != hipSuccess) return hip_fail(e, "ra_lse_merge launch");
   return ok();
 }
@@ -192,7 +241,7 @@ int ra_ring_fwd(const void* q, const void* const* k_chunks, const void* const* v
   if (ring_mode == RA_RING_RESIDENT) {
     for (size_t i = 0; i < steps.size(); ++i) {
       const Step& sp = steps[i];
-      const hipError_t e = ra::launch_fwd_step(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, i > 0), cs);
+      const hipError_t e = fwd_step(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, i > 0), cs);
       if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd step launch");
     }
     return ok();
@@ -234,12 +283,12 @@ int ra_ring_fwd(const void* q, const void* const* k_chunks, const void* const* v
     }
     const Step& sp = steps[i];
     if (i == 0) {
-      e = ra::launch_fwd_step(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, false), cs);
+      e = fwd_step(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, false), cs);
     } else {
       const int slot = (i - 1) & 1;
       if (two_streams && (e = hipStreamWaitEvent(cs, ev->copied[slot], 0)) != hipSuccess)
         return hip_fail(e, "ra_ring_fwd wait");
-      e = ra::launch_fwd_step(step_args(slot_k(slot), slot_v(slot), sp.diag, true), cs);
+      e = fwd_step(step_args(slot_k(slot), slot_v(slot), sp.diag, true), cs);
       if (e == hipSuccess && two_streams) e = hipEventRecord(ev->consumed[slot], cs);
     }
     if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd step");
@@ -276,14 +325,19 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v
   hipStream_t cs = static_cast<hipStream_t>(stream);
   float* Dbuf = static_cast<float*>(workspace);
   const int rows = B * H * C;
-  hipError_t e = ra::launch_bwd_rowdot(static_cast<const uint16_t*>(dO), o, Dbuf, rows, d, cs);
-  if (e == hipSuccess) e = ra::launch_zero_f32(dq, (size_t)rows * d, cs);
+  hipError_t e = traced(RA_TRACE_BWD_ROWDOT, cs, [&] {
+    return ra::launch_bwd_rowdot(static_cast<const uint16_t*>(dO), o, Dbuf, rows, d, cs);
+  });
+  if (e == hipSuccess) e = traced(RA_TRACE_BWD_ZERO, cs, [&] { return ra::launch_zero_f32(dq, (size_t)rows * d, cs); });
   if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd preprocess");
   for (const Step& sp : steps) {
     ra::BwdStepArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_chunks[sp.j]),
                       static_cast<const uint16_t*>(v_chunks[sp.j]), static_cast<const uint16_t*>(dO), lse, Dbuf, dq,
                       dk_chunks[sp.j], dv_chunks[sp.j], B * H, C, C, d, scale, sp.diag};
-    e = ra::launch_bwd_step(a, cs);
+    e = traced(sp.diag ? RA_TRACE_BWD_DQ_DIAG : RA_TRACE_BWD_DQ_FULL, cs, [&] { return ra::launch_bwd_dq(a, cs); });
+    if (e == hipSuccess)
+      e = traced(sp.diag ? RA_TRACE_BWD_DKDV_DIAG : RA_TRACE_BWD_DKDV_FULL, cs,
+                 [&] { return ra::launch_bwd_dkdv(a, cs); });
     if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd step");
   }
   return ok();

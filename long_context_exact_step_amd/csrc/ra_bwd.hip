@@ -360,45 +360,48 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(const uint16_t* __restric
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdStepArgs& a, hipStream_t stream) {
+hipError_t launch_dq_d(const BwdStepArgs& a, hipStream_t stream) {
+  const int nq = (a.Sq + 127) / 128;
+  const long long total = (long long)nq * a.BH;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (total == 0) return hipSuccess;
   const float sl2 = a.scale * kLog2e;
-  {
-    const int nq = (a.Sq + 127) / 128;
-    const long long total = (long long)nq * a.BH;
-    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (total > 0) {
-      if (a.diag)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v,
-                           a.dO, a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
-      else
-        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v,
-                           a.dO, a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  {
-    const int nk = (a.Sk + 127) / 128;
-    const long long total = (long long)nk * a.BH;
-    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (total > 0) {
-      if (a.diag)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v,
-                           a.dO, a.lse, a.D, a.dk, a.dv, a.Sq, a.Sk, nk, (int)total, sl2, a.scale);
-      else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k,
-                           a.v, a.dO, a.lse, a.D, a.dk, a.dv, a.Sq, a.Sk, nk, (int)total, sl2, a.scale);
-      return hipGetLastError();
-    }
-  }
-  return hipSuccess;
+  if (a.diag)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v, a.dO,
+                       a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v, a.dO,
+                       a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dkdv_d(const BwdStepArgs& a, hipStream_t stream) {
+  const int nk = (a.Sk + 127) / 128;
+  const long long total = (long long)nk * a.BH;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (total == 0) return hipSuccess;
+  const float sl2 = a.scale * kLog2e;
+  if (a.diag)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v,
+                       a.dO, a.lse, a.D, a.dk, a.dv, a.Sq, a.Sk, nk, (int)total, sl2, a.scale);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v,
+                       a.dO, a.lse, a.D, a.dk, a.dv, a.Sq, a.Sk, nk, (int)total, sl2, a.scale);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_step(const BwdStepArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_bwd_d<128>(a, stream);
-  if (a.d == 64) return launch_bwd_d<64>(a, stream);
+hipError_t launch_bwd_dq(const BwdStepArgs& a, hipStream_t stream) {
+  if (a.d == 128) return launch_dq_d<128>(a, stream);
+  if (a.d == 64) return launch_dq_d<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dkdv(const BwdStepArgs& a, hipStream_t stream) {
+  if (a.d == 128) return launch_dkdv_d<128>(a, stream);
+  if (a.d == 64) return launch_dkdv_d<64>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -45,7 +45,8 @@ struct BwdStepArgs {
   float scale;
   bool diag;
 };
-hipError_t launch_bwd_step(const BwdStepArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdStepArgs& a, hipStream_t stream);    // dq += ...
+hipError_t launch_bwd_dkdv(const BwdStepArgs& a, hipStream_t stream);  // dk, dv += ...
 
 // dq <- 0 over n floats (a small fill kernel, safe under graph capture).
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream);
