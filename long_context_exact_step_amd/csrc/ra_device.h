@@ -42,6 +42,20 @@ __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32, kWave);
 }
 
+// max / sum of x over the lane pair (l, l ^ 32) with v_permlane32_swap (a
+// VALU lane exchange, no LDS round trip): swapping the upper half of one copy
+// with the lower half of another leaves x[l] and x[l^32] in the two results.
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 // Logical tile for a dispatched block: gives each XCD one contiguous range of
 // logical tiles, so blocks resident on one XCD share K/V lines in its L2.
 __device__ __forceinline__ int xcd_remap(int b, int total) {
@@ -112,5 +126,113 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& a, int base) {
   return u32x4{pack_bf16(a[base + 0], a[base + 1]), pack_bf16(a[base + 2], a[base + 3]),
                pack_bf16(a[base + 4], a[base + 5]), pack_bf16(a[base + 6], a[base + 7])};
 }
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS tiles of 64 tokens (row-major, D bf16 per token).
+//
+// 16-byte chunk c of token row r sits at physical chunk swz<D>(r, c) of its
+// row.  The XOR mask is chosen so that both reads the MFMAs need are free of
+// bank conflicts:
+//  * A operand of K Q^T: 32 consecutive rows, one chunk each (any 16
+//    consecutive rows land in 16 distinct 16-byte bank groups);
+//  * the transposing read of V (ds_read_b64_tr_b16): 4 consecutive rows x
+//    4 consecutive chunks per 32 lanes, all distinct.
+// XOR with a row-only mask is its own inverse, so the same function maps a
+// physical slot back to its logical chunk.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int row, int c) {
+  if constexpr (D == 128) {
+    const int x = row & 15;
+    return c ^ (((x & 3) << 2) | ((x >> 2) & 3));
+  } else {
+    const int x = (row >> 1) & 7;
+    return c ^ (((x & 1) << 2) | ((x >> 1) & 3));
+  }
+}
+
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int c) {
+  return row * (D * 2) + (swz<D>(row, c) << 4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Loads tokens t0 .. t0+63 of a [n, D] bf16 matrix straight into an LDS
+// tile with global_load_lds (16 bytes per lane, 1 KB per instruction, no
+// registers).  Wave `wave` of `nw` issues its share of the 1 KB pieces.
+// Tokens past n - 1 read row n - 1 (in bounds; the kernels mask them).
+template <int D, int NW>
+__device__ __forceinline__ void load_tile_lds(uint8_t* tile, const uint16_t* base, int t0, int n, int wave,
+                                              int lane) {
+  constexpr int kPieces = kTileTokens * D * 2 / 1024;
+  constexpr int kRowsPerPiece = 1024 / (D * 2);
+  constexpr int kPerWave = kPieces / NW;
+  static_assert(kPieces % NW == 0, "tile pieces must split evenly over waves");
+  const int rin = (lane * 16) / (D * 2);
+  const int p = ((lane * 16) % (D * 2)) >> 4;
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int piece = wave * kPerWave + i;
+    const int row = piece * kRowsPerPiece + rin;
+    const int tok = (t0 + row < n) ? t0 + row : n - 1;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass never emits this device-only code
+    __builtin_amdgcn_global_load_lds(base + (size_t)tok * D + swz<D>(row, p) * 8,
+                                     (lds_void*)(tile + piece * 1024), 16, 0, 0);
+#endif
+  }
+}
+
+// 16-byte A-operand chunk of row `row`, logical chunk c, of a tile.
+template <int D>
+__device__ __forceinline__ u32x4 ld_row16(const uint8_t* tile, int row, int c) {
+  return *reinterpret_cast<const u32x4*>(tile + tile_off<D>(row, c));
+}
+
+// One ds_read_b64_tr_b16 at LDS byte address `addr`.  Issued as inline
+// assembly: the compiler cannot see which LDS buffer the intrinsic form
+// reads and would make every such read wait for all global_load_lds still in
+// flight (into any buffer).  The result is valid only after lds_wait().
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(0), tied to the registers it makes valid.
+__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
+}
+
+// A operand of O^T += V^T P^T for 32 feature rows d0 .. d0+31 and the 16
+// tokens 16*h .. 16*h+15 of 32-token block kb, read transposed from a
+// row-major V tile with two ds_read_b64_tr_b16.  In each 16-lane group the
+// lane 4a+b receives element b of the 8-byte rows given by lanes a, 4+a, 8+a
+// and 12+a; lane 4m+a therefore points at token k_m, features 4a..4a+3 of
+// its 16-feature half, and every lane gets 4 tokens of one feature.  Slot
+// 4t+m of lane l holds token 32*kb + 16*h + 4*(l/32) + 8*t + m -- the order
+// in which the S^T accumulator holds its keys.  Needs lds_wait() before use.
+template <int D>
+__device__ __forceinline__ u32x4 ld_vt(const uint8_t* tile, int d0, int kb, int h, int lane) {
+  const int m = (lane & 15) >> 2, a = lane & 3;
+  const int g = lane >> 5, half16 = (lane >> 4) & 1;
+  const int d = d0 + 16 * half16 + 4 * a;
+  const uint32_t base = lds_addr(tile) + ((d & 4) ? 8 : 0);
+  const int tok0 = 32 * kb + 16 * h + 4 * g + m;
+  const u32x2 lo = ds_read_tr16(base + tile_off<D>(tok0, d >> 3));
+  const u32x2 hi = ds_read_tr16(base + tile_off<D>(tok0 + 8, d >> 3));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// s_waitcnt vmcnt(0) (global loads, including loads into LDS, complete).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace ra

@@ -2,27 +2,39 @@
 // KV chunk with a fused log-sum-exp merge into the running output.
 //
 // Each ring step is one FlashAttention-style pass: K/V tiles are staged in
-// on-chip memory and the score tile never leaves the chip; running row
+// on-chip memory and the score tile never leaves the chip; a running row
 // maximum and running sum of exponentials make the result exact ("Training
 // Long-Context Models Without OOM: Ring Attention", "Ring Attention
 // Demystified").  The epilogue folds the step's partial into the running
-// (O, lse) in HBM ("Context Parallelism", 2 "Ring Attention", "How It Works",
-// online softmax across steps), so only O and lse cross HBM between steps.
+// (O, lse) in HBM ("Context Parallelism", 2 "Ring Attention", "How It Works":
+// online softmax merges partial results across steps), so only O and lse
+// cross HBM between steps.
 //
-// gfx950 design.  A block is 4 waves; each wave owns NQW query rows.  The
-// score tile is computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-// K (32 keys x 16 d) comes from LDS as the A operand, Q^T stays in registers
-// as the B operand for the whole kernel.  In the accumulator a lane holds one
-// query and 16 of its keys, so the softmax statistics are per-lane scalars
-// (one cross-lane exchange with lane^32 per row maximum) and the probability
-// registers are already the B operand of O^T += V^T P^T -- no shuffle.  V^T
-// is staged in LDS, transposed in registers on the way in, with its keys
-// permuted to match the accumulator's row order.  Both LDS tiles use an XOR
-// swizzle of 16-byte chunks so the 32-row MFMA operand reads are free of bank
-// conflicts.  The exponent base is 2 with scale*log2(e) folded into one FMA.
-// The running maximum is only raised when a row's tile maximum exceeds it by
-// more than 2^8 (exact: numerator and denominator share the stale maximum),
-// so the O rescale is rare.
+// gfx950 design.
+//  * A block is 4 waves (one per SIMD); each wave owns 64 query rows, so a
+//    block covers 256 rows and every K/V byte read from LDS feeds 64 queries.
+//  * Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: K (32 keys x 16 d) is the A operand read from
+//    LDS; Q^T is the B operand and stays in registers for the whole kernel.
+//    In the accumulator a lane holds one query and 16 of its keys, so the
+//    softmax statistics are per-lane scalars (one lane^32 exchange per row
+//    maximum), and the probabilities, packed to bf16, are already the B
+//    operand of O^T += V^T P^T.  V^T's A operand comes straight from the
+//    row-major V tile through ds_read_b64_tr_b16 (no transpose pass).
+//  * K and V tiles (64 keys) go global -> LDS with global_load_lds
+//    (no registers, no LDS store instructions); three K and two V buffers
+//    give every load a whole tile of compute to land, with one block barrier
+//    per tile.
+//  * Software pipeline over 32-key sub-tiles: while the VALU does the
+//    softmax of sub-tile u, the matrix cores already compute S^T of u+1;
+//    then P V of u.
+//  * exp2 with scale*log2(e) folded into one FMA; the running maximum is
+//    raised only when a row's tile maximum exceeds it by more than 2^8
+//    (exact: numerator and denominator share the stale maximum), so the
+//    O rescale is rare.
+//  * Blocks are mapped so each XCD works on one contiguous range of
+//    (head, query tile) pairs (K/V lines shared in that XCD's L2); on the
+//    diagonal chunk the longest query tiles go first.
 #include "ra_device.h"
 #include "ra_kernels.h"
 
@@ -32,40 +44,36 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyTau = 8.0f;  // log2 of the largest un-rescaled probability
 
-template <int D, int NQW>
+template <int D, int NW_, int NQW_>
 struct FwdCfg {
-  static constexpr int kThreads = 256;
-  static constexpr int kWaves = 4;
-  static constexpr int BR = kWaves * NQW;  // query rows per block
-  static constexpr int BC = 64;            // keys per tile
-  static constexpr int NCB = NQW / 32;     // 32-query column blocks per wave
-  static constexpr int NKS = D / 16;       // MFMA k-steps of Q K^T
-  static constexpr int NDB = D / 32;       // 32-row d blocks of O^T
-  static constexpr int NKB = BC / 32;      // 32-key row blocks of S^T
-  static constexpr int KCH = D / 8;        // 16-byte chunks per K row
-  static constexpr int K_BYTES = BC * D * 2;
-  static constexpr int V_BYTES = D * BC * 2;
-  static constexpr int K_ITEMS = BC * KCH;         // 16-byte K chunks per tile
-  static constexpr int KPT = K_ITEMS / kThreads;   // per thread
-  static constexpr int V_ITEMS = (D / 8) * (BC / 4);  // (8 d x 4 keys) items per tile
-  static constexpr int VPT = (V_ITEMS + kThreads - 1) / kThreads;
-  static_assert(K_ITEMS % kThreads == 0, "K tile must split evenly");
+  static constexpr int kWaves = NW_;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int NQW = NQW_;             // query rows per wave
+  static constexpr int BR = kWaves * NQW;      // query rows per block
+  static constexpr int BC = kTileTokens;       // keys per tile
+  static constexpr int NCB = NQW / 32;         // 32-query column blocks per wave
+  static constexpr int NKS = D / 16;           // MFMA k-steps of K Q^T
+  static constexpr int NDB = D / 32;           // 32-row d blocks of O^T
+  static constexpr int NKB = BC / 32;          // 32-key row blocks of S^T
+  static constexpr int TILE = BC * D * 2;      // bytes of one K or V tile
 };
 
-template <int D, int NQW, bool DIAG, bool MERGE>
-__global__ __launch_bounds__(256) void fwd_step_kernel(const uint16_t* __restrict__ qg,
+template <int D, int NW_, int NQW_, bool DIAG, bool MERGE>
+__global__ __launch_bounds__(64 * NW_) void fwd_step_kernel(const uint16_t* __restrict__ qg,
                                                        const uint16_t* __restrict__ kg,
                                                        const uint16_t* __restrict__ vg,
                                                        float* __restrict__ og,
                                                        float* __restrict__ lseg, int Sq, int Sk,
                                                        int n_qtiles, int total_tiles,
                                                        float scale_log2) {
-  using Cfg = FwdCfg<D, NQW>;
-  constexpr int BR = Cfg::BR, BC = Cfg::BC, NCB = Cfg::NCB, NKS = Cfg::NKS;
-  constexpr int NDB = Cfg::NDB, NKB = Cfg::NKB, KCH = Cfg::KCH;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::K_BYTES + Cfg::V_BYTES];
-  uint8_t* const ks = smem;
-  uint8_t* const vs = smem + Cfg::K_BYTES;
+  using Cfg = FwdCfg<D, NW_, NQW_>;
+  constexpr int NW = Cfg::kWaves, NQW = Cfg::NQW, BR = Cfg::BR, BC = Cfg::BC, NCB = Cfg::NCB;
+  constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB, TILE = Cfg::TILE;
+  // LDS: three K tiles then two V tiles.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * TILE];
+  uint8_t* const kbuf0 = smem;
+  uint8_t* const kbuf1 = smem + TILE;
+  uint8_t* const vbuf0 = smem + 3 * TILE;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
@@ -80,6 +88,14 @@ __global__ __launch_bounds__(256) void fwd_step_kernel(const uint16_t* __restric
   const uint16_t* __restrict__ qp = qg + (size_t)bh * Sq * D;
   const uint16_t* __restrict__ kp = kg + (size_t)bh * Sk * D;
   const uint16_t* __restrict__ vp = vg + (size_t)bh * Sk * D;
+
+  int kend = Sk;
+  if (DIAG) kend = min(kend, q0 + BR);
+  const int ntiles = (kend + BC - 1) / BC;
+  // Prologue loads: K(0), K(1), V(0).
+  load_tile_lds<D, NW>(kbuf0, kp, 0, Sk, wave, lane);
+  if (ntiles > 1) load_tile_lds<D, NW>(kbuf1, kp, BC, Sk, wave, lane);
+  load_tile_lds<D, NW>(vbuf0, vp, 0, Sk, wave, lane);
 
   // Q^T fragments: column = query, k = 8 consecutive d values.
   u32x4 qf[NCB][NKS];
@@ -105,101 +121,47 @@ __global__ __launch_bounds__(256) void fwd_step_kernel(const uint16_t* __restric
     lrow[cb] = 0.f;
   }
 
-  int kend = Sk;
-  if (DIAG) kend = min(kend, q0 + BR);
-  const int ntiles = (kend + BC - 1) / BC;
+  // Compute proceeds in 32-key sub-tiles u (LDS tile u/2, half u%2).
+  const int nsub = (kend + 31) / 32;
+  const int wsub = DIAG ? min(nsub, max(0, (min(qw0 + NQW, Sq) - 1) / 32 + 1)) : nsub;
 
-  // Register staging of the next K/V tile.
-  u32x4 kr[Cfg::KPT];
-  u32x4 vr[Cfg::VPT][4];
-  auto load_tile = [&](int k0) {
+  // S^T of sub-tile `half` of a K tile into `acc`.
+  auto scores = [&](f32x16 (&acc)[NCB], const uint8_t* kt, int half) {
 #pragma unroll
-    for (int i = 0; i < Cfg::KPT; ++i) {
-      const int it = tid + i * Cfg::kThreads;
-      const int r = it / KCH, c = it % KCH;
-      kr[i] = (k0 + r < Sk) ? ld16(kp + (size_t)(k0 + r) * D + c * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int i = 0; i < Cfg::VPT; ++i) {
-      const int it = tid + i * Cfg::kThreads;
-      if (it < Cfg::V_ITEMS) {
-        const int dc = it % (D / 8), kq = it / (D / 8);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int key = k0 + kq * 4 + rr;
-          vr[i][rr] = (key < Sk) ? ld16(vp + (size_t)key * D + dc * 8) : u32x4{0, 0, 0, 0};
-        }
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < Cfg::KPT; ++i) {
-      const int it = tid + i * Cfg::kThreads;
-      const int r = it / KCH, c = it % KCH;
-      *reinterpret_cast<u32x4*>(ks + row_off<D>(r, c)) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::VPT; ++i) {
-      const int it = tid + i * Cfg::kThreads;
-      if (it < Cfg::V_ITEMS) {
-        const int dc = it % (D / 8), kq = it / (D / 8);
-        store_tr4x8(vs, dc, kq, vr[i]);
-      }
-    }
-  };
-
-  load_tile(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int k0 = tile * BC;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (tile + 1 < ntiles) load_tile(k0 + BC);
-
-    // Diagonal chunk: a wave whose rows all precede this tile has nothing to do.
-    if (DIAG && k0 > qw0 + NQW - 1) continue;
-
-    f32x16 sacc[NKB][NCB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][cb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
+      const u32x4 af = ld_row16<D>(kt, half * 32 + l32, s * 2 + g);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(ks + row_off<D>(kb * 32 + l32, s * 2 + g));
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) sacc[kb][cb] = mfma32(af, qf[cb][s], sacc[kb][cb]);
-      }
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma32(af, qf[cb][s], acc[cb]);
     }
+  };
 
-    const bool need_mask = (k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0);
+  // Online softmax of sub-tile u held in `acc` (overwritten with P), then
+  // O^T += V^T P^T from half `half` of the V tile.
+  auto softmax_pv = [&](f32x16 (&acc)[NCB], int u, const uint8_t* vt, int half) {
+    const int k0 = u * 32;
+    const bool need_mask = (k0 + 32 > Sk) || (DIAG && k0 + 31 > qw0);
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int qq = qw0 + cb * 32 + l32;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int qq = qw0 + cb * 32 + l32;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= Sk || (DIAG && key > qq)) sacc[kb][cb][i] = kNegInf;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= Sk || (DIAG && key > qq)) acc[cb][i] = kNegInf;
         }
+      }
     }
-
+    u32x4 pb[2][NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][cb][i]);
-      mx = fmaxf(mx, xor32(mx)) * scale_log2;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[cb][i]);
+      mx = pair_max(mx) * scale_log2;
       if (__ballot(mx > mrow[cb] + kLazyTau) != 0) {
         const float mnew = fmaxf(mrow[cb], mx);
         const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(mrow[cb] - mnew);
@@ -213,37 +175,58 @@ __global__ __launch_bounds__(256) void fwd_step_kernel(const uint16_t* __restric
       const float mb = (mrow[cb] == kNegInf) ? 0.f : mrow[cb];
       float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(sacc[kb][cb][i], scale_log2, -mb));
-          sacc[kb][cb][i] = p;
-          ls += p;
-        }
-      lrow[cb] += ls;
-    }
-
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 pb[NCB];
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) pb[cb] = pack8(sacc[kb][cb], 8 * h);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x4 vf = ld_tr(vs, db * 32 + l32, kb, h, g);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) oacc[cb][db] = mfma32(vf, pb[cb], oacc[cb][db]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(acc[cb][i], scale_log2, -mb));
+        acc[cb][i] = p;
+        ls += p;
       }
+      lrow[cb] += ls;
+      pb[0][cb] = pack8(acc[cb], 0);
+      pb[1][cb] = pack8(acc[cb], 8);
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 vf[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vf[db] = ld_vt<D>(vt, db * 32, half, h, lane);
+      if constexpr (NDB == 4) lds_wait(vf[0], vf[1], vf[2], vf[3]);
+      else lds_wait(vf[0], vf[1]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) oacc[cb][db] = mfma32(vf[db], pb[h][cb], oacc[cb][db]);
+    }
+  };
+
+  auto kbuf = [&](int i) { return smem + i * TILE; };        // K tile T in buffer T % 3
+  auto vbuf = [&](int i) { return smem + (3 + i) * TILE; };  // V tile T in buffer T % 2
+
+  f32x16 sA[NCB], sB[NCB];
+  wait_vmem();
+  __syncthreads();
+  if (0 < wsub) scores(sA, kbuf0, 0);
+  // Iteration T: at its top K(T+1) and V(T) have landed and every wave is
+  // done with K(T-1) and V(T-1), whose buffers then receive K(T+2) and
+  // V(T+1).  Sub-step u = 2T: S^T(2T+1) from the second half of K(T) while
+  // the softmax and P V of 2T run; sub-step 2T+1: S^T(2T+2) from the first
+  // half of K(T+1) while the softmax and P V of 2T+1 run.
+  for (int T = 0; T < ntiles; ++T) {
+    wait_vmem();
+    __syncthreads();
+    if (T + 2 < ntiles) load_tile_lds<D, NW>(kbuf((T + 2) % 3), kp, (T + 2) * BC, Sk, wave, lane);
+    if (T + 1 < ntiles) load_tile_lds<D, NW>(vbuf((T + 1) & 1), vp, (T + 1) * BC, Sk, wave, lane);
+    const int u0 = 2 * T, u1 = 2 * T + 1;
+    const uint8_t* vt = vbuf(T & 1);
+    if (u0 + 1 < wsub) scores(sB, kbuf(T % 3), 1);
+    if (u0 < wsub) softmax_pv(sA, u0, vt, 0);
+    if (u1 + 1 < wsub) scores(sA, kbuf((T + 1) % 3), 0);
+    if (u1 < wsub) softmax_pv(sB, u1, vt, 1);
   }
 
   // Epilogue: this step's partial (oacc / l, m + log2 l) folded into (O, lse).
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    const float lt = lrow[cb] + xor32(lrow[cb]);
+    const float lt = pair_sum(lrow[cb]);
     const int qq = qw0 + cb * 32 + l32;
     if (qq >= Sq) continue;
     const float lse_s = (lt > 0.f) ? mrow[cb] + log2f(lt) : kNegInf;  // log2 units
@@ -284,18 +267,18 @@ __global__ __launch_bounds__(256) void fwd_step_kernel(const uint16_t* __restric
   }
 }
 
-template <int D, int NQW>
+template <int D, int NW, int NQW>
 hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
-  using Cfg = FwdCfg<D, NQW>;
+  using Cfg = FwdCfg<D, NW, NQW>;
   const int n_qtiles = (a.Sq + Cfg::BR - 1) / Cfg::BR;
   const long long total = (long long)n_qtiles * a.BH;
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   const float sl2 = a.scale * kLog2e;
   dim3 grid((unsigned)total), block(Cfg::kThreads);
-#define RA_FWD_LAUNCH(DIAG, MERGE)                                                          \
-  hipLaunchKernelGGL((fwd_step_kernel<D, NQW, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, \
-                     a.v, a.o, a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2)
+#define RA_FWD_LAUNCH(DIAG, MERGE)                                                                      \
+  hipLaunchKernelGGL((fwd_step_kernel<D, NW, NQW, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, a.v, a.o, a.lse, \
+                     a.Sq, a.Sk, n_qtiles, (int)total, sl2)
   if (a.diag) {
     if (a.merge) RA_FWD_LAUNCH(true, true);
     else RA_FWD_LAUNCH(true, false);
@@ -309,13 +292,16 @@ hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-#ifndef RA_FWD_NQW
-#define RA_FWD_NQW 32
+#ifndef RA_FWD_WAVES
+#define RA_FWD_WAVES 8
+#endif
+#ifndef RA_FWD_ROWS_PER_WAVE
+#define RA_FWD_ROWS_PER_WAVE 32
 #endif
 
 hipError_t launch_fwd_step(const FwdStepArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_cfg<128, RA_FWD_NQW>(a, stream);
-  if (a.d == 64) return launch_cfg<64, RA_FWD_NQW>(a, stream);
+  if (a.d == 128) return launch_cfg<128, RA_FWD_WAVES, RA_FWD_ROWS_PER_WAVE>(a, stream);
+  if (a.d == 64) return launch_cfg<64, RA_FWD_WAVES, RA_FWD_ROWS_PER_WAVE>(a, stream);
   return hipErrorInvalidValue;
 }
 
