@@ -159,29 +159,63 @@ __device__ __forceinline__ int tile_off(int row, int c) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// Loads tokens t0 .. t0+63 of a [n, D] bf16 matrix straight into an LDS
-// tile with global_load_lds (16 bytes per lane, 1 KB per instruction, no
-// registers).  Wave `wave` of `nw` issues its share of the 1 KB pieces.
-// Tokens past n - 1 read row n - 1 (in bounds; the kernels mask them).
+// Direct-to-LDS loading of 64-token tiles with global_load_lds (16 bytes per
+// lane, 1 KB per instruction, no registers).  Wave `wave` of NW issues its
+// share of the tile's 1 KB pieces; piece p fills LDS bytes [1024p, 1024p+1024)
+// of the tile in lane order, so lane l loads the global chunk that belongs
+// at physical slot l of the piece.  The per-lane byte offset inside a tile's
+// rows is fixed, so a full tile needs only a uniform base address.
+template <int D, int NW>
+struct TileDma {
+  static constexpr int kPieces = kTileTokens * D * 2 / 1024;
+  static constexpr int kRowsPerPiece = 1024 / (D * 2);
+  static constexpr int kPerWave = kPieces / NW;
+  static_assert(kPieces % NW == 0, "tile pieces must split evenly over waves");
+  uint32_t off[kPerWave];  // byte offset of this lane's 16 bytes from the tile's first row
+  int row[kPerWave];       // tile row of this lane's chunk
+  int piece0;              // first piece of this wave
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int rin = (lane * 16) / (D * 2);
+    const int p = ((lane * 16) % (D * 2)) >> 4;
+    piece0 = wave * kPerWave;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      row[i] = (piece0 + i) * kRowsPerPiece + rin;
+      off[i] = (uint32_t)(row[i] * D * 2 + swz<D>(row[i], p) * 16);
+    }
+  }
+
+  // Tokens t0 .. t0+63 of the [n, D] bf16 matrix at `mat` into `tile`.
+  // Tokens past n - 1 read row n - 1 (in bounds; the kernels mask them).
+  __device__ __forceinline__ void load(uint8_t* tile, const uint16_t* mat, int t0, int n) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass never emits this device-only code
+    if (t0 + kTileTokens <= n) {
+      const uint8_t* g = reinterpret_cast<const uint8_t*>(mat) + (size_t)t0 * D * 2;
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i)
+        __builtin_amdgcn_global_load_lds(g + off[i], (lds_void*)(tile + (piece0 + i) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int tok = (t0 + row[i] < n) ? t0 + row[i] : n - 1;
+        const uint8_t* g = reinterpret_cast<const uint8_t*>(mat) + (size_t)tok * D * 2 +
+                           (off[i] - (uint32_t)(row[i] * D * 2));
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + (piece0 + i) * 1024), 16, 0, 0);
+      }
+    }
+#endif
+  }
+};
+
+// Loads tokens t0 .. t0+63 of a [n, D] bf16 matrix into an LDS tile (the
+// TileDma pattern, computed on the spot).
 template <int D, int NW>
 __device__ __forceinline__ void load_tile_lds(uint8_t* tile, const uint16_t* base, int t0, int n, int wave,
                                               int lane) {
-  constexpr int kPieces = kTileTokens * D * 2 / 1024;
-  constexpr int kRowsPerPiece = 1024 / (D * 2);
-  constexpr int kPerWave = kPieces / NW;
-  static_assert(kPieces % NW == 0, "tile pieces must split evenly over waves");
-  const int rin = (lane * 16) / (D * 2);
-  const int p = ((lane * 16) % (D * 2)) >> 4;
-#pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int piece = wave * kPerWave + i;
-    const int row = piece * kRowsPerPiece + rin;
-    const int tok = (t0 + row < n) ? t0 + row : n - 1;
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass never emits this device-only code
-    __builtin_amdgcn_global_load_lds(base + (size_t)tok * D + swz<D>(row, p) * 8,
-                                     (lds_void*)(tile + piece * 1024), 16, 0, 0);
-#endif
-  }
+  TileDma<D, NW> dma;
+  dma.init(wave, lane);
+  dma.load(tile, base, t0, n);
 }
 
 // 16-byte A-operand chunk of row `row`, logical chunk c, of a tile.
@@ -197,6 +231,13 @@ __device__ __forceinline__ u32x4 ld_row16(const uint8_t* tile, int row, int c) {
 __device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
   u32x2 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_off(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
 }
 

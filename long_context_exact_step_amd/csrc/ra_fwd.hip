@@ -35,6 +35,8 @@
 //  * Blocks are mapped so each XCD works on one contiguous range of
 //    (head, query tile) pairs (K/V lines shared in that XCD's L2); on the
 //    diagonal chunk the longest query tiles go first.
+#include <type_traits>
+
 #include "ra_device.h"
 #include "ra_kernels.h"
 
@@ -69,11 +71,10 @@ __global__ __launch_bounds__(64 * NW_) void fwd_step_kernel(const uint16_t* __re
   using Cfg = FwdCfg<D, NW_, NQW_>;
   constexpr int NW = Cfg::kWaves, NQW = Cfg::NQW, BR = Cfg::BR, BC = Cfg::BC, NCB = Cfg::NCB;
   constexpr int NKS = Cfg::NKS, NDB = Cfg::NDB, TILE = Cfg::TILE;
-  // LDS: three K tiles then two V tiles.
+  // LDS: K tiles in buffers 0..2, V tiles in buffers 3..4 (TILE bytes each).
+  // K tile T sits in K buffer T % 3 and V tile T in V buffer T % 2; the
+  // main loop is unrolled by 6 so every buffer offset is an immediate.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * TILE];
-  uint8_t* const kbuf0 = smem;
-  uint8_t* const kbuf1 = smem + TILE;
-  uint8_t* const vbuf0 = smem + 3 * TILE;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
@@ -93,9 +94,11 @@ __global__ __launch_bounds__(64 * NW_) void fwd_step_kernel(const uint16_t* __re
   if (DIAG) kend = min(kend, q0 + BR);
   const int ntiles = (kend + BC - 1) / BC;
   // Prologue loads: K(0), K(1), V(0).
-  load_tile_lds<D, NW>(kbuf0, kp, 0, Sk, wave, lane);
-  if (ntiles > 1) load_tile_lds<D, NW>(kbuf1, kp, BC, Sk, wave, lane);
-  load_tile_lds<D, NW>(vbuf0, vp, 0, Sk, wave, lane);
+  TileDma<D, NW> dma;
+  dma.init(wave, lane);
+  dma.load(smem, kp, 0, Sk);
+  if (ntiles > 1) dma.load(smem + TILE, kp, BC, Sk);
+  dma.load(smem + 3 * TILE, vp, 0, Sk);
 
   // Q^T fragments: column = query, k = 8 consecutive d values.
   u32x4 qf[NCB][NKS];
@@ -125,23 +128,62 @@ __global__ __launch_bounds__(64 * NW_) void fwd_step_kernel(const uint16_t* __re
   const int nsub = (kend + 31) / 32;
   const int wsub = DIAG ? min(nsub, max(0, (min(qw0 + NQW, Sq) - 1) / 32 + 1)) : nsub;
 
-  // S^T of sub-tile `half` of a K tile into `acc`.
-  auto scores = [&](f32x16 (&acc)[NCB], const uint8_t* kt, int half) {
+  // Lane parts of the LDS addresses, fixed for the whole kernel: the K
+  // operand chunk of k-step s (row l32, chunk 2s+g of a K tile), and the two
+  // transposed-read addresses of each 32-feature block of a V tile.  Tile,
+  // half and 16-token offsets are added as immediates.
+  uint32_t kofs[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) kofs[s] = (uint32_t)tile_off<D>(l32, 2 * s + g);
+  uint32_t vaddr[NDB][2];
+  {
+    const int m = (lane & 15) >> 2, a4 = lane & 3, half16 = (lane >> 4) & 1;
+    const uint32_t vbase = lds_addr(smem) + 3 * TILE;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 32 + 16 * half16 + 4 * a4;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        vaddr[db][t] = vbase + tile_off<D>(4 * g + m + 8 * t, d >> 3) + ((d & 4) ? 8 : 0);
+    }
+  }
+
+  // S^T of sub-tile HALF of K buffer KB into `acc`.
+  auto scores = [&](f32x16 (&acc)[NCB], auto kbc, auto halfc) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(kbc)::value * TILE + decltype(halfc)::value * 32 * D * 2;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const u32x4 af = ld_row16<D>(kt, half * 32 + l32, s * 2 + g);
+      const u32x4 af = *reinterpret_cast<const u32x4*>(smem + kofs[s] + OFF);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma32(af, qf[cb][s], acc[cb]);
     }
   };
 
+  // O^T += V^T P^T for the 16 tokens h of sub-tile HALF of V buffer VB.
+  auto pv = [&](const u32x4 (&pb)[NCB], auto vbc, auto halfc, auto hc) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(vbc)::value * TILE + (32 * decltype(halfc)::value + 16 * decltype(hc)::value) * D * 2;
+    u32x4 vf[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const u32x2 lo = ds_read_tr16_off<OFF>(vaddr[db][0]);
+      const u32x2 hi = ds_read_tr16_off<OFF>(vaddr[db][1]);
+      vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    if constexpr (NDB == 4) lds_wait(vf[0], vf[1], vf[2], vf[3]);
+    else lds_wait(vf[0], vf[1]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) oacc[cb][db] = mfma32(vf[db], pb[cb], oacc[cb][db]);
+  };
+
   // Online softmax of sub-tile u held in `acc` (overwritten with P), then
-  // O^T += V^T P^T from half `half` of the V tile.
-  auto softmax_pv = [&](f32x16 (&acc)[NCB], int u, const uint8_t* vt, int half) {
+  // O^T += V^T P^T from half HALF of V buffer VB.
+  auto softmax_pv = [&](f32x16 (&acc)[NCB], int u, auto vbc, auto halfc) __attribute__((always_inline)) {
     const int k0 = u * 32;
     const bool need_mask = (k0 + 32 > Sk) || (DIAG && k0 + 31 > qw0);
     if (need_mask) {
@@ -155,7 +197,7 @@ __global__ __launch_bounds__(64 * NW_) void fwd_step_kernel(const uint16_t* __re
         }
       }
     }
-    u32x4 pb[2][NCB];
+    u32x4 pb0[NCB], pb1[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       float mx = kNegInf;
@@ -181,46 +223,47 @@ __global__ __launch_bounds__(64 * NW_) void fwd_step_kernel(const uint16_t* __re
         ls += p;
       }
       lrow[cb] += ls;
-      pb[0][cb] = pack8(acc[cb], 0);
-      pb[1][cb] = pack8(acc[cb], 8);
+      pb0[cb] = pack8(acc[cb], 0);
+      pb1[cb] = pack8(acc[cb], 8);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 vf[NDB];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) vf[db] = ld_vt<D>(vt, db * 32, half, h, lane);
-      if constexpr (NDB == 4) lds_wait(vf[0], vf[1], vf[2], vf[3]);
-      else lds_wait(vf[0], vf[1]);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) oacc[cb][db] = mfma32(vf[db], pb[h][cb], oacc[cb][db]);
-    }
+    pv(pb0, vbc, halfc, std::integral_constant<int, 0>{});
+    pv(pb1, vbc, halfc, std::integral_constant<int, 1>{});
   };
 
-  auto kbuf = [&](int i) { return smem + i * TILE; };        // K tile T in buffer T % 3
-  auto vbuf = [&](int i) { return smem + (3 + i) * TILE; };  // V tile T in buffer T % 2
-
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   f32x16 sA[NCB], sB[NCB];
   wait_vmem();
   __syncthreads();
-  if (0 < wsub) scores(sA, kbuf0, 0);
-  // Iteration T: at its top K(T+1) and V(T) have landed and every wave is
-  // done with K(T-1) and V(T-1), whose buffers then receive K(T+2) and
-  // V(T+1).  Sub-step u = 2T: S^T(2T+1) from the second half of K(T) while
-  // the softmax and P V of 2T run; sub-step 2T+1: S^T(2T+2) from the first
-  // half of K(T+1) while the softmax and P V of 2T+1 run.
-  for (int T = 0; T < ntiles; ++T) {
+  if (0 < wsub) scores(sA, I0{}, I0{});
+  // Iteration T (T % 6 == I): at its top K(T+1) and V(T) have landed and
+  // every wave is done with K(T-1) and V(T-1), whose buffers then receive
+  // K(T+2) and V(T+1).  Sub-step 2T: S^T(2T+1) from the second half of K(T)
+  // while the softmax and P V of 2T run; sub-step 2T+1: S^T(2T+2) from the
+  // first half of K(T+1) while the softmax and P V of 2T+1 run.
+  auto iteration = [&](auto ic, int T) __attribute__((always_inline)) {
+    constexpr int I = decltype(ic)::value;
+    using KC = std::integral_constant<int, I % 3>;
+    using KN = std::integral_constant<int, (I + 1) % 3>;
+    using VC = std::integral_constant<int, I % 2>;
+    constexpr int KL = (I + 2) % 3, VN = (I + 1) % 2;
     wait_vmem();
     __syncthreads();
-    if (T + 2 < ntiles) load_tile_lds<D, NW>(kbuf((T + 2) % 3), kp, (T + 2) * BC, Sk, wave, lane);
-    if (T + 1 < ntiles) load_tile_lds<D, NW>(vbuf((T + 1) & 1), vp, (T + 1) * BC, Sk, wave, lane);
+    if (T + 2 < ntiles) dma.load(smem + KL * TILE, kp, (T + 2) * BC, Sk);
+    if (T + 1 < ntiles) dma.load(smem + (3 + VN) * TILE, vp, (T + 1) * BC, Sk);
     const int u0 = 2 * T, u1 = 2 * T + 1;
-    const uint8_t* vt = vbuf(T & 1);
-    if (u0 + 1 < wsub) scores(sB, kbuf(T % 3), 1);
-    if (u0 < wsub) softmax_pv(sA, u0, vt, 0);
-    if (u1 + 1 < wsub) scores(sA, kbuf((T + 1) % 3), 0);
-    if (u1 < wsub) softmax_pv(sB, u1, vt, 1);
+    if (u0 + 1 < wsub) scores(sB, KC{}, I1{});
+    if (u0 < wsub) softmax_pv(sA, u0, VC{}, I0{});
+    if (u1 + 1 < wsub) scores(sA, KN{}, I0{});
+    if (u1 < wsub) softmax_pv(sB, u1, VC{}, I1{});
+  };
+  for (int T = 0; T < ntiles; T += 6) {
+    iteration(std::integral_constant<int, 0>{}, T);
+    if (T + 1 < ntiles) iteration(std::integral_constant<int, 1>{}, T + 1);
+    if (T + 2 < ntiles) iteration(std::integral_constant<int, 2>{}, T + 2);
+    if (T + 3 < ntiles) iteration(std::integral_constant<int, 3>{}, T + 3);
+    if (T + 4 < ntiles) iteration(std::integral_constant<int, 4>{}, T + 4);
+    if (T + 5 < ntiles) iteration(std::integral_constant<int, 5>{}, T + 5);
   }
 
   // Epilogue: this step's partial (oacc / l, m + log2 l) folded into (O, lse).
