@@ -165,9 +165,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // of the tile in lane order, so lane l loads the global chunk that belongs
 // at physical slot l of the piece.  The per-lane byte offset inside a tile's
 // rows is fixed, so a full tile needs only a uniform base address.
-template <int D, int NW>
+template <int D, int NW, int TOK = kTileTokens>
 struct TileDma {
-  static constexpr int kPieces = kTileTokens * D * 2 / 1024;
+  static constexpr int kPieces = TOK * D * 2 / 1024;
   static constexpr int kRowsPerPiece = 1024 / (D * 2);
   static constexpr int kPerWave = kPieces / NW;
   static_assert(kPieces % NW == 0, "tile pieces must split evenly over waves");
@@ -186,11 +186,11 @@ struct TileDma {
     }
   }
 
-  // Tokens t0 .. t0+63 of the [n, D] bf16 matrix at `mat` into `tile`.
+  // Tokens t0 .. t0+TOK-1 of the [n, D] bf16 matrix at `mat` into `tile`.
   // Tokens past n - 1 read row n - 1 (in bounds; the kernels mask them).
   __device__ __forceinline__ void load(uint8_t* tile, const uint16_t* mat, int t0, int n) const {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass never emits this device-only code
-    if (t0 + kTileTokens <= n) {
+    if (t0 + TOK <= n) {
       const uint8_t* g = reinterpret_cast<const uint8_t*>(mat) + (size_t)t0 * D * 2;
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i)

@@ -1,0 +1,285 @@
+"""GPU parity on the five ring-attention workloads at their full sizes, in the
+launch configuration bench.py times (double-buffered ring walk with a copy
+stream).
+
+* Tiny ring (S=512, P=4, d=64, non-causal) and the full ring (S=32K, P=8,
+  every rank): every row of O and lse against the fp64 oracle.
+* 128K/CP=4 and 1M/CP=8 local shares: 256 seeded query rows per head against
+  the oracle, plus closed forms checked on every row: Q = 0 makes every
+  visible score 0, so lse_p = ln(p + 1) and O_p is the mean of V over the
+  visible prefix; V = 1 makes O = 1.
+* Training share (C=16K, P=4, rank 3): O/lse and dQ on 256 sampled query
+  rows per head, dK/dV on 256 sampled key rows per chunk for 4 heads, and on
+  every key the sums that hold exactly: sum_k dK_k = 0 and
+  sum_k dV_k = sum_q dO_q.
+
+The oracle runs on the host, fanned out over heads with one BLAS thread per
+task.
+"""
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+from threadpoolctl import threadpool_limits
+
+import long_context_exact_step_amd as ra
+import oracle
+from long_context_exact_step_amd import inputs
+from long_context_exact_step_amd.workloads import WORKLOADS
+from parity import TOL_GRAD, TOL_LSE, TOL_O, TOL_REL, assert_close, dev, f64, workers
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def gen_workload(w, ranks=None, with_do=False):
+    ranks = w.ranks if ranks is None else ranks
+    q = {r: inputs.chunk(w.id, inputs.Q, r, w.B, w.H, w.C, w.d) for r in ranks}
+    k = [inputs.chunk(w.id, inputs.K, j, w.B, w.H, w.C, w.d) for j in range(w.P)]
+    v = [inputs.chunk(w.id, inputs.V, j, w.B, w.H, w.C, w.d) for j in range(w.P)]
+    do = {r: inputs.chunk(w.id, inputs.DO, r, w.B, w.H, w.C, w.d) for r in ranks} if with_do else None
+    return q, k, v, do
+
+
+def gpu_ring_fwd(w, rank, q, kd, vd, mode="double_buffer"):
+    o = torch.full((w.B, w.H, w.C, w.d), float("nan"), device=dev())
+    lse = torch.full((w.B, w.H, w.C), float("nan"), device=dev())
+    cs = torch.cuda.Stream(dev()) if mode == "double_buffer" else None
+    ra.ring_fwd(q.to(dev()), kd, vd, o, lse, rank, w.causal, w.scale, ring_mode=mode, copy_stream=cs)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def head_full(chunks, h):
+    """fp64 [1, 1, P*C, d] of one head over the unchunked sequence."""
+    return np.concatenate([f64(c[:, h:h + 1]) for c in chunks], axis=2)
+
+
+def fan_out(fn, items):
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=workers()) as ex:
+        return list(ex.map(fn, items))
+
+
+def check_rows(w, rank, q, k, v, o, lse, rows_of_head, label):
+    """Oracle on rows_of_head(h) of every head vs the GPU (o, lse)."""
+    o_c, l_c = o.cpu(), lse.cpu()
+
+    def one(h):
+        rows = rows_of_head(h)
+        kh, vh = head_full(k, h), head_full(v, h)
+        qh = f64(q[:, h:h + 1, rows])
+        ro, rl = oracle.attention_fwd(qh, kh, vh, w.scale, w.causal, q_pos=rank * w.C + rows)
+        go, gl = f64(o_c[:, h:h + 1, rows]), f64(l_c[:, h:h + 1, rows])
+        return (np.abs(go - ro).max(), np.abs(gl - rl).max(),
+                np.linalg.norm(go - ro) ** 2, np.linalg.norm(ro) ** 2, np.isfinite(go).all())
+
+    res = fan_out(one, range(w.H))
+    err_o = max(r[0] for r in res)
+    err_l = max(r[1] for r in res)
+    rel = math.sqrt(sum(r[2] for r in res) / sum(r[3] for r in res))
+    say(f"{label}: max|dO|={err_o:.2e} max|dlse|={err_l:.2e} rel={rel:.2e}")
+    assert all(r[4] for r in res), f"{label}: non-finite output"
+    assert err_o <= TOL_O, f"{label}: O max abs err {err_o}"
+    assert err_l <= TOL_LSE, f"{label}: lse max abs err {err_l}"
+    assert rel <= TOL_REL, f"{label}: O relative err {rel}"
+
+
+# ---------------------------------------------------------------------------
+# Tiny ring, every rank, every row, both ring modes.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", ["double_buffer", "resident"])
+def test_tiny_ring_all_rows(mode):
+    w = WORKLOADS[1]
+    q, k, v, _ = gen_workload(w)
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    for r in w.ranks:
+        say(f"tiny ring rank {r} mode {mode}")
+        o, lse = gpu_ring_fwd(w, r, q[r], kd, vd, mode)
+        check_rows(w, r, q[r], k, v, o, lse, lambda h: np.arange(w.C), f"tiny rank {r}")
+
+
+# ---------------------------------------------------------------------------
+# Full ring S=32K, P=8: every rank, every row.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.timeout(600)
+def test_full_ring_all_rows():
+    w = WORKLOADS[3]
+    q, k, v, _ = gen_workload(w)
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    for r in w.ranks:
+        say(f"full ring rank {r}: GPU walk, then oracle on all {w.C} rows x {w.H} heads")
+        o, lse = gpu_ring_fwd(w, r, q[r], kd, vd)
+        check_rows(w, r, q[r], k, v, o, lse, lambda h: np.arange(w.C), f"full ring rank {r}")
+
+
+# ---------------------------------------------------------------------------
+# 128K/CP=4 and 1M/CP=8 local shares.
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def share_inputs():
+    cache = {}
+
+    def get(wid):
+        if wid not in cache:
+            cache.clear()
+            w = WORKLOADS[wid]
+            say(f"generating inputs of {w.name}")
+            q, k, v, _ = gen_workload(w)
+            cache[wid] = (q, k, v, [t.to(dev()) for t in k], [t.to(dev()) for t in v])
+        return cache[wid]
+
+    yield get
+    cache.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("wid", [2, 4])
+def test_local_share_sampled_rows(wid, share_inputs):
+    w = WORKLOADS[wid]
+    r = w.ranks[0]
+    q, k, v, kd, vd = share_inputs(wid)
+    say(f"{w.name}: GPU walk")
+    o, lse = gpu_ring_fwd(w, r, q[r], kd, vd)
+    check_rows(w, r, q[r], k, v, o, lse, lambda h: inputs.query_row_sample(w.id, h, w.C),
+               f"{w.name} sampled rows")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("wid", [2, 4])
+def test_local_share_closed_forms_every_row(wid, share_inputs):
+    w = WORKLOADS[wid]
+    r = w.ranks[0]
+    q, k, v, kd, vd = share_inputs(wid)
+    pos = r * w.C + np.arange(w.C)
+
+    say(f"{w.name}: Q = 0 (lse = ln(p+1), O = prefix mean of V)")
+    o, lse = gpu_ring_fwd(w, r, torch.zeros_like(q[r]), kd, vd)
+    o_c, l_c = o.cpu(), lse.cpu()
+    want_l = np.log(pos + 1.0)
+
+    def one(h):
+        vh = head_full(v, h)[0, 0]
+        pref = (np.cumsum(vh, axis=0)[pos] / (pos + 1)[:, None])
+        return (np.abs(f64(o_c[0, h]) - pref).max(), np.abs(f64(l_c[0, h]) - want_l).max())
+
+    res = fan_out(one, range(w.H))
+    err_o, err_l = max(x[0] for x in res), max(x[1] for x in res)
+    say(f"  max|O - prefix mean|={err_o:.2e} max|lse - ln(p+1)|={err_l:.2e}")
+    assert err_o <= TOL_O and err_l <= TOL_LSE
+
+    say(f"{w.name}: V = 1 (O = 1)")
+    ones = [torch.ones_like(t) for t in vd]
+    o, lse = gpu_ring_fwd(w, r, q[r], kd, ones)
+    err = (o - 1).abs().max().item()
+    say(f"  max|O - 1|={err:.2e}")
+    assert err <= TOL_O
+    assert torch.isfinite(lse).all()
+
+
+# ---------------------------------------------------------------------------
+# Training share: forward + backward.
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def train_run():
+    w = WORKLOADS[5]
+    r = w.ranks[0]
+    say(f"{w.name}: inputs")
+    q, k, v, do = gen_workload(w, with_do=True)
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    o, lse = gpu_ring_fwd(w, r, q[r], kd, vd)
+    dq = torch.full_like(o, float("nan"))
+    dk = [torch.zeros(w.B, w.H, w.C, w.d, device=dev()) for _ in range(w.P)]
+    dv = [torch.zeros(w.B, w.H, w.C, w.d, device=dev()) for _ in range(w.P)]
+    say(f"{w.name}: GPU backward walk")
+    ra.ring_bwd(q[r].to(dev()), kd, vd, o, lse, do[r].to(dev()), dq, dk, dv, r, w.causal, w.scale)
+    torch.cuda.synchronize()
+    out = dict(w=w, r=r, q=q[r], k=k, v=v, do=do[r], o=o.cpu(), lse=lse.cpu(), dq=dq.cpu(),
+               dk=[t.cpu() for t in dk], dv=[t.cpu() for t in dv])
+    del kd, vd, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return out
+
+
+@pytest.mark.timeout(600)
+def test_train_forward_and_dq_sampled_rows(train_run):
+    t = train_run
+    w, r = t["w"], t["r"]
+
+    def one(h):
+        rows = inputs.query_row_sample(w.id, h, w.C)
+        kh, vh = head_full(t["k"], h), head_full(t["v"], h)
+        qh, doh = f64(t["q"][:, h:h + 1, rows]), f64(t["do"][:, h:h + 1, rows])
+        pos = r * w.C + rows
+        ro, rl = oracle.attention_fwd(qh, kh, vh, w.scale, True, q_pos=pos)
+        rq, _, _ = oracle.attention_bwd(qh, kh, vh, doh, w.scale, True, q_pos=pos)
+        go, gl, gq = (f64(t[n][:, h:h + 1, rows]) for n in ("o", "lse", "dq"))
+        return (np.abs(go - ro).max(), np.abs(gl - rl).max(), np.abs(gq - rq).max(),
+                np.linalg.norm(gq - rq) ** 2, np.linalg.norm(rq) ** 2)
+
+    say(f"{w.name}: oracle forward + dQ on 256 rows x {w.H} heads")
+    res = fan_out(one, range(w.H))
+    e_o, e_l, e_q = (max(x[i] for x in res) for i in range(3))
+    rel_q = math.sqrt(sum(x[3] for x in res) / sum(x[4] for x in res))
+    say(f"  max|dO|={e_o:.2e} max|dlse|={e_l:.2e} max|ddQ|={e_q:.2e} rel dQ={rel_q:.2e}")
+    assert e_o <= TOL_O and e_l <= TOL_LSE and e_q <= TOL_GRAD and rel_q <= TOL_REL
+
+
+@pytest.mark.timeout(900)
+def test_train_dk_dv_sampled_key_rows(train_run):
+    t = train_run
+    w, r = t["w"], t["r"]
+    heads = [0, 11, 22, 31]
+    pos = r * w.C + np.arange(w.C)
+
+    def one(h):
+        kh, vh = head_full(t["k"], h), head_full(t["v"], h)
+        qh, doh = f64(t["q"][:, h:h + 1]), f64(t["do"][:, h:h + 1])
+        per_chunk = [inputs.key_row_sample(w.id, h, j, w.C) for j in range(w.P)]
+        all_rows = np.concatenate([j * w.C + rows for j, rows in enumerate(per_chunk)])
+        rk, rv = oracle.attention_bwd_key_rows(qh, kh, vh, doh, w.scale, True, all_rows, q_pos=pos)
+        errs = []
+        n0 = 0
+        for j, rows in enumerate(per_chunk):
+            sl = slice(n0, n0 + len(rows))
+            n0 += len(rows)
+            gk, gv = f64(t["dk"][j][:, h:h + 1, rows]), f64(t["dv"][j][:, h:h + 1, rows])
+            errs.append((np.abs(gk - rk[:, :, sl]).max(), np.abs(gv - rv[:, :, sl]).max(),
+                         np.linalg.norm(gk - rk[:, :, sl]) ** 2 + np.linalg.norm(gv - rv[:, :, sl]) ** 2,
+                         np.linalg.norm(rk[:, :, sl]) ** 2 + np.linalg.norm(rv[:, :, sl]) ** 2))
+        return errs
+
+    say(f"{w.name}: oracle dK/dV on 256 key rows x {w.P} chunks x heads {heads}")
+    res = [e for per_head in fan_out(one, heads) for e in per_head]
+    e_k, e_v = max(x[0] for x in res), max(x[1] for x in res)
+    rel = math.sqrt(sum(x[2] for x in res) / sum(x[3] for x in res))
+    say(f"  max|ddK|={e_k:.2e} max|ddV|={e_v:.2e} rel={rel:.2e}")
+    assert e_k <= TOL_GRAD and e_v <= TOL_GRAD and rel <= TOL_REL
+
+
+def test_train_gradient_sums_every_key(train_run):
+    t = train_run
+    w = t["w"]
+    dk = torch.cat(t["dk"], dim=2).double()
+    dv = torch.cat(t["dv"], dim=2).double()
+    sum_dk = dk.sum(dim=2)
+    scale_k = dk.abs().sum(dim=2)
+    sum_dv = dv.sum(dim=2)
+    sum_do = t["do"].double().sum(dim=2)
+    r_k = (sum_dk.abs() / scale_k.clamp_min(1e-30)).max().item()
+    r_v = ((sum_dv - sum_do).abs().max() / sum_do.abs().max()).item()
+    say(f"{w.name}: max|sum dK|/sum|dK|={r_k:.2e}  max|sum dV - sum dO|/max|sum dO|={r_v:.2e}")
+    assert r_k <= 1e-3 and r_v <= 1e-3
