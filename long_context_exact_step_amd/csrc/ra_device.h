@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
+#include <utility>
 
 namespace ra {
 
@@ -247,6 +249,50 @@ __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b, u32x4& c, u32x4& d)
 }
 __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+
+// One ds_read_b128 at LDS byte address addr + OFF, as inline assembly like
+// ds_read_tr16_off (valid only after a wait that names the result).
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128_off(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Waits until at most N LDS operations of this wave are outstanding.  LDS
+// operations complete in issue order, so when N counts only reads issued
+// after the one that produced the tied registers, those registers are valid
+// afterwards; tying them orders their consumers after the wait.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& a) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x2& a, u32x2& b) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
+// Workgroup barrier that no instruction is scheduled across, with no memory
+// fence: every LDS read before it has already been waited for by its consumer,
+// and LDS-DMA completion is waited for explicitly (wait_vmem) where needed.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {

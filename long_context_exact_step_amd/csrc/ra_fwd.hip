@@ -47,82 +47,96 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyTau = 8.0f;  // log2 of the largest un-rescaled probability
 
 
-// Epilogue shared by the forward kernels: this step's partial
-// (oacc / l, m + log2 l) folded into the running (O, lse) of the lane's rows.
-template <int D, int NCB, bool MERGE>
-__device__ __forceinline__ void fwd_epilogue(const f32x16 (&oacc)[NCB][D / 32], const float (&mrow)[NCB],
-                                             const float (&lrow)[NCB], float* __restrict__ og,
-                                             float* __restrict__ lseg, int bh, int Sq, int qw0, int l32, int g) {
+// Epilogue: this step's partial (oacc / l, m + log2 l) of the lane's query
+// row folded into the running (O, lse).
+template <int D, bool MERGE>
+__device__ __forceinline__ void fwd_epilogue(const f32x16 (&oacc)[D / 32], float mrow, float lrow,
+                                             float* __restrict__ og, float* __restrict__ lseg, int bh, int Sq,
+                                             int qq, int g) {
   constexpr int NDB = D / 32;
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const float lt = pair_sum(lrow[cb]);
-    const int qq = qw0 + cb * 32 + l32;
-    if (qq >= Sq) continue;
-    const float lse_s = (lt > 0.f) ? mrow[cb] + log2f(lt) : kNegInf;  // log2 units
-    float w_old = 0.f, w_step, lse_new;
-    float* orow = og + ((size_t)bh * Sq + qq) * D;
-    float* lp = lseg + (size_t)bh * Sq + qq;
-    if (MERGE) {
-      const float lold = *lp * kLog2e;
-      const float M = fmaxf(lold, lse_s);
-      if (M == kNegInf) {
-        lse_new = kNegInf;
-        w_step = 0.f;
-      } else {
-        const float eo = exp2f(lold - M), es = exp2f(lse_s - M);
-        const float tot = eo + es;
-        lse_new = M + log2f(tot);
-        w_old = eo / tot;
-        w_step = (lt > 0.f) ? es / tot / lt : 0.f;
-      }
+  const float lt = pair_sum(lrow);
+  if (qq >= Sq) return;
+  const float lse_s = (lt > 0.f) ? mrow + log2f(lt) : kNegInf;  // log2 units
+  float w_old = 0.f, w_step, lse_new;
+  float* orow = og + ((size_t)bh * Sq + qq) * D;
+  float* lp = lseg + (size_t)bh * Sq + qq;
+  if (MERGE) {
+    const float lold = *lp * kLog2e;
+    const float M = fmaxf(lold, lse_s);
+    if (M == kNegInf) {
+      lse_new = kNegInf;
+      w_step = 0.f;
     } else {
-      lse_new = lse_s;
-      w_step = (lt > 0.f) ? 1.f / lt : 0.f;
+      const float eo = exp2f(lold - M), es = exp2f(lse_s - M);
+      const float tot = eo + es;
+      lse_new = M + log2f(tot);
+      w_old = eo / tot;
+      w_step = (lt > 0.f) ? es / tot / lt : 0.f;
     }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float* dst = orow + db * 32 + 8 * j + 4 * g;
-        f32x4 val = {oacc[cb][db][4 * j + 0] * w_step, oacc[cb][db][4 * j + 1] * w_step,
-                     oacc[cb][db][4 * j + 2] * w_step, oacc[cb][db][4 * j + 3] * w_step};
-        if (MERGE) {
-          const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
-          val += w_old * old;
-        }
-        *reinterpret_cast<f32x4*>(dst) = val;
-      }
-    if (g == 0) *lp = lse_new * kLn2;
+  } else {
+    lse_new = lse_s;
+    w_step = (lt > 0.f) ? 1.f / lt : 0.f;
   }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float* dst = orow + db * 32 + 8 * j + 4 * g;
+      f32x4 val = {oacc[db][4 * j + 0] * w_step, oacc[db][4 * j + 1] * w_step, oacc[db][4 * j + 2] * w_step,
+                   oacc[db][4 * j + 3] * w_step};
+      if (MERGE) {
+        const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+        val += w_old * old;
+      }
+      *reinterpret_cast<f32x4*>(dst) = val;
+    }
+  if (g == 0) *lp = lse_new * kLn2;
 }
 
-// One ring step.  A block is NW waves; wave w owns NQW query rows.  Step t
-// of the key loop computes S^T for the next whole 64-key tile (two 32-key
-// blocks) while the online softmax of tile t runs, then O^T += V^T P^T of
-// tile t.  Two K and two V buffers: K(t+2) overwrites K(t), whose last reader
-// (S^T(t)) ran in the previous iteration.
-template <int D, int NW_, int NQW_, bool DIAG, bool MERGE>
-__global__ __launch_bounds__(64 * NW_) void fwd_step_kernel(const uint16_t* __restrict__ qg,
-                                                                const uint16_t* __restrict__ kg,
-                                                                const uint16_t* __restrict__ vg,
-                                                                float* __restrict__ og,
-                                                                float* __restrict__ lseg, int Sq, int Sk,
-                                                                int n_qtiles, int total_tiles,
-                                                                float scale_log2) {
-  constexpr int NW = NW_, NQW = NQW_, BR = NW * NQW, BC = kTileTokens, NCB = NQW / 32;
-  constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2;
+// LDS reads still in flight after those of MFMA m, when the reads of MFMAs
+// m+1 .. m+LA have been issued; the first NPV MFMAs take two reads each.
+__host__ __device__ constexpr int reads_after(int m, int LA, int NPV, int NOP) {
+  int n = 0;
+  for (int k = m + 1; k <= m + LA && k < NOP; ++k) n += (k < NPV) ? 2 : 1;
+  return n;
+}
+
+constexpr int kFwdWaves = 8;       // waves per block; waves w and w + 4 share a SIMD
+constexpr int kFwdRowsPerWave = 32;
+constexpr int kFwdLookahead = 6;   // MFMAs whose LDS operands are read ahead
+
+// One ring step.  A block holds 256 query rows, 32 per wave, and walks the
+// chunk's keys in 64-key tiles.  Per tile a wave runs two phases:
+//   MFMA phase of tile t:     O^T += V^T P^T(t-1), then S^T(t) = K(t) Q^T;
+//   softmax phase of tile t:  the online softmax of S^T(t) -> P^T(t) in bf16.
+// Waves 4..7 run one phase behind waves 0..3, with a workgroup barrier
+// between phases, so on every SIMD one wave keeps the matrix core busy while
+// the other computes exponentials.  Phase 2u starts the loads of K(u+1) and
+// V(u) (two buffers each); they are waited for at the end of phase 2u+1,
+// before anyone reads them in phase 2u+2.
+template <int D, bool DIAG, bool MERGE>
+__global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t* __restrict__ qg,
+                                                                  const uint16_t* __restrict__ kg,
+                                                                  const uint16_t* __restrict__ vg,
+                                                                  float* __restrict__ og,
+                                                                  float* __restrict__ lseg, int Sq, int Sk,
+                                                                  int n_qtiles, int total_tiles,
+                                                                  float scale_log2) {
+  constexpr int NW = kFwdWaves, NQW = kFwdRowsPerWave, BR = NW * NQW, BC = kTileTokens;
+  constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kFwdLookahead;
   // LDS: K tiles in buffers 0..1, V tiles in buffers 2..3; tile t uses buffer t % 2.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
+  const bool lead = wave < NW / 2;
   const int t = xcd_remap(blockIdx.x, total_tiles);
   const int bh = t / n_qtiles;
   int qt = t - bh * n_qtiles;
   if (DIAG) qt = n_qtiles - 1 - qt;  // longest rows of the triangle first
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * NQW;
+  const int qq = qw0 + l32;
   const uint16_t* __restrict__ qp = qg + (size_t)bh * Sq * D;
   const uint16_t* __restrict__ kp = kg + (size_t)bh * Sk * D;
   const uint16_t* __restrict__ vp = vg + (size_t)bh * Sk * D;
@@ -135,197 +149,188 @@ __global__ __launch_bounds__(64 * NW_) void fwd_step_kernel(const uint16_t* __re
   TileDma<D, NW, BC> dma;
   dma.init(wave, lane);
   dma.load(smem, kp, 0, Sk);
-  if (ntiles > 1) dma.load(smem + TILE, kp, BC, Sk);
-  dma.load(smem + 2 * TILE, vp, 0, Sk);
+  dma.load(smem + 3 * TILE, vp, 0, Sk);  // finite data for the P = 0 product of tile 0
 
-  u32x4 qf[NCB][NKS];
+  u32x4 qf[NKS];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int qq = qw0 + cb * 32 + l32;
+  for (int s = 0; s < NKS; ++s) qf[s] = (qq < Sq) ? ld16(qp + (size_t)qq * D + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
+  f32x16 oacc[NDB];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s)
-      qf[cb][s] = (qq < Sq) ? ld16(qp + (size_t)qq * D + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
-  }
-  f32x16 oacc[NCB][NDB];
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float mrow = kNegInf, lrow = 0.f;
+  f32x16 sacc[NKB];
+  u32x4 pb[NKB][2];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[cb][db][i] = 0.f;
-  float mrow[NCB], lrow[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    mrow[cb] = kNegInf;
-    lrow[cb] = 0.f;
-  }
+  for (int kb = 0; kb < NKB; ++kb) pb[kb][0] = pb[kb][1] = u32x4{0, 0, 0, 0};
 
-  uint32_t kofs[NKS];
+  const uint32_t base = lds_addr(smem);
+  uint32_t kaddr[NKS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) kofs[s] = (uint32_t)tile_off<D>(l32, 2 * s + g);
+  for (int s = 0; s < NKS; ++s) kaddr[s] = base + (uint32_t)tile_off<D>(l32, 2 * s + g);
   uint32_t vaddr[NDB][2];
   {
     const int m = (lane & 15) >> 2, a4 = lane & 3, half16 = (lane >> 4) & 1;
-    const uint32_t vbase = lds_addr(smem) + 2 * TILE;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int d = db * 32 + 16 * half16 + 4 * a4;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        vaddr[db][tt] = vbase + tile_off<D>(4 * g + m + 8 * tt, d >> 3) + ((d & 4) ? 8 : 0);
+        vaddr[db][tt] = base + tile_off<D>(4 * g + m + 8 * tt, d >> 3) + ((d & 4) ? 8 : 0);
     }
   }
 
-  // S^T of K buffer KB (both 32-key blocks) into `acc`.
-  auto scores = [&](f32x16 (&acc)[NKB][NCB], auto kbc) __attribute__((always_inline)) {
-    constexpr int OFF = decltype(kbc)::value * TILE;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[kb][cb][i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(smem + kofs[s] + OFF + kb * 32 * D * 2);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[kb][cb] = mfma32(af, qf[cb][s], acc[kb][cb]);
+  // MFMA phase: O^T += V^T P^T from V buffer VB, then S^T from K buffer KB
+  // into sacc.  The LDS operands of the next LA MFMAs are always in flight;
+  // each MFMA waits only for its own.
+  auto mfma_phase = [&](auto kbc, auto vbc) __attribute__((always_inline)) {
+    constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
+    constexpr int NPV = 4 * NDB, NOP = NPV + NKS * NKB;
+    u32x2 lo[LA + 1], hi[LA + 1];
+    u32x4 kq[LA + 1];
+    auto issue = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value, b = m % (LA + 1);
+      if constexpr (m < NPV) {
+        // V^T block db for tokens 32*(gi/2) + 16*(gi%2) .. +15.
+        constexpr int gi = m / NDB, db = m % NDB;
+        constexpr int OFF = (2 + VB) * TILE + (32 * (gi >> 1) + 16 * (gi & 1)) * D * 2;
+        lo[b] = ds_read_tr16_off<OFF>(vaddr[db][0]);
+        hi[b] = ds_read_tr16_off<OFF>(vaddr[db][1]);
+      } else if constexpr (m < NOP) {
+        constexpr int j = m - NPV, s = j / NKB, kb = j % NKB;
+        kq[b] = ds_read_b128_off<KB * TILE + kb * 32 * D * 2>(kaddr[s]);
       }
+    };
+    auto run = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value, b = m % (LA + 1);
+      constexpr int N = reads_after(m, LA, NPV, NOP);
+      issue(std::integral_constant<int, m + LA>{});
+      if constexpr (m < NPV) {
+        constexpr int gi = m / NDB, db = m % NDB;
+        lgkm_wait<N>(lo[b], hi[b]);
+        const u32x4 a = {lo[b][0], lo[b][1], hi[b][0], hi[b][1]};
+        oacc[db] = mfma32(a, pb[gi >> 1][gi & 1], oacc[db]);
+      } else {
+        constexpr int j = m - NPV, s = j / NKB, kb = j % NKB;
+        lgkm_wait<N>(kq[b]);
+        if constexpr (s == 0) sacc[kb] = mfma32(kq[b], qf[0], f32x16{});
+        else sacc[kb] = mfma32(kq[b], qf[s], sacc[kb]);
+      }
+    };
+    static_for<LA>(issue);
+    static_for<NOP>(run);
   };
 
-  // O^T += V^T P^T for tokens 32*KB2 + 16*H of V buffer VB.
-  auto pv = [&](const u32x4 (&pb)[NCB], auto vbc, auto kbc, auto hc) __attribute__((always_inline)) {
-    constexpr int OFF =
-        decltype(vbc)::value * TILE + (32 * decltype(kbc)::value + 16 * decltype(hc)::value) * D * 2;
-    u32x4 vf[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const u32x2 lo = ds_read_tr16_off<OFF>(vaddr[db][0]);
-      const u32x2 hi = ds_read_tr16_off<OFF>(vaddr[db][1]);
-      vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-    if constexpr (NDB == 4) lds_wait(vf[0], vf[1], vf[2], vf[3]);
-    else lds_wait(vf[0], vf[1]);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) oacc[cb][db] = mfma32(vf[db], pb[cb], oacc[cb][db]);
-  };
-
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  // Step t: S^T(t+1) into `nxt` from K buffer KBN while the online softmax of
-  // tile t (in `cur`) runs, then O^T += V^T P^T from V buffer VB.
-  auto step = [&](f32x16 (&cur)[NKB][NCB], f32x16 (&nxt)[NKB][NCB], int tile, auto kbn, auto vbc)
-                  __attribute__((always_inline)) {
-    if (tile >= wtiles) return;
-    const int k0 = tile * BC;
+  // Softmax phase of tile tt: mask, running maximum (raised lazily), P in
+  // bf16 into pb, running sum, and the rare rescale of O.
+  auto softmax_phase = [&](int tt) __attribute__((always_inline)) {
+    const int k0 = tt * BC;
     if ((k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0)) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int qq = qw0 + cb * 32 + l32;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= Sk || (DIAG && key > qq)) cur[kb][cb][i] = kNegInf;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= Sk || (DIAG && key > qq)) sacc[kb][i] = kNegInf;
         }
     }
-    scores(nxt, kbn);
-    float mnew[NCB], ls[NCB];
-    bool grow = false;
-    u32x4 pb[NKB][2][NCB];
+    // Row maximum as a tree (short dependency chains).
+    float mp[4];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      float mx = kNegInf;
+    for (int j = 0; j < 4; ++j) mp[j] = fmaxf(fmaxf(sacc[j >> 1][8 * (j & 1)], sacc[j >> 1][8 * (j & 1) + 1]),
+                                            sacc[j >> 1][8 * (j & 1) + 2]);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, cur[kb][cb][i]);
-      mx = pair_max(mx) * scale_log2;
-      const bool g_cb = __ballot(mx > mrow[cb] + kLazyTau) != 0;
-      grow = grow || g_cb;
-      mnew[cb] = g_cb ? fmaxf(mrow[cb], mx) : mrow[cb];
-      const float mb = (mnew[cb] == kNegInf) ? 0.f : mnew[cb];
-      float acc_l = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(cur[kb][cb][i], scale_log2, -mb));
-          cur[kb][cb][i] = p;
-          acc_l += p;
-        }
-      ls[cb] = acc_l;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        pb[kb][0][cb] = pack8(cur[kb][cb], 0);
-        pb[kb][1][cb] = pack8(cur[kb][cb], 8);
+      for (int i = 3; i < 8; ++i) {
+        mp[2 * kb] = fmaxf(mp[2 * kb], sacc[kb][i]);
+        mp[2 * kb + 1] = fmaxf(mp[2 * kb + 1], sacc[kb][8 + i]);
       }
+    float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+    mx = pair_max(mx) * scale_log2;
+    const bool grow = __ballot(mx > mrow + kLazyTau) != 0;
+    const float mnew = grow ? fmaxf(mrow, mx) : mrow;
+    const float mb = (mnew == kNegInf) ? 0.f : mnew;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = fmaf(sacc[kb][i], scale_log2, -mb);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(sacc[kb][i]);
+    // Row sum with four partial sums.
+    float lp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lp[(i & 1) + 2 * kb] += sacc[kb][i];
+    const float acc_l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      pb[kb][0] = pack8(sacc[kb], 0);
+      pb[kb][1] = pack8(sacc[kb], 8);
     }
     if (grow) {
+      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(mrow - mnew);
+      lrow *= alpha;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const float alpha = (mnew[cb] == kNegInf) ? 1.f : fast_exp2(mrow[cb] - mnew[cb]);
-        lrow[cb] *= alpha;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[cb][db][i] *= alpha;
-      }
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      mrow[cb] = mnew[cb];
-      lrow[cb] += ls[cb];
-    }
-    pv(pb[0][0], vbc, I0{}, I0{});
-    pv(pb[0][1], vbc, I0{}, I1{});
-    pv(pb[1][0], vbc, I1{}, I0{});
-    pv(pb[1][1], vbc, I1{}, I1{});
+    mrow = mnew;
+    lrow += acc_l;
   };
 
-  f32x16 sA[NKB][NCB], sB[NKB][NCB];
-  wait_vmem();
-  __syncthreads();
-  if (0 < wtiles) scores(sA, I0{});
-  // Iteration t (t % 2 == I): at its top K(t+1) and V(t) have landed and
-  // every wave is done with K(t) (read by S^T(t) last iteration) and V(t-1),
-  // whose buffers then receive K(t+2) and V(t+1).
-  auto iteration = [&](auto ic, int tile) __attribute__((always_inline)) {
-    constexpr int I = decltype(ic)::value;
-    using KN = std::integral_constant<int, (I + 1) % 2>;
-    using VC = std::integral_constant<int, I>;
-    wait_vmem();
-    __syncthreads();
-    if (tile + 2 < ntiles) dma.load(smem + I * TILE, kp, (tile + 2) * BC, Sk);
-    if (tile + 1 < ntiles) dma.load(smem + (2 + (I + 1) % 2) * TILE, vp, (tile + 1) * BC, Sk);
-    if constexpr (I == 0) step(sA, sB, tile, KN{}, VC{});
-    else step(sB, sA, tile, KN{}, VC{});
+  // Tile tt's MFMA phase runs for 0 <= tt <= wtiles: at tt = 0 P is still
+  // zero (the V buffer it multiplies holds finite data), and at tt = wtiles the
+  // score tile is computed but never used.  One code shape for every tile.
+  auto mfma_tile = [&](int tt, auto kbc, auto vbc) __attribute__((always_inline)) {
+    if (tt <= wtiles) mfma_phase(kbc, vbc);
   };
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    iteration(I0{}, tile);
-    if (tile + 1 < ntiles) iteration(I1{}, tile + 1);
+  auto softmax_tile = [&](int tt) __attribute__((always_inline)) {
+    if (tt >= 0 && tt < wtiles) softmax_phase(tt);
+  };
+  // Phases 2u and 2u + 1 (u % 2 == I): K(u) sits in K buffer I and V(u-1) in
+  // V buffer 1 - I; K(u+1) and V(u) are loaded into the other two.
+  auto phase_pair = [&](auto ic, int u) __attribute__((always_inline)) {
+    constexpr int I = decltype(ic)::value;
+    using KC = std::integral_constant<int, I>;
+    using VC = std::integral_constant<int, 1 - I>;
+    if (u + 1 < ntiles) dma.load(smem + (1 - I) * TILE, kp, (u + 1) * BC, Sk);
+    if (u < ntiles) dma.load(smem + (2 + I) * TILE, vp, u * BC, Sk);
+    if (lead) mfma_tile(u, KC{}, VC{});
+    else softmax_tile(u - 1);
+    phase_barrier();
+    if (lead) softmax_tile(u);
+    else mfma_tile(u, KC{}, VC{});
+    wait_vmem();
+    phase_barrier();
+  };
+
+  wait_vmem();
+  phase_barrier();
+  for (int u = 0; u <= ntiles; u += 2) {
+    phase_pair(std::integral_constant<int, 0>{}, u);
+    if (u + 1 <= ntiles) phase_pair(std::integral_constant<int, 1>{}, u + 1);
   }
 
-  fwd_epilogue<D, NCB, MERGE>(oacc, mrow, lrow, og, lseg, bh, Sq, qw0, l32, g);
+  fwd_epilogue<D, MERGE>(oacc, mrow, lrow, og, lseg, bh, Sq, qq, g);
 }
 
-template <int D, int NW, int NQW>
+template <int D>
 hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
-  constexpr int BR = NW * NQW;
+  constexpr int BR = kFwdWaves * kFwdRowsPerWave;
   const int n_qtiles = (a.Sq + BR - 1) / BR;
   const long long total = (long long)n_qtiles * a.BH;
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   const float sl2 = a.scale * kLog2e;
-  dim3 grid((unsigned)total), block(64 * NW);
+  dim3 grid((unsigned)total), block(64 * kFwdWaves);
 #define RA_FWD_LAUNCH(DIAG, MERGE)                                                                         \
-  hipLaunchKernelGGL((fwd_step_kernel<D, NW, NQW, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, a.v, a.o, \
+  hipLaunchKernelGGL((fwd_step_kernel<D, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, a.v, a.o, \
                      a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2)
   if (a.diag) {
     if (a.merge) RA_FWD_LAUNCH(true, true);
@@ -340,14 +345,9 @@ hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// 8 waves of 32 query rows: two waves share each SIMD, so one's softmax can
-// overlap the other's MFMAs.
-constexpr int kFwdWaves = 8;
-constexpr int kFwdRowsPerWave = 32;
-
 hipError_t launch_fwd_step(const FwdStepArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_cfg<128, kFwdWaves, kFwdRowsPerWave>(a, stream);
-  if (a.d == 64) return launch_cfg<64, kFwdWaves, kFwdRowsPerWave>(a, stream);
+  if (a.d == 128) return launch_cfg<128>(a, stream);
+  if (a.d == 64) return launch_cfg<64>(a, stream);
   return hipErrorInvalidValue;
 }
 
