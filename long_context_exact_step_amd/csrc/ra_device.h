@@ -174,7 +174,6 @@ struct TileDma {
   static constexpr int kPerWave = kPieces / NW;
   static_assert(kPieces % NW == 0, "tile pieces must split evenly over waves");
   uint32_t off[kPerWave];  // byte offset of this lane's 16 bytes from the tile's first row
-  int row[kPerWave];       // tile row of this lane's chunk
   int piece0;              // first piece of this wave
 
   __device__ __forceinline__ void init(int wave, int lane) {
@@ -183,9 +182,25 @@ struct TileDma {
     piece0 = wave * kPerWave;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      row[i] = (piece0 + i) * kRowsPerPiece + rin;
-      off[i] = (uint32_t)(row[i] * D * 2 + swz<D>(row[i], p) * 16);
+      const int row = (piece0 + i) * kRowsPerPiece + rin;
+      off[i] = (uint32_t)(row * D * 2 + swz<D>(row, p) * 16);
     }
+  }
+
+  // This wave's piece i of tokens t0 .. t0+TOK-1 of the [n, D] bf16 matrix
+  // at `mat` into `tile`.  Tokens past n - 1 read row n - 1 (in bounds; the
+  // kernels mask them), so any t0 >= 0 is safe.
+  __device__ __forceinline__ void load_piece(int i, uint8_t* tile, const uint16_t* mat, int t0, int n) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // Branch-free (it is issued from inside MFMA streams): the row is clamped
+    // to n - 1 with a min, a no-op on full tiles.
+    uint32_t o = off[i];
+    asm volatile("" : "+v"(o));  // keeps a 32-bit offset (no hoisted 64-bit address)
+    const uint32_t row = o / (D * 2);
+    const uint32_t tok = min((uint32_t)t0 + row, (uint32_t)(n - 1));
+    const uint8_t* g = reinterpret_cast<const uint8_t*>(mat) + (tok * (uint32_t)(D * 2) + (o - row * (D * 2)));
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + (piece0 + i) * 1024), 16, 0, 0);
+#endif
   }
 
   // Tokens t0 .. t0+TOK-1 of the [n, D] bf16 matrix at `mat` into `tile`.
@@ -195,14 +210,20 @@ struct TileDma {
     if (t0 + TOK <= n) {
       const uint8_t* g = reinterpret_cast<const uint8_t*>(mat) + (size_t)t0 * D * 2;
 #pragma unroll
-      for (int i = 0; i < kPerWave; ++i)
-        __builtin_amdgcn_global_load_lds(g + off[i], (lds_void*)(tile + (piece0 + i) * 1024), 16, 0, 0);
+      for (int i = 0; i < kPerWave; ++i) {
+        // Opaque to loop-invariant code motion: the per-lane part stays a
+        // 32-bit offset to a uniform base instead of a hoisted 64-bit address.
+        uint32_t o = off[i];
+        asm volatile("" : "+v"(o));
+        __builtin_amdgcn_global_load_lds(g + o, (lds_void*)(tile + (piece0 + i) * 1024), 16, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) {
-        const int tok = (t0 + row[i] < n) ? t0 + row[i] : n - 1;
+        const int row = (int)(off[i] / (D * 2));
+        const int tok = (t0 + row < n) ? t0 + row : n - 1;
         const uint8_t* g = reinterpret_cast<const uint8_t*>(mat) + (size_t)tok * D * 2 +
-                           (off[i] - (uint32_t)(row[i] * D * 2));
+                           (off[i] - (uint32_t)(row * D * 2));
         __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + (piece0 + i) * 1024), 16, 0, 0);
       }
     }
@@ -321,5 +342,12 @@ __device__ __forceinline__ u32x4 ld_vt(const uint8_t* tile, int d0, int kb, int 
 
 // s_waitcnt vmcnt(0) (global loads, including loads into LDS, complete).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Waits until at most N vector-memory operations of this wave are
+// outstanding (vmcnt(N), N < 16); they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt low field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 }  // namespace ra

@@ -44,7 +44,7 @@ namespace ra {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kLazyTau = 8.0f;  // log2 of the largest un-rescaled probability
+constexpr float kLazyBound = 256.0f;  // largest row sum of one tile computed without a new maximum
 
 
 // Epilogue: this step's partial (oacc / l, m + log2 l) of the lane's query
@@ -93,27 +93,34 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&oacc)[D / 32], float
   if (g == 0) *lp = lse_new * kLn2;
 }
 
-// LDS reads still in flight after those of MFMA m, when the reads of MFMAs
-// m+1 .. m+LA have been issued; the first NPV MFMAs take two reads each.
-__host__ __device__ constexpr int reads_after(int m, int LA, int NPV, int NOP) {
-  int n = 0;
-  for (int k = m + 1; k <= m + LA && k < NOP; ++k) n += (k < NPV) ? 2 : 1;
-  return n;
+// First softmax element issued in MFMA slot m when NEL elements are spread in
+// order over slots SH .. NOP-1 (element e goes to slot SH + e*(NOP-SH)/NEL).
+__host__ __device__ constexpr int first_element(int m, int SH, int NOP, int NEL) {
+  return m <= SH ? 0 : (m >= NOP ? NEL : ((m - SH) * NEL + (NOP - SH) - 1) / (NOP - SH));
 }
 
-constexpr int kFwdWaves = 8;       // waves per block; waves w and w + 4 share a SIMD
+constexpr int kFwdWaves = 8;      // waves per block, two per SIMD
 constexpr int kFwdRowsPerWave = 32;
-constexpr int kFwdLookahead = 6;   // MFMAs whose LDS operands are read ahead
+constexpr int kFwdLookahead = 3;  // MFMAs whose LDS operands are read ahead
+constexpr int kFwdBuffers = 4;    // LDS buffers per operand (K, V)
 
 // One ring step.  A block holds 256 query rows, 32 per wave, and walks the
-// chunk's keys in 64-key tiles.  Per tile a wave runs two phases:
-//   MFMA phase of tile t:     O^T += V^T P^T(t-1), then S^T(t) = K(t) Q^T;
-//   softmax phase of tile t:  the online softmax of S^T(t) -> P^T(t) in bf16.
-// Waves 4..7 run one phase behind waves 0..3, with a workgroup barrier
-// between phases, so on every SIMD one wave keeps the matrix core busy while
-// the other computes exponentials.  Phase 2u starts the loads of K(u+1) and
-// V(u) (two buffers each); they are waited for at the end of phase 2u+1,
-// before anyone reads them in phase 2u+2.
+// chunk's keys in 64-key tiles with a three-stage software pipeline per wave.
+// Iteration t issues, one MFMA per slot,
+//   O^T += V^T P^T(t-1)      (16 MFMAs at d = 128; V^T read transposed)
+//   S^T(t+1) = K(t+1) Q^T    (16 MFMAs)
+// and, in the vector-ALU slots between those MFMAs, the online softmax of
+// S^T(t) (computed one iteration earlier): about one score per MFMA slot, so
+// the exponentials never wait on a matrix result and never stall the matrix
+// core.  The exponentials use the running maximum as reference without
+// computing the tile maximum first; a wave-uniform test on the tile's row
+// sums sends the rare tile whose scores exceed the reference by more than
+// 2^8 (and every row's first tile) to an exact path that takes the maximum,
+// recomputes P and rescales O.
+// K and V tiles arrive by direct-to-LDS loads into four buffers each, two
+// tiles ahead of use, so the operands of an iteration's first MFMAs are read
+// before the barrier that ends the previous one and the operand stream runs
+// on across it.  One workgroup barrier per tile.
 template <int D, bool DIAG, bool MERGE>
 __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t* __restrict__ qg,
                                                                   const uint16_t* __restrict__ kg,
@@ -124,12 +131,27 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
                                                                   float scale_log2) {
   constexpr int NW = kFwdWaves, NQW = kFwdRowsPerWave, BR = NW * NQW, BC = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kFwdLookahead;
-  // LDS: K tiles in buffers 0..1, V tiles in buffers 2..3; tile t uses buffer t % 2.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE];
+  constexpr int NB = kFwdBuffers;
+  constexpr int NPV = 4 * NDB, NS = NKS * NKB, NOP = NPV + NS, NEL = 16 * NKB;
+  // The ring of LA + 1 operand registers lines up with every stream.
+  static_assert(NOP % (LA + 1) == 0 && NS % (LA + 1) == 0, "operand ring must divide the streams");
+  static_assert(LA <= NPV, "the next iteration's first operands are PV reads");
+  // Softmax element e of tile t (keys 16j .. 16j+15 for e in 8j .. 8j+7)
+  // overwrites P^T(t-1) of the same keys, which the MFMAs of slots
+  // NDB*j .. NDB*j+NDB-1 read; starting the elements at slot SH keeps every
+  // write after the slot of the last MFMA that reads its register.
+  constexpr int SH = 3;
+  // LDS: V tiles in buffers 0 .. NB-1, K tiles in buffers NB .. 2NB-1 (the
+  // K half starts at VOFF, folded into the K addresses so that every read
+  // offset fits the 16-bit immediate); tile j uses buffer j % NB.
+  constexpr int VOFF = NB * TILE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NB * TILE];
+  auto kbuf = [&](int b) __attribute__((always_inline)) { return smem + VOFF + b * TILE; };
+  auto vbuf = [&](int b) __attribute__((always_inline)) { return smem + b * TILE; };
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
   const int l32 = lane & 31, g = lane >> 5;
-  const bool lead = wave < NW / 2;
   const int t = xcd_remap(blockIdx.x, total_tiles);
   const int bh = t / n_qtiles;
   int qt = t - bh * n_qtiles;
@@ -145,11 +167,21 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   if (DIAG) kend = min(kend, q0 + BR);
   const int ntiles = (kend + BC - 1) / BC;
   const int wtiles = DIAG ? min(ntiles, max(0, (min(qw0 + NQW, Sq) - 1) / BC + 1)) : ntiles;
+  // Keys at or past `lim` are masked for this lane's query.
+  const int lim = DIAG ? min(Sk, qq + 1) : Sk;
 
-  TileDma<D, NW, BC> dma;
+  // Iteration t reads K(t+1) and V(t-1); step t loads V(t+1) and K(t+3),
+  // one 1 KB piece per MFMA slot in DMA_SLOT, V pieces first.  A step ends
+  // waiting for all but its K pieces, which have one more step to land.
+  using Dma = TileDma<D, NW, BC>;
+  constexpr int NPIECE = Dma::kPerWave;  // pieces per tile per wave
+  Dma dma;
   dma.init(wave, lane);
-  dma.load(smem, kp, 0, Sk);
-  dma.load(smem + 3 * TILE, vp, 0, Sk);  // finite data for the P = 0 product of tile 0
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < ntiles) dma.load(kbuf(j), kp, j * BC, Sk);
+  dma.load(vbuf(0), vp, 0, Sk);
+  dma.load(vbuf(NB - 1), vp, 0, Sk);  // finite data for the P = 0 product of iteration 0
 
   u32x4 qf[NKS];
 #pragma unroll
@@ -160,7 +192,10 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float mrow = kNegInf, lrow = 0.f;
-  f32x16 sacc[NKB];
+  // S^T of tiles t (being softmaxed) and t + 1 (being computed): sacc[t % 2].
+  f32x16 sacc[2][NKB];
+  // P^T in bf16: P^T(t-1) while iteration t multiplies it, overwritten in
+  // place by P^T(t) as the softmax of tile t produces it.
   u32x4 pb[NKB][2];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) pb[kb][0] = pb[kb][1] = u32x4{0, 0, 0, 0};
@@ -168,7 +203,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   const uint32_t base = lds_addr(smem);
   uint32_t kaddr[NKS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) kaddr[s] = base + (uint32_t)tile_off<D>(l32, 2 * s + g);
+  for (int s = 0; s < NKS; ++s) kaddr[s] = base + VOFF + (uint32_t)tile_off<D>(l32, 2 * s + g);
   uint32_t vaddr[NDB][2];
   {
     const int m = (lane & 15) >> 2, a4 = lane & 3, half16 = (lane >> 4) & 1;
@@ -181,141 +216,205 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
     }
   }
 
-  // MFMA phase: O^T += V^T P^T from V buffer VB, then S^T from K buffer KB
-  // into sacc.  The LDS operands of the next LA MFMAs are always in flight;
-  // each MFMA waits only for its own.
-  auto mfma_phase = [&](auto kbc, auto vbc) __attribute__((always_inline)) {
-    constexpr int KB = decltype(kbc)::value, VB = decltype(vbc)::value;
-    constexpr int NPV = 4 * NDB, NOP = NPV + NKS * NKB;
-    u32x2 lo[LA + 1], hi[LA + 1];
-    u32x4 kq[LA + 1];
+  // Offset of element (kb, i) of a score accumulator from the tile's first key,
+  // less 4g (the lane half's own offset).
+  auto key_off = [](int kb, int i) { return 32 * kb + 8 * (i >> 2) + (i & 3); };
+
+  // Operand registers of the MFMAs whose LDS reads are in flight; op m of any
+  // stream uses ring slot m % (LA + 1).  They carry over from one stream to
+  // the next.
+  u32x2 lo[LA + 1], hi[LA + 1];
+  u32x4 kq[LA + 1];
+  // Reads of PV op m (V^T block db for tokens 32*(gi/2) + 16*(gi%2) .. +15)
+  // from V buffer VB, or of S op m from K buffer KB.
+  auto read_pv = [&](auto mc, auto vbc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value, VB = decltype(vbc)::value, b = m % (LA + 1);
+    constexpr int gi = m / NDB, db = m % NDB;
+    constexpr int OFF = VB * TILE + (32 * (gi >> 1) + 16 * (gi & 1)) * D * 2;
+    lo[b] = ds_read_tr16_off<OFF>(vaddr[db][0]);
+    hi[b] = ds_read_tr16_off<OFF>(vaddr[db][1]);
+  };
+  auto read_s = [&](auto mc, auto jc, auto kbc) __attribute__((always_inline)) {
+    constexpr int b = decltype(mc)::value % (LA + 1), j = decltype(jc)::value, KB = decltype(kbc)::value;
+    constexpr int s = j / NKB, kb = j % NKB;
+    kq[b] = ds_read_b128_off<KB * TILE + kb * 32 * D * 2>(kaddr[s]);
+  };
+
+  // One MFMA stream: PV from V buffer VB with P^T `pb` (if PV), then S^T from
+  // K buffer KB into `sn`, with `valu(m)` in the slot of MFMA m.  The reads of
+  // the first LA ops were issued before the stream (by the previous stream);
+  // the stream's last slots issue those of the next stream, a PV from V
+  // buffer VBN.  Each MFMA waits only for its own operands; sched_barrier
+  // keeps every slot's instructions in their slot.
+  auto mfma_stream = [&](auto pvc, auto kbc, auto vbc, auto vbnc, f32x16 (&sn)[NKB], auto&& valu)
+                         __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pvc)::value;
+    constexpr int N2 = PV ? NPV : 0, NO = N2 + NS;
+    // Reads in flight after those of op m: ops m+1 .. m+LA, the ones past
+    // the end being the next stream's PV ops (two reads each).
+    auto reads_after = [](int m) {
+      int n = 0;
+      for (int k = m + 1; k <= m + LA; ++k) n += (k < N2 || k >= NO) ? 2 : 1;
+      return n;
+    };
     auto issue = [&](auto mc) __attribute__((always_inline)) {
-      constexpr int m = decltype(mc)::value, b = m % (LA + 1);
-      if constexpr (m < NPV) {
-        // V^T block db for tokens 32*(gi/2) + 16*(gi%2) .. +15.
-        constexpr int gi = m / NDB, db = m % NDB;
-        constexpr int OFF = (2 + VB) * TILE + (32 * (gi >> 1) + 16 * (gi & 1)) * D * 2;
-        lo[b] = ds_read_tr16_off<OFF>(vaddr[db][0]);
-        hi[b] = ds_read_tr16_off<OFF>(vaddr[db][1]);
-      } else if constexpr (m < NOP) {
-        constexpr int j = m - NPV, s = j / NKB, kb = j % NKB;
-        kq[b] = ds_read_b128_off<KB * TILE + kb * 32 * D * 2>(kaddr[s]);
-      }
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < N2) read_pv(mc, vbc);
+      else if constexpr (m < NO) read_s(mc, std::integral_constant<int, m - N2>{}, kbc);
+      else read_pv(std::integral_constant<int, m - NO>{}, vbnc);
     };
     auto run = [&](auto mc) __attribute__((always_inline)) {
       constexpr int m = decltype(mc)::value, b = m % (LA + 1);
-      constexpr int N = reads_after(m, LA, NPV, NOP);
+      constexpr int N = reads_after(m);
       issue(std::integral_constant<int, m + LA>{});
-      if constexpr (m < NPV) {
+      if constexpr (m < N2) {
         constexpr int gi = m / NDB, db = m % NDB;
         lgkm_wait<N>(lo[b], hi[b]);
         const u32x4 a = {lo[b][0], lo[b][1], hi[b][0], hi[b][1]};
         oacc[db] = mfma32(a, pb[gi >> 1][gi & 1], oacc[db]);
       } else {
-        constexpr int j = m - NPV, s = j / NKB, kb = j % NKB;
+        constexpr int j = m - N2, s = j / NKB, kb = j % NKB;
         lgkm_wait<N>(kq[b]);
-        if constexpr (s == 0) sacc[kb] = mfma32(kq[b], qf[0], f32x16{});
-        else sacc[kb] = mfma32(kq[b], qf[s], sacc[kb]);
+        if constexpr (s == 0) sn[kb] = mfma32(kq[b], qf[0], f32x16{});
+        else sn[kb] = mfma32(kq[b], qf[s], sn[kb]);
       }
+      valu(mc);
+      __builtin_amdgcn_sched_barrier(0);
     };
-    static_for<LA>(issue);
-    static_for<NOP>(run);
+    static_for<NO>(run);
   };
 
-  // Softmax phase of tile tt: mask, running maximum (raised lazily), P in
-  // bf16 into pb, running sum, and the rare rescale of O.
-  auto softmax_phase = [&](int tt) __attribute__((always_inline)) {
-    const int k0 = tt * BC;
-    if ((k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0)) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= Sk || (DIAG && key > qq)) sacc[kb][i] = kNegInf;
-        }
-    }
-    // Row maximum as a tree (short dependency chains).
-    float mp[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mp[j] = fmaxf(fmaxf(sacc[j >> 1][8 * (j & 1)], sacc[j >> 1][8 * (j & 1) + 1]),
-                                            sacc[j >> 1][8 * (j & 1) + 2]);
+  // Exact path of the softmax of tile tt (rare): mask, tile maximum, P and
+  // its row sums recomputed against the raised reference, O and l rescaled.
+  auto softmax_exact = [&](int tt, f32x16 (&sc)[NKB]) __attribute__((always_inline)) {
+    const int r = lim - tt * BC - 4 * g;
+    float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 3; i < 8; ++i) {
-        mp[2 * kb] = fmaxf(mp[2 * kb], sacc[kb][i]);
-        mp[2 * kb + 1] = fmaxf(mp[2 * kb + 1], sacc[kb][8 + i]);
+      for (int i = 0; i < 16; ++i) {
+        if (key_off(kb, i) >= r) sc[kb][i] = kNegInf;
+        mx = fmaxf(mx, sc[kb][i]);
       }
-    float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
     mx = pair_max(mx) * scale_log2;
-    const bool grow = __ballot(mx > mrow + kLazyTau) != 0;
-    const float mnew = grow ? fmaxf(mrow, mx) : mrow;
+    const float mnew = fmaxf(mrow, mx);
     const float mb = (mnew == kNegInf) ? 0.f : mnew;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = fmaf(sacc[kb][i], scale_log2, -mb);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(sacc[kb][i]);
-    // Row sum with four partial sums.
-    float lp[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) lp[(i & 1) + 2 * kb] += sacc[kb][i];
-    const float acc_l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      pb[kb][0] = pack8(sacc[kb], 0);
-      pb[kb][1] = pack8(sacc[kb], 8);
-    }
-    if (grow) {
-      const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(mrow - mnew);
-      lrow *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(sc[kb][i], scale_log2, -mb));
+        sc[kb][i] = p;
+        l4[i & 3] += p;
+      }
+      pb[kb][0] = pack8(sc[kb], 0);
+      pb[kb][1] = pack8(sc[kb], 8);
     }
+    const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(mrow - mnew);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    lrow = lrow * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
     mrow = mnew;
-    lrow += acc_l;
   };
 
-  // Tile tt's MFMA phase runs for 0 <= tt <= wtiles: at tt = 0 P is still
-  // zero (the V buffer it multiplies holds finite data), and at tt = wtiles the
-  // score tile is computed but never used.  One code shape for every tile.
-  auto mfma_tile = [&](int tt, auto kbc, auto vbc) __attribute__((always_inline)) {
-    if (tt <= wtiles) mfma_phase(kbc, vbc);
-  };
-  auto softmax_tile = [&](int tt) __attribute__((always_inline)) {
-    if (tt >= 0 && tt < wtiles) softmax_phase(tt);
-  };
-  // Phases 2u and 2u + 1 (u % 2 == I): K(u) sits in K buffer I and V(u-1) in
-  // V buffer 1 - I; K(u+1) and V(u) are loaded into the other two.
-  auto phase_pair = [&](auto ic, int u) __attribute__((always_inline)) {
+  // Piece k of step tt's loads: V(tt+1) replaces V(tt-3) and K(tt+3)
+  // replaces K(tt-1), both last read in iteration tt - 2 or earlier.  Loads
+  // past the last tile read clamped rows and are never used.
+  auto dma_piece = [&](int tt, auto ic, int k) __attribute__((always_inline)) {
     constexpr int I = decltype(ic)::value;
-    using KC = std::integral_constant<int, I>;
-    using VC = std::integral_constant<int, 1 - I>;
-    if (u + 1 < ntiles) dma.load(smem + (1 - I) * TILE, kp, (u + 1) * BC, Sk);
-    if (u < ntiles) dma.load(smem + (2 + I) * TILE, vp, u * BC, Sk);
-    if (lead) mfma_tile(u, KC{}, VC{});
-    else softmax_tile(u - 1);
-    phase_barrier();
-    if (lead) softmax_tile(u);
-    else mfma_tile(u, KC{}, VC{});
-    wait_vmem();
+    if (k < NPIECE) dma.load_piece(k, vbuf((I + 1) % NB), vp, (tt + 1) * BC, Sk);
+    else dma.load_piece(k - NPIECE, kbuf((I + 3) % NB), kp, (tt + 3) * BC, Sk);
+  };
+  // Iteration tt (tt % NB == I): PV(tt-1), S^T(tt+1) and the softmax of tile
+  // tt.  The same code runs for tt = wtiles, where only PV(tt-1) matters: the
+  // score tile and the softmax it computes there are never committed or
+  // used.  Tiles that need a mask (keys past the chunk, or past the
+  // diagonal) take the exact path, which applies it.
+  auto iteration = [&](int tt, auto ic) __attribute__((always_inline)) {
+    constexpr int I = decltype(ic)::value;
+    f32x16(&sc)[NKB] = sacc[I % 2];
+    const float mb = (mrow == kNegInf) ? 0.f : mrow;
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+    // Each element runs as three stages in three consecutive slots (scale,
+    // exp2, sum and pack), so no instruction waits on one issued in its own
+    // slot.  xs / ps hold the elements between stages, by element index.
+    float xs[NEL], ps[NEL];
+    auto scale_stage = [&](int e) __attribute__((always_inline)) {
+      xs[e] = fmaf(sc[e >> 4][e & 15], scale_log2, -mb);
+    };
+    auto exp_stage = [&](int e) __attribute__((always_inline)) { ps[e] = fast_exp2(xs[e]); };
+    auto sum_stage = [&](int e) __attribute__((always_inline)) {
+      const int kb = e >> 4, i = e & 15;
+      l4[i & 3] += ps[e];
+      asm volatile("" : "+v"(l4[i & 3]));  // keeps the sum in this slot
+      if (i & 1) pb[kb][i >> 3][(i & 7) >> 1] = pack_bf16(ps[e - 1], ps[e]);
+    };
+    // Slots SH .. NOP-1 take the elements in order, spread evenly: slot m
+    // starts elements first_element(m) .. first_element(m + 1) - 1.  The
+    // step's tile loads go to evenly spaced slots.
+    auto valu = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int DMA_EVERY = NOP / (2 * NPIECE);
+      if constexpr (m % DMA_EVERY == DMA_EVERY / 2) dma_piece(tt, ic, m / DMA_EVERY);
+#pragma unroll
+      for (int e = first_element(m - 2, SH, NOP, NEL); e < first_element(m - 1, SH, NOP, NEL); ++e) sum_stage(e);
+#pragma unroll
+      for (int e = first_element(m - 1, SH, NOP, NEL); e < first_element(m, SH, NOP, NEL); ++e) exp_stage(e);
+#pragma unroll
+      for (int e = first_element(m, SH, NOP, NEL); e < first_element(m + 1, SH, NOP, NEL); ++e) scale_stage(e);
+    };
+    mfma_stream(std::true_type{}, std::integral_constant<int, (I + 1) % NB>{},
+                std::integral_constant<int, (I + NB - 1) % NB>{}, std::integral_constant<int, I>{},
+                sacc[1 - I % 2], valu);
+    // The stages still in flight after the last slot.
+#pragma unroll
+    for (int e = first_element(NOP - 2, SH, NOP, NEL); e < NEL; ++e) {
+      if (e >= first_element(NOP - 1, SH, NOP, NEL)) exp_stage(e);
+      sum_stage(e);
+    }
+    if (tt < wtiles) {
+      const int k0 = tt * BC;
+      const bool masked = (k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0);
+      const float lt = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+      if (masked || __ballot(!(lt <= kLazyBound) || mrow == kNegInf) != 0) softmax_exact(tt, sc);
+      else lrow += lt;
+    }
+  };
+  auto step = [&](int tt, auto ic) __attribute__((always_inline)) {
+    if (tt <= wtiles) iteration(tt, ic);
+    // A wave past its last tile still loads its share of the tiles.
+    if (tt > wtiles) {
+#pragma unroll
+      for (int k = 0; k < 2 * NPIECE; ++k) dma_piece(tt, ic, k);
+    }
+    wait_vmem_but<NPIECE>();
     phase_barrier();
   };
 
+  // Prologue: S^T(0) once K(0) has landed (computed, harmlessly, also for a
+  // wave with no rows); its stream issues iteration 0's first reads.
   wait_vmem();
   phase_barrier();
-  for (int u = 0; u <= ntiles; u += 2) {
-    phase_pair(std::integral_constant<int, 0>{}, u);
-    if (u + 1 <= ntiles) phase_pair(std::integral_constant<int, 1>{}, u + 1);
+  {
+    auto none = [](auto) __attribute__((always_inline)) {};
+    static_for<LA>([&](auto mc) __attribute__((always_inline)) {
+      read_s(mc, mc, std::integral_constant<int, 0>{});
+    });
+    mfma_stream(std::false_type{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+                std::integral_constant<int, NB - 1>{}, sacc[0], none);
   }
+  // Steps past ntiles only keep the barrier count uniform.
+  for (int tt = 0; tt <= ntiles; tt += NB) {
+    step(tt, std::integral_constant<int, 0>{});
+    step(tt + 1, std::integral_constant<int, 1>{});
+    step(tt + 2, std::integral_constant<int, 2>{});
+    step(tt + 3, std::integral_constant<int, 3>{});
+  }
+  // Reads issued for an iteration that never ran.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
   fwd_epilogue<D, MERGE>(oacc, mrow, lrow, og, lseg, bh, Sq, qq, g);
 }
