@@ -12,7 +12,7 @@
 //
 // gfx950 design.
 //  * A block is 8 waves of 32 query rows (256 rows); two waves share each
-//    SIMD, so one wave's softmax (VALU) overlaps the other's MFMAs.
+//    SIMD and interleave on its matrix core.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K (32 keys x 16 d) is the A operand read from
 //    LDS; Q^T is the B operand and stays in registers for the whole kernel.
@@ -21,17 +21,19 @@
 //    maximum), and the probabilities, packed to bf16, are already the B
 //    operand of O^T += V^T P^T.  V^T's A operand comes straight from the
 //    row-major V tile through ds_read_b64_tr_b16 (no transpose pass).
-//  * K and V tiles (64 keys) go global -> LDS with global_load_lds
-//    (no registers, no LDS store instructions), two buffers each, one block
-//    barrier per tile; each load has a whole tile of compute to land.
-//  * Software pipeline per wave: S^T of tile t+1 is computed in the same
-//    basic block as the softmax of tile t, then P V of tile t.
-//  * The loop is unrolled by 2 so every LDS offset is an immediate; the lane
-//    parts of the LDS addresses are computed once per kernel.
-//  * exp2 with scale*log2(e) folded into one FMA; the running maximum is
-//    raised only when a row's tile maximum exceeds it by more than 2^8
-//    (exact: numerator and denominator share the stale maximum), so the
-//    O rescale is rare.
+//  * Per 64-key tile each wave issues one stream of 32 MFMAs (P V of the
+//    previous tile, S^T of the next) and runs the softmax of the current
+//    tile in the vector-ALU slots between them, one score per slot, each
+//    score spread over three slots so no instruction waits on its own slot.
+//  * LDS operands are read three MFMAs ahead with counted waits, and the
+//    stream runs on across tiles.
+//  * K and V tiles (64 keys) go global -> LDS with global_load_lds (no
+//    registers) into four buffers each, two tiles ahead of use, one 1 KB
+//    piece per MFMA slot; one block barrier per tile.
+//  * exp2 with scale*log2(e) folded into one FMA, against the running
+//    maximum; the tile maximum is only taken (and O rescaled) on the exact
+//    path: a row's first tile, masked tiles, and tiles whose row sums exceed
+//    2^8.
 //  * Blocks are mapped so each XCD works on one contiguous range of
 //    (head, query tile) pairs (K/V lines shared in that XCD's L2); on the
 //    diagonal chunk the longest query tiles go first.
