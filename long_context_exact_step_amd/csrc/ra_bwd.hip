@@ -6,18 +6,21 @@
 //   P = exp(scale q k^T - lse), dP = dO v^T, dS = P (dP - D), D = rowsum(dO o),
 //   dq += scale dS k,  dk += scale dS^T q,  dv += P^T dO.
 //
-// Two kernels per step, neither with atomics (results are deterministic):
-//  * dq kernel -- a block owns 128 query rows (32 per wave, Q^T and dO^T in
+// Three launches per step, none with atomics (results are deterministic):
+//  * dq kernel -- a block owns 256 query rows (32 per wave, Q^T and dO^T in
 //    registers as MFMA B operands, like the forward) and streams 64-key tiles
-//    of K, V (row-major LDS tiles, A operands) and K^T (transposed LDS tile).
-//    Scores are computed transposed (S^T = K Q^T, dP^T = V dO^T), so lse and
-//    D are per-lane scalars and dS^T feeds dq^T += K^T dS^T directly.
-//  * dk/dv kernel -- a block owns 128 keys of the chunk (32 per wave, K and V
-//    in registers as B operands) and streams 64-query tiles of Q, dO
-//    (row-major) and Q^T, dO^T (transposed).  Here S = Q K^T has a lane per
-//    key, so P and dS feed dv^T += dO^T P and dk^T += Q^T dS directly; lse and
-//    D of the tile's queries come from LDS.
-// The price of avoiding atomics is recomputing S and dP in both kernels.
+//    of K and V (row-major LDS tiles, A operands; K^T is read from the same
+//    tile through the transposing LDS read).  Scores are computed transposed
+//    (S^T = K Q^T, dP^T = V dO^T), so lse and D are per-lane scalars and dS^T
+//    feeds dq^T += K^T dS^T directly.
+//  * dv pass, then dk pass of the key kernel -- a block owns 256 keys of the
+//    chunk (32 per wave, K and V in registers as B operands) and streams
+//    64-query tiles of Q and dO (row-major; Q^T and dO^T through the
+//    transposing read).  Here S = Q K^T has a lane per key, so P and dS feed
+//    dv^T += dO^T P and dk^T += Q^T dS directly; lse and D of the tile's
+//    queries are staged in LDS.
+// The price of avoiding atomics is recomputing S in all three launches and dP
+// in two.
 #include "ra_device.h"
 #include "ra_kernels.h"
 
@@ -27,84 +30,72 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 
-// Per-thread staging of one 64-token tile: item `it` holds tokens
-// 4*kq .. 4*kq+3, features 8*dc .. 8*dc+7.
-template <int D>
-struct TileItems {
-  static constexpr int kItems = (D / 8) * (kTileTokens / 4);
-  static constexpr int kPerThread = (kItems + 255) / 256;
-};
-
-template <int D>
-__device__ __forceinline__ void load_items(u32x4 (&r)[TileItems<D>::kPerThread][4], const uint16_t* base,
-                                           int t0, int n, int tid) {
-#pragma unroll
-  for (int i = 0; i < TileItems<D>::kPerThread; ++i) {
-    const int it = tid + i * 256;
-    if (it < TileItems<D>::kItems) {
-      const int dc = it % (D / 8), kq = it / (D / 8);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int tok = t0 + kq * 4 + rr;
-        r[i][rr] = (tok < n) ? ld16(base + (size_t)tok * D + dc * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_items_rows(uint8_t* tile, const u32x4 (&r)[TileItems<D>::kPerThread][4],
-                                                 int tid) {
-#pragma unroll
-  for (int i = 0; i < TileItems<D>::kPerThread; ++i) {
-    const int it = tid + i * 256;
-    if (it < TileItems<D>::kItems) {
-      const int dc = it % (D / 8), kq = it / (D / 8);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        *reinterpret_cast<u32x4*>(tile + row_off<D>(kq * 4 + rr, dc)) = r[i][rr];
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_items_tr(uint8_t* tile, const u32x4 (&r)[TileItems<D>::kPerThread][4],
-                                               int tid) {
-#pragma unroll
-  for (int i = 0; i < TileItems<D>::kPerThread; ++i) {
-    const int it = tid + i * 256;
-    if (it < TileItems<D>::kItems) store_tr4x8(tile, it % (D / 8), it / (D / 8), r[i]);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // dq kernel.
 // ---------------------------------------------------------------------------
-template <int D, bool DIAG>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
-                                                     const uint16_t* __restrict__ vg, const uint16_t* __restrict__ dog,
-                                                     const float* __restrict__ lseg, const float* __restrict__ Dg,
-                                                     float* __restrict__ dqg, int Sq, int Sk, int n_qtiles,
-                                                     int total_tiles, float scale_log2, float scale) {
-  constexpr int BR = 128, BC = kTileTokens, NKS = D / 16, NDB = D / 32, NKB = BC / 32;
-  constexpr int TB = BC * D * 2;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * TB];
-  uint8_t* const ks = smem;
-  uint8_t* const vs = smem + TB;
-  uint8_t* const kts = smem + 2 * TB;
+constexpr int kDqWaves = 8;  // waves per block; waves w and w + 4 share a SIMD
+constexpr int kDqRowsPerWave = 32;
+constexpr int kDqLookahead = 2;  // MFMAs whose LDS operands are read ahead
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+// dq^T += scale K^T dS^T for one ring step.  A block holds 256 query rows,
+// 32 per wave (Q^T and dO^T in registers as MFMA B operands), and walks the
+// chunk's keys in 64-key tiles.  Per tile a wave runs two phases:
+//   MFMA phase of tile t:  dq^T += K^T(t-1) dS^T(t-1), S^T(t) = K(t) Q^T,
+//                          dP^T(t) = V(t) dO^T   (48 MFMAs at d = 128);
+//   vector phase of tile t: P = exp2(S scale - lse) (masked where needed),
+//                          dS = P (dP - D), packed to bf16.
+// Waves 4..7 run the same code one phase behind waves 0..3 (one extra
+// barrier first), with a workgroup barrier between phases, so each SIMD's
+// matrix core is fed by one wave while the other does the element-wise
+// work.  K^T comes straight from the row-major K tile through
+// ds_read_b64_tr_b16.  LDS operands are read LA MFMAs ahead with counted
+// waits.  Tiles load two ahead of use: K into four LDS buffers (a phase
+// reads K(t-1) and K(t)), V into three.
+template <int D, bool DIAG>
+__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+    const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ Dg,
+    float* __restrict__ dqg, int Sq, int Sk, int n_qtiles, int total_tiles, float scale_log2, float scale) {
+  constexpr int NW = kDqWaves, NQW = kDqRowsPerWave, BR = NW * NQW, BC = kTileTokens;
+  constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kDqLookahead;
+  constexpr int NQ = 4 * NDB, NS = 2 * NKS * NKB, NOP = NQ + NS;  // dq ops, then S and dP ops
+  // LDS: V tiles in buffers 0..2 at [0, 3 TILE), K tiles in buffers 0..3 at
+  // [KOFF, KOFF + 4 TILE); tile j uses K buffer j % 4 and V buffer j % 3.
+  // Buffer offsets are added per read at run time (the vector unit is idle
+  // in the MFMA phase), so one copy of the code serves every tile.
+  constexpr int KOFF = 3 * TILE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[7 * TILE];
+  auto kbuf = [&](int b) __attribute__((always_inline)) { return smem + KOFF + b * TILE; };
+  auto vbuf = [&](int b) __attribute__((always_inline)) { return smem + b * TILE; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
+  const bool lead = wave < NW / 2;  // waves 4..7 run one phase behind
   const int t = xcd_remap(blockIdx.x, total_tiles);
   const int bh = t / n_qtiles;
   int qt = t - bh * n_qtiles;
-  if (DIAG) qt = n_qtiles - 1 - qt;
+  if (DIAG) qt = n_qtiles - 1 - qt;  // longest rows of the triangle first
   const int q0 = qt * BR;
-  const int qw0 = q0 + wave * 32;
+  const int qw0 = q0 + wave * NQW;
   const int qq = qw0 + l32;
-
   const uint16_t* __restrict__ kp = kg + (size_t)bh * Sk * D;
   const uint16_t* __restrict__ vp = vg + (size_t)bh * Sk * D;
+
+  int kend = Sk;
+  if (DIAG) kend = min(kend, q0 + BR);
+  const int ntiles = (kend + BC - 1) / BC;
+  const int wtiles = DIAG ? min(ntiles, max(0, (min(qw0 + NQW, Sq) - 1) / BC + 1)) : ntiles;
+  const int lim = DIAG ? min(Sk, qq + 1) : Sk;  // keys at or past lim are masked
+
+  TileDma<D, NW, BC> dma;
+  dma.init(wave, lane);
+  dma.load(kbuf(0), kp, 0, Sk);
+  dma.load(kbuf(1), kp, BC, Sk);
+  dma.load(kbuf(3), kp, 0, Sk);  // finite data for the dS = 0 product of tile 0
+  dma.load(vbuf(0), vp, 0, Sk);
+  dma.load(vbuf(1), vp, BC, Sk);
+
   u32x4 qf[NKS], df[NKS];
   {
     const uint16_t* qrow = qg + ((size_t)bh * Sq + qq) * D;
@@ -121,71 +112,135 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const uint16_t* __restrict_
     if (lse2 == kNegInf) lse2 = kPosInf;  // a row that saw no key has P = 0
     Dq = Dg[(size_t)bh * Sq + qq];
   }
-
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  f32x16 sacc[NKB], pacc[NKB];
+  u32x4 dsb[NKB][2];  // dS^T of the last vector phase, bf16 (B operand of dq^T)
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) dsb[kb][0] = dsb[kb][1] = u32x4{0, 0, 0, 0};
 
-  int kend = Sk;
-  if (DIAG) kend = min(kend, q0 + BR);
-  const int ntiles = (kend + BC - 1) / BC;
-
-  u32x4 kr[TileItems<D>::kPerThread][4], vr[TileItems<D>::kPerThread][4];
-  load_items<D>(kr, kp, 0, Sk, tid);
-  load_items<D>(vr, vp, 0, Sk, tid);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int k0 = tile * BC;
-    __syncthreads();
-    store_items_rows<D>(ks, kr, tid);
-    store_items_tr<D>(kts, kr, tid);
-    store_items_rows<D>(vs, vr, tid);
-    __syncthreads();
-    if (tile + 1 < ntiles) {
-      load_items<D>(kr, kp, k0 + BC, Sk, tid);
-      load_items<D>(vr, vp, k0 + BC, Sk, tid);
+  const uint32_t base = lds_addr(smem);
+  uint32_t kaddr[NKS];  // row-major operand (K or V) of lane l32, chunk pair s
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) kaddr[s] = base + KOFF + (uint32_t)tile_off<D>(l32, 2 * s + g);
+  uint32_t taddr[NDB][2];  // transposed K operand
+  {
+    const int m = (lane & 15) >> 2, a4 = lane & 3, half16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 32 + 16 * half16 + 4 * a4;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        taddr[db][tt] = base + KOFF + tile_off<D>(4 * g + m + 8 * tt, d >> 3) + ((d & 4) ? 8 : 0);
     }
-    if (DIAG && k0 > qw0 + 31) continue;
-
-    f32x16 s_[NKB], dp[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s_[kb][i] = 0.f;
-        dp[kb][i] = 0.f;
-      }
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(ks + row_off<D>(kb * 32 + l32, s * 2 + g));
-        const u32x4 va = *reinterpret_cast<const u32x4*>(vs + row_off<D>(kb * 32 + l32, s * 2 + g));
-        s_[kb] = mfma32(ka, qf[s], s_[kb]);
-        dp[kb] = mfma32(va, df[s], dp[kb]);
-      }
-    const bool need_mask = (k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(s_[kb][i], scale_log2, -lse2));
-        if (need_mask) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= Sk || (DIAG && key > qq)) p = 0.f;
-        }
-        s_[kb][i] = p * (dp[kb][i] - Dq);  // dS^T
-      }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 b = pack8(s_[kb], 8 * h);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db] = mfma32(ld_tr(kts, db * 32 + l32, kb, h, g), b, acc[db]);
-      }
   }
+
+  // MFMA phase: dq^T from the K buffer at byte offset kpo (previous tile)
+  // and dsb, then S^T from the K buffer at kbo and dP^T from the V buffer at
+  // vbo (offsets from the first buffer of each kind; the vector unit is idle
+  // in this phase, so adding them per read costs nothing).
+  auto mfma_phase = [&](uint32_t kpo, uint32_t kbo, uint32_t vbo) __attribute__((always_inline)) {
+    u32x2 lo[LA + 1], hi[LA + 1];
+    u32x4 rq[LA + 1];
+    auto reads_after = [](int m) {
+      int n = 0;
+      for (int k = m + 1; k <= m + LA && k < NOP; ++k) n += (k < NQ) ? 2 : 1;
+      return n;
+    };
+    auto issue = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value, b = m % (LA + 1);
+      if constexpr (m < NQ) {
+        // K^T block db for keys 32*(gi/2) + 16*(gi%2) .. +15.
+        constexpr int gi = m / NDB, db = m % NDB;
+        constexpr int OFF = (32 * (gi >> 1) + 16 * (gi & 1)) * D * 2;
+        lo[b] = ds_read_tr16_off<OFF>(taddr[db][0] + kpo);
+        hi[b] = ds_read_tr16_off<OFF>(taddr[db][1] + kpo);
+      } else if constexpr (m < NOP) {
+        // s-major: S kb0, S kb1, dP kb0, dP kb1 for each chunk pair s.
+        constexpr int j = m - NQ, s = j / (2 * NKB), r = j % (2 * NKB), kb = r % NKB;
+        if constexpr (r < NKB) rq[b] = ds_read_b128_off<kb * 32 * D * 2>(kaddr[s] + kbo);
+        else rq[b] = ds_read_b128_off<kb * 32 * D * 2>(kaddr[s] + vbo - (uint32_t)KOFF);
+      }
+    };
+    auto run = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value, b = m % (LA + 1);
+      constexpr int N = reads_after(m);
+      issue(std::integral_constant<int, m + LA>{});
+      if constexpr (m < NQ) {
+        constexpr int gi = m / NDB, db = m % NDB;
+        lgkm_wait<N>(lo[b], hi[b]);
+        const u32x4 a = {lo[b][0], lo[b][1], hi[b][0], hi[b][1]};
+        acc[db] = mfma32(a, dsb[gi >> 1][gi & 1], acc[db]);
+      } else {
+        constexpr int j = m - NQ, s = j / (2 * NKB), r = j % (2 * NKB), kb = r % NKB;
+        lgkm_wait<N>(rq[b]);
+        if constexpr (r < NKB) {
+          if constexpr (s == 0) sacc[kb] = mfma32(rq[b], qf[0], f32x16{});
+          else sacc[kb] = mfma32(rq[b], qf[s], sacc[kb]);
+        } else {
+          if constexpr (s == 0) pacc[kb] = mfma32(rq[b], df[0], f32x16{});
+          else pacc[kb] = mfma32(rq[b], df[s], pacc[kb]);
+        }
+      }
+    };
+    static_for<LA>(issue);
+    static_for<NOP>(run);
+  };
+
+  // Vector phase of tile tt: dS^T = P^T (dP^T - D) into dsb.
+  auto vector_phase = [&](int tt) __attribute__((always_inline)) {
+    const int k0 = tt * BC;
+    const bool masked = (k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0);
+    const int r = lim - k0 - 4 * g;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lse2));
+        if (masked && 32 * kb + 8 * (i >> 2) + (i & 3) >= r) p = 0.f;
+        sacc[kb][i] = p * (pacc[kb][i] - Dq);
+      }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      dsb[kb][0] = pack8(sacc[kb], 0);
+      dsb[kb][1] = pack8(sacc[kb], 8);
+    }
+  };
+
+  // Tile tt's MFMA phase runs for 0 <= tt <= wtiles: at tt = 0 dS is still
+  // zero (the K buffer it multiplies holds finite data), and at tt = wtiles
+  // only its dq part is used.  One code shape for every tile.
+  auto mfma_tile = [&](int tt) __attribute__((always_inline)) {
+    if (tt <= wtiles)
+      mfma_phase((uint32_t)(((tt + 3) & 3) * TILE), (uint32_t)((tt & 3) * TILE), (uint32_t)((tt % 3) * TILE));
+  };
+  auto vector_tile = [&](int tt) __attribute__((always_inline)) {
+    if (tt >= 0 && tt < wtiles) vector_phase(tt);
+  };
+  // Iteration u: MFMA phase of tile u (reads K(u-1), K(u), V(u)), vector
+  // phase of tile u.  It starts by loading tile u + 2 into the K and V
+  // buffers of tiles u - 2 and u - 1, whose last readers finished in the
+  // MFMA phase of tile u - 1 two phases back (for either wave group), and
+  // ends waiting for that load; the barrier after the trailing group's wait
+  // comes two phases before anyone reads tile u + 2.
+  wait_vmem();
+  phase_barrier();
+  if (!lead) phase_barrier();
+  for (int u = 0; u <= ntiles; ++u) {
+    if (u + 2 < ntiles) {
+      dma.load(kbuf((u + 2) & 3), kp, (u + 2) * BC, Sk);
+      dma.load(vbuf((u + 2) % 3), vp, (u + 2) * BC, Sk);
+    }
+    mfma_tile(u);
+    phase_barrier();
+    vector_tile(u);
+    wait_vmem();
+    phase_barrier();
+  }
+  if (lead) phase_barrier();
 
   if (qq < Sq) {
     float* row = dqg + ((size_t)bh * Sq + qq) * D;
@@ -203,191 +258,289 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// dk/dv kernel.
+// dk/dv kernel, in two passes.
 // ---------------------------------------------------------------------------
-template <int D, bool DIAG>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
-                                                       const uint16_t* __restrict__ vg, const uint16_t* __restrict__ dog,
-                                                       const float* __restrict__ lseg, const float* __restrict__ Dg,
-                                                       float* __restrict__ dkg, float* __restrict__ dvg, int Sq, int Sk,
-                                                       int n_ktiles, int total_tiles, float scale_log2, float scale) {
-  constexpr int BK = 128, BQ = kTileTokens, NKS = D / 16, NDB = D / 32, NQB = BQ / 32;
-  constexpr int TB = BQ * D * 2;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TB + 2 * BQ * 4];
-  uint8_t* const qs = smem;
-  uint8_t* const dos = smem + TB;
-  uint8_t* const qts = smem + 2 * TB;
-  uint8_t* const dots = smem + 3 * TB;
-  float* const lse_s = reinterpret_cast<float*>(smem + 4 * TB);
-  float* const d_s = lse_s + BQ;
+constexpr int kKvWaves = 8;  // waves per block; waves w and w + 4 share a SIMD
+constexpr int kKvKeysPerWave = 32;
+constexpr int kKvLookahead = 2;  // MFMAs whose LDS operands are read ahead
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+// dv^T += dO^T P (DK = false) or dk^T += scale Q^T dS (DK = true) for one
+// ring step.  A block holds 256 keys of the chunk, 32 per wave (K and, for
+// dk, V in registers as MFMA B operands), and walks the query rows in
+// 64-row tiles.  Scores are computed with a lane per key, S = Q K^T (and
+// dP = dO V^T), so P and dS pack straight into the B operands of the
+// transposed products; lse and D of a tile's rows are staged in LDS.  Per
+// tile a wave runs two phases, as in the dq kernel:
+//   MFMA phase of tile t:  acc += X^T(t-1) Y(t-1) (X = dO, Y = P; or X = Q,
+//                          Y = dS), S(t) [and dP(t)];
+//   vector phase of tile t: P = exp2(S scale - lse) (masked), [dS = P (dP - D)],
+//                          packed to bf16.
+// Waves 4..7 run the same code one phase behind waves 0..3.  Splitting dk
+// and dv into two passes keeps each under the 256 registers two waves per
+// SIMD allow (both accumulators plus K, V, S and dP would not fit); the
+// price is computing S twice.
+template <int D, bool DIAG, bool DK>
+__global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+    const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ Dg,
+    float* __restrict__ outg, int Sq, int Sk, int n_ktiles, int total_tiles, float scale_log2, float scale) {
+  constexpr int NW = kKvWaves, NKW = kKvKeysPerWave, BK = NW * NKW, BQ = kTileTokens;
+  constexpr int NKS = D / 16, NDB = D / 32, NQB = BQ / 32, TILE = BQ * D * 2, LA = kKvLookahead;
+  constexpr int NX = 4 * NDB, NS = (DK ? 2 : 1) * NKS * NQB, NOP = NX + NS;
+  // LDS: Q tiles in buffers 0..3, dO tiles in buffers 0..3 at DOFF, then the
+  // rows' lse and D (64 floats per tile each); tile j uses buffer j % 4.
+  constexpr int DOFF = 4 * TILE, LOFF = 8 * TILE, DLOFF = LOFF + 4 * BQ * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[8 * TILE + 8 * BQ * 4];
+  auto qbuf = [&](int b) __attribute__((always_inline)) { return smem + b * TILE; };
+  auto dbuf = [&](int b) __attribute__((always_inline)) { return smem + DOFF + b * TILE; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
+  const bool lead = wave < NW / 2;  // waves 4..7 run one phase behind
   const int t = xcd_remap(blockIdx.x, total_tiles);
   const int bh = t / n_ktiles;
   const int kt = t - bh * n_ktiles;  // low key tiles see the most queries: they go first
   const int kb0 = kt * BK;
-  const int kw0 = kb0 + wave * 32;
+  const int kw0 = kb0 + wave * NKW;
   const int kk = kw0 + l32;
-
   const uint16_t* __restrict__ qp = qg + (size_t)bh * Sq * D;
-  const uint16_t* __restrict__ dp_ = dog + (size_t)bh * Sq * D;
+  const uint16_t* __restrict__ dp = dog + (size_t)bh * Sq * D;
   const float* __restrict__ lp = lseg + (size_t)bh * Sq;
   const float* __restrict__ Dp = Dg + (size_t)bh * Sq;
 
-  u32x4 kf[NKS], vf[NKS];
+  // Query tiles qs .. ntq-1; this wave's keys see tiles from ws on (causal:
+  // query q sees keys <= q).
+  const int qs = DIAG ? kb0 / BQ : 0;
+  const int ntq = (Sq + BQ - 1) / BQ;
+  const int ws = DIAG ? min(max(qs, kw0 / BQ), ntq) : qs;
+
+  TileDma<D, NW, BQ> dma;
+  dma.init(wave, lane);
+  // lse and D of tile j (rows clamped to Sq - 1) into their LDS slots: one
+  // 4-byte load per lane, issued by waves 0 and 1.
+  auto load_rows = [&](int j) __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int row = min(j * BQ + lane, Sq - 1);
+    if (wave == 0) __builtin_amdgcn_global_load_lds(lp + row, (lds_void*)(smem + LOFF + (j & 3) * BQ * 4), 4, 0, 0);
+    if (DK && wave == 1)
+      __builtin_amdgcn_global_load_lds(Dp + row, (lds_void*)(smem + DLOFF + (j & 3) * BQ * 4), 4, 0, 0);
+#endif
+  };
+  auto load_tile = [&](int j) __attribute__((always_inline)) {
+    dma.load(qbuf(j & 3), qp, j * BQ, Sq);
+    dma.load(dbuf(j & 3), dp, j * BQ, Sq);
+    load_rows(j);
+  };
+  if (qs < ntq) {
+    load_tile(qs);
+    if (qs + 1 < ntq) load_tile(qs + 1);
+    // Finite data for the Y = 0 product of the first tile.
+    dma.load(DK ? qbuf((qs + 3) & 3) : dbuf((qs + 3) & 3), DK ? qp : dp, qs * BQ, Sq);
+  }
+
+  u32x4 kf[NKS], vf[DK ? NKS : 1];
   {
     const uint16_t* krow = kg + ((size_t)bh * Sk + kk) * D;
     const uint16_t* vrow = vg + ((size_t)bh * Sk + kk) * D;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       kf[s] = (kk < Sk) ? ld16(krow + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
-      vf[s] = (kk < Sk) ? ld16(vrow + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
+      if constexpr (DK) vf[s] = (kk < Sk) ? ld16(vrow + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
     }
   }
-  f32x16 dk[NDB], dv[NDB];
+  f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[db][i] = 0.f;
-      dv[db][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  f32x16 sacc[NQB], pacc[DK ? NQB : 1];
+  u32x4 yb[NQB][2];  // P or dS of the last vector phase, bf16 (B operand of the product)
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) yb[qb][0] = yb[qb][1] = u32x4{0, 0, 0, 0};
+
+  const uint32_t base = lds_addr(smem);
+  uint32_t raddr[NKS];  // row-major operand (Q or dO) of row l32, chunk pair s
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) raddr[s] = base + (uint32_t)tile_off<D>(l32, 2 * s + g);
+  uint32_t taddr[NDB][2];  // transposed operand (dO^T or Q^T)
+  {
+    const int m = (lane & 15) >> 2, a4 = lane & 3, half16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 32 + 16 * half16 + 4 * a4;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        taddr[db][tt] = base + (DK ? 0u : (uint32_t)DOFF) + tile_off<D>(4 * g + m + 8 * tt, d >> 3) + ((d & 4) ? 8 : 0);
     }
+  }
+  const uint32_t laddr = base + LOFF + (uint32_t)(4 * g) * 4;  // this lane's rows 4g .. 4g+3 of a tile's lse
 
-  const int qstart = DIAG ? (kb0 / BQ) * BQ : 0;
-  const int ntiles = (Sq > qstart) ? (Sq - qstart + BQ - 1) / BQ : 0;
-
-  u32x4 qr[TileItems<D>::kPerThread][4], dr[TileItems<D>::kPerThread][4];
-  float lr = kPosInf, dr1 = 0.f;
-  auto load_q = [&](int q0) {
-    load_items<D>(qr, qp, q0, Sq, tid);
-    load_items<D>(dr, dp_, q0, Sq, tid);
-    if (tid < BQ) {
-      const int qi = q0 + tid;
-      lr = kPosInf;
-      dr1 = 0.f;
-      if (qi < Sq) {
-        lr = lp[qi] * kLog2e;
-        if (lr == kNegInf) lr = kPosInf;
-        dr1 = Dp[qi];
+  // MFMA phase: acc from the X buffer at xo (previous tile) and yb, then S
+  // from the Q buffer at bo [and dP from the dO buffer at bo].
+  auto mfma_phase = [&](uint32_t xo, uint32_t bo) __attribute__((always_inline)) {
+    u32x2 lo[LA + 1], hi[LA + 1];
+    u32x4 rq[LA + 1];
+    auto reads_after = [](int m) {
+      int n = 0;
+      for (int k = m + 1; k <= m + LA && k < NOP; ++k) n += (k < NX) ? 2 : 1;
+      return n;
+    };
+    auto issue = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value, b = m % (LA + 1);
+      if constexpr (m < NX) {
+        constexpr int gi = m / NDB, db = m % NDB;
+        constexpr int OFF = (32 * (gi >> 1) + 16 * (gi & 1)) * D * 2;
+        lo[b] = ds_read_tr16_off<OFF>(taddr[db][0] + xo);
+        hi[b] = ds_read_tr16_off<OFF>(taddr[db][1] + xo);
+      } else if constexpr (m < NOP) {
+        constexpr int j = m - NX, s = j / (NS / NKS), r = j % (NS / NKS), qb = r % NQB;
+        if constexpr (r < NQB) rq[b] = ds_read_b128_off<qb * 32 * D * 2>(raddr[s] + bo);
+        else rq[b] = ds_read_b128_off<qb * 32 * D * 2>(raddr[s] + bo + (uint32_t)DOFF);
       }
-    }
+    };
+    auto run = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value, b = m % (LA + 1);
+      constexpr int N = reads_after(m);
+      issue(std::integral_constant<int, m + LA>{});
+      if constexpr (m < NX) {
+        constexpr int gi = m / NDB, db = m % NDB;
+        lgkm_wait<N>(lo[b], hi[b]);
+        const u32x4 a = {lo[b][0], lo[b][1], hi[b][0], hi[b][1]};
+        acc[db] = mfma32(a, yb[gi >> 1][gi & 1], acc[db]);
+      } else {
+        constexpr int j = m - NX, s = j / (NS / NKS), r = j % (NS / NKS), qb = r % NQB;
+        lgkm_wait<N>(rq[b]);
+        if constexpr (r < NQB) {
+          if constexpr (s == 0) sacc[qb] = mfma32(rq[b], kf[0], f32x16{});
+          else sacc[qb] = mfma32(rq[b], kf[s], sacc[qb]);
+        } else {
+          if constexpr (s == 0) pacc[qb] = mfma32(rq[b], vf[0], f32x16{});
+          else pacc[qb] = mfma32(rq[b], vf[s], pacc[qb]);
+        }
+      }
+    };
+    static_for<LA>(issue);
+    static_for<NOP>(run);
   };
-  if (ntiles > 0) load_q(qstart);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int q0 = qstart + tile * BQ;
-    __syncthreads();
-    store_items_rows<D>(qs, qr, tid);
-    store_items_tr<D>(qts, qr, tid);
-    store_items_rows<D>(dos, dr, tid);
-    store_items_tr<D>(dots, dr, tid);
-    if (tid < BQ) {
-      lse_s[tid] = lr;
-      d_s[tid] = dr1;
-    }
-    __syncthreads();
-    if (tile + 1 < ntiles) load_q(q0 + BQ);
-    if (DIAG && q0 + BQ - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
 
-    f32x16 s_[NQB], dpv[NQB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s_[qb][i] = 0.f;
-        dpv[qb][i] = 0.f;
-      }
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const u32x4 qa = *reinterpret_cast<const u32x4*>(qs + row_off<D>(qb * 32 + l32, s * 2 + g));
-        const u32x4 da = *reinterpret_cast<const u32x4*>(dos + row_off<D>(qb * 32 + l32, s * 2 + g));
-        s_[qb] = mfma32(qa, kf[s], s_[qb]);
-        dpv[qb] = mfma32(da, vf[s], dpv[qb]);
-      }
-    const bool need_mask = (q0 + BQ > Sq) || (DIAG && q0 < kw0 + 31);
+  // Vector phase of tile tt: Y = P or dS into yb.  Row i of accumulator qb
+  // is query 32*qb + 8*(i/4) + 4g + i%4 of the tile.
+  auto vector_phase = [&](int tt) __attribute__((always_inline)) {
+    const int q0 = tt * BQ;
+    const bool masked = (q0 + BQ > Sq) || (DIAG && q0 < kw0 + NKW);
+    const uint32_t lo_ = laddr + (uint32_t)((tt & 3) * BQ * 4);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r0 = qb * 32 + 8 * j + 4 * g;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + r0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + r0);
+        u32x4 lr = ds_read_b128_off<0>(lo_ + (qb * 32 + 8 * j) * 4);
+        u32x4 dr = {0, 0, 0, 0};
+        if constexpr (DK) {
+          dr = ds_read_b128_off<DLOFF - LOFF>(lo_ + (qb * 32 + 8 * j) * 4);
+          lgkm_wait<0>(dr);
+        }
+        lgkm_wait<0>(lr);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * j + e;
-          float p = fast_exp2(fmaf(s_[qb][i], scale_log2, -l4[e]));
-          if (need_mask) {
-            const int qi = q0 + r0 + e;
+          float l2 = as_float(lr[e]) * kLog2e;
+          if (l2 == kNegInf) l2 = kPosInf;  // a row that saw no key has P = 0
+          float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -l2));
+          if (masked) {
+            const int qi = q0 + qb * 32 + 8 * j + 4 * g + e;
             if (qi >= Sq || (DIAG && kk > qi)) p = 0.f;
           }
-          s_[qb][i] = p;
-          dpv[qb][i] = p * (dpv[qb][i] - d4[e]);  // dS
+          if constexpr (DK) sacc[qb][i] = p * (pacc[qb][i] - as_float(dr[e]));
+          else sacc[qb][i] = p;
         }
       }
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 pb = pack8(s_[qb], 8 * h);
-        const u32x4 sb = pack8(dpv[qb], 8 * h);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[db] = mfma32(ld_tr(dots, db * 32 + l32, qb, h, g), pb, dv[db]);
-          dk[db] = mfma32(ld_tr(qts, db * 32 + l32, qb, h, g), sb, dk[db]);
-        }
-      }
+    for (int qb = 0; qb < NQB; ++qb) {
+      yb[qb][0] = pack8(sacc[qb], 0);
+      yb[qb][1] = pack8(sacc[qb], 8);
+    }
+  };
+
+  // Tile tt's MFMA phase runs for ws <= tt <= ntq: at tt = ws Y is still zero
+  // (the X buffer it multiplies holds finite data), and at tt = ntq only its
+  // product with the previous tile is used.
+  auto mfma_tile = [&](int tt) __attribute__((always_inline)) {
+    if (tt >= ws && tt <= ntq)
+      mfma_phase((uint32_t)(((tt + 3) & 3) * TILE), (uint32_t)((tt & 3) * TILE));
+  };
+  auto vector_tile = [&](int tt) __attribute__((always_inline)) {
+    if (tt >= ws && tt < ntq) vector_phase(tt);
+  };
+  // Iteration u: MFMA phase of tile u (reads Q(u), dO(u) and X(u-1)), vector
+  // phase of tile u.  It starts by loading tile u + 2 into buffers whose last
+  // readers (tiles u - 2 and u - 1's products) finished two phases back for
+  // either wave group, and ends waiting for that load.
+  wait_vmem();
+  phase_barrier();
+  if (!lead) phase_barrier();
+  for (int u = qs; u <= ntq; ++u) {
+    if (u + 2 < ntq) load_tile(u + 2);
+    mfma_tile(u);
+    phase_barrier();
+    vector_tile(u);
+    wait_vmem();
+    phase_barrier();
   }
+  if (lead) phase_barrier();
 
   if (kk < Sk) {
-    float* krow = dkg + ((size_t)bh * Sk + kk) * D;
-    float* vrow = dvg + ((size_t)bh * Sk + kk) * D;
+    float* row = outg + ((size_t)bh * Sk + kk) * D;
+    const float f = DK ? scale : 1.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int off = db * 32 + 8 * j + 4 * g;
-        f32x4 a = {dk[db][4 * j] * scale, dk[db][4 * j + 1] * scale, dk[db][4 * j + 2] * scale,
-                   dk[db][4 * j + 3] * scale};
-        a += *reinterpret_cast<const f32x4*>(krow + off);
-        *reinterpret_cast<f32x4*>(krow + off) = a;
-        f32x4 b = {dv[db][4 * j], dv[db][4 * j + 1], dv[db][4 * j + 2], dv[db][4 * j + 3]};
-        b += *reinterpret_cast<const f32x4*>(vrow + off);
-        *reinterpret_cast<f32x4*>(vrow + off) = b;
+        float* dst = row + db * 32 + 8 * j + 4 * g;
+        f32x4 val = {acc[db][4 * j] * f, acc[db][4 * j + 1] * f, acc[db][4 * j + 2] * f, acc[db][4 * j + 3] * f};
+        val += *reinterpret_cast<const f32x4*>(dst);
+        *reinterpret_cast<f32x4*>(dst) = val;
       }
   }
 }
 
 template <int D>
 hipError_t launch_dq_d(const BwdStepArgs& a, hipStream_t stream) {
-  const int nq = (a.Sq + 127) / 128;
+  constexpr int BR = kDqWaves * kDqRowsPerWave;
+  const int nq = (a.Sq + BR - 1) / BR;
   const long long total = (long long)nq * a.BH;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   if (total == 0) return hipSuccess;
   const float sl2 = a.scale * kLog2e;
   if (a.diag)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v, a.dO,
-                       a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(64 * kDqWaves), 0, stream, a.q, a.k,
+                       a.v, a.dO, a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v, a.dO,
-                       a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(64 * kDqWaves), 0, stream, a.q, a.k,
+                       a.v, a.dO, a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_dkdv_d(const BwdStepArgs& a, hipStream_t stream) {
-  const int nk = (a.Sk + 127) / 128;
+  constexpr int BK = kKvWaves * kKvKeysPerWave;
+  const int nk = (a.Sk + BK - 1) / BK;
   const long long total = (long long)nk * a.BH;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   if (total == 0) return hipSuccess;
   const float sl2 = a.scale * kLog2e;
-  if (a.diag)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v,
-                       a.dO, a.lse, a.D, a.dk, a.dv, a.Sq, a.Sk, nk, (int)total, sl2, a.scale);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)total), dim3(256), 0, stream, a.q, a.k, a.v,
-                       a.dO, a.lse, a.D, a.dk, a.dv, a.Sq, a.Sk, nk, (int)total, sl2, a.scale);
+  const dim3 grid((unsigned)total), block(64 * kKvWaves);
+#define RA_KV_LAUNCH(DIAG, DK, OUT)                                                                               \
+  hipLaunchKernelGGL((bwd_kv_kernel<D, DIAG, DK>), grid, block, 0, stream, a.q, a.k, a.v, a.dO, a.lse, a.D, OUT, \
+                     a.Sq, a.Sk, nk, (int)total, sl2, a.scale)
+  if (a.diag) {
+    RA_KV_LAUNCH(true, false, a.dv);
+    RA_KV_LAUNCH(true, true, a.dk);
+  } else {
+    RA_KV_LAUNCH(false, false, a.dv);
+    RA_KV_LAUNCH(false, true, a.dk);
+  }
+#undef RA_KV_LAUNCH
   return hipGetLastError();
 }
 

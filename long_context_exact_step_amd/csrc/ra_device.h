@@ -37,12 +37,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// A 32-bit pattern as float, taken by value.  __builtin_bit_cast applied to
+// a vector element (v[e]) reinterprets the vector's storage from element 0
+// whatever e is, so vector elements go through this scalar parameter.
+__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// Value held by lane (l ^ 32).
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, kWave);
-}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // max / sum of x over the lane pair (l, l ^ 32) with v_permlane32_swap (a
 // VALU lane exchange, no LDS round trip): swapping the upper half of one copy
@@ -68,59 +68,6 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
-
-// ---------------------------------------------------------------------------
-// LDS tiles of 64 tokens.
-//
-// Row-major tile: 64 token rows x D bf16, 16-byte chunk c of row r at
-// row_off<D>(r, c).  The XOR swizzle puts the same chunk of 16 consecutive
-// rows in 16 different bank groups, so the 32-row MFMA operand reads (one
-// 16-byte chunk per lane) are conflict-free.
-//
-// Transposed tile: D rows (one per feature) x 64 token positions bf16, 128
-// bytes per row.  Token positions are permuted within each group of 16
-// (bits 2 and 3 of the index swapped) so that the 8 tokens a lane needs as
-// the k slots of an MFMA operand -- rows 16h + 4g + {0..3, 8..11} of a 32x32
-// accumulator -- are one contiguous 16-byte chunk: chunk 4*kb + 2*h + g of a
-// row holds those tokens for 32-token block kb.
-// ---------------------------------------------------------------------------
-constexpr int kTileTokens = 64;
-
-template <int D>
-__device__ __forceinline__ int row_off(int r, int c) {
-  if constexpr (D == 128) return r * 256 + ((c ^ (r & 15)) << 4);
-  else return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
-}
-
-__device__ __forceinline__ int tr_off(int d, int c) { return d * 128 + ((c ^ ((d >> 1) & 7)) << 4); }
-
-// Writes tokens 4*kq .. 4*kq+3 (rows[rr] = features 8*dc .. 8*dc+7 of token
-// 4*kq+rr) into the transposed tile.
-__device__ __forceinline__ void store_tr4x8(uint8_t* ts, int dc, int kq, const u32x4 (&rows)[4]) {
-  const int u = kq & 3;
-  const int pos = (kq & ~3) * 4 + (((u & 1) << 1) | (u >> 1)) * 4;
-  const int half = (pos & 4) ? 8 : 0;
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    const int w = cc >> 1;
-    uint32_t lo, hi;
-    if (cc & 1) {
-      lo = (rows[0][w] >> 16) | (rows[1][w] & 0xffff0000u);
-      hi = (rows[2][w] >> 16) | (rows[3][w] & 0xffff0000u);
-    } else {
-      lo = (rows[0][w] & 0xffffu) | (rows[1][w] << 16);
-      hi = (rows[2][w] & 0xffffu) | (rows[3][w] << 16);
-    }
-    *reinterpret_cast<u32x2*>(ts + tr_off(dc * 8 + cc, pos >> 3) + half) = u32x2{lo, hi};
-  }
-}
-
-// The 16-byte operand chunk of a transposed tile: feature row d, 32-token
-// block kb, half h (tokens 16h..16h+15 of the block), lane group g.
-__device__ __forceinline__ u32x4 ld_tr(const uint8_t* ts, int d, int kb, int h, int g) {
-  return *reinterpret_cast<const u32x4*>(ts + tr_off(d, kb * 4 + 2 * h + g));
-}
 
 // Eight consecutive accumulator registers (the k slots of one MFMA operand)
 // packed to bf16.
@@ -128,6 +75,8 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& a, int base) {
   return u32x4{pack_bf16(a[base + 0], a[base + 1]), pack_bf16(a[base + 2], a[base + 3]),
                pack_bf16(a[base + 4], a[base + 5]), pack_bf16(a[base + 6], a[base + 7])};
 }
+
+constexpr int kTileTokens = 64;  // tokens per LDS tile
 
 // ---------------------------------------------------------------------------
 // Direct-to-LDS tiles of 64 tokens (row-major, D bf16 per token).
@@ -206,70 +155,23 @@ struct TileDma {
   // Tokens t0 .. t0+TOK-1 of the [n, D] bf16 matrix at `mat` into `tile`.
   // Tokens past n - 1 read row n - 1 (in bounds; the kernels mask them).
   __device__ __forceinline__ void load(uint8_t* tile, const uint16_t* mat, int t0, int n) const {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass never emits this device-only code
-    if (t0 + TOK <= n) {
-      const uint8_t* g = reinterpret_cast<const uint8_t*>(mat) + (size_t)t0 * D * 2;
 #pragma unroll
-      for (int i = 0; i < kPerWave; ++i) {
-        // Opaque to loop-invariant code motion: the per-lane part stays a
-        // 32-bit offset to a uniform base instead of a hoisted 64-bit address.
-        uint32_t o = off[i];
-        asm volatile("" : "+v"(o));
-        __builtin_amdgcn_global_load_lds(g + o, (lds_void*)(tile + (piece0 + i) * 1024), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kPerWave; ++i) {
-        const int row = (int)(off[i] / (D * 2));
-        const int tok = (t0 + row < n) ? t0 + row : n - 1;
-        const uint8_t* g = reinterpret_cast<const uint8_t*>(mat) + (size_t)tok * D * 2 +
-                           (off[i] - (uint32_t)(row * D * 2));
-        __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + (piece0 + i) * 1024), 16, 0, 0);
-      }
-    }
-#endif
+    for (int i = 0; i < kPerWave; ++i) load_piece(i, tile, mat, t0, n);
   }
 };
 
-// Loads tokens t0 .. t0+63 of a [n, D] bf16 matrix into an LDS tile (the
-// TileDma pattern, computed on the spot).
-template <int D, int NW>
-__device__ __forceinline__ void load_tile_lds(uint8_t* tile, const uint16_t* base, int t0, int n, int wave,
-                                              int lane) {
-  TileDma<D, NW> dma;
-  dma.init(wave, lane);
-  dma.load(tile, base, t0, n);
-}
-
-// 16-byte A-operand chunk of row `row`, logical chunk c, of a tile.
-template <int D>
-__device__ __forceinline__ u32x4 ld_row16(const uint8_t* tile, int row, int c) {
-  return *reinterpret_cast<const u32x4*>(tile + tile_off<D>(row, c));
-}
-
-// One ds_read_b64_tr_b16 at LDS byte address `addr`.  Issued as inline
-// assembly: the compiler cannot see which LDS buffer the intrinsic form
-// reads and would make every such read wait for all global_load_lds still in
-// flight (into any buffer).  The result is valid only after lds_wait().
-__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
+// One ds_read_b64_tr_b16 at LDS byte address addr + OFF, as inline assembly:
+// the compiler cannot see which LDS buffer the intrinsic form reads, so it
+// would wait for every direct-to-LDS load in flight (into any buffer).  The
+// result is valid only after a wait that names it (lgkm_wait).  Within each
+// 16-lane group, lane 4a+b receives element b of the 64-bit rows supplied
+// by lanes a, 4+a, 8+a, 12+a.
 template <int OFF>
 __device__ __forceinline__ u32x2 ds_read_tr16_off(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
   u32x2 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
-}
-
-// s_waitcnt lgkmcnt(0), tied to the registers it makes valid.
-__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-}
-__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
 }
 
 // One ds_read_b128 at LDS byte address addr + OFF, as inline assembly like
@@ -318,26 +220,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
-}
-
-// A operand of O^T += V^T P^T for 32 feature rows d0 .. d0+31 and the 16
-// tokens 16*h .. 16*h+15 of 32-token block kb, read transposed from a
-// row-major V tile with two ds_read_b64_tr_b16.  In each 16-lane group the
-// lane 4a+b receives element b of the 8-byte rows given by lanes a, 4+a, 8+a
-// and 12+a; lane 4m+a therefore points at token k_m, features 4a..4a+3 of
-// its 16-feature half, and every lane gets 4 tokens of one feature.  Slot
-// 4t+m of lane l holds token 32*kb + 16*h + 4*(l/32) + 8*t + m -- the order
-// in which the S^T accumulator holds its keys.  Needs lds_wait() before use.
-template <int D>
-__device__ __forceinline__ u32x4 ld_vt(const uint8_t* tile, int d0, int kb, int h, int lane) {
-  const int m = (lane & 15) >> 2, a = lane & 3;
-  const int g = lane >> 5, half16 = (lane >> 4) & 1;
-  const int d = d0 + 16 * half16 + 4 * a;
-  const uint32_t base = lds_addr(tile) + ((d & 4) ? 8 : 0);
-  const int tok0 = 32 * kb + 16 * h + 4 * g + m;
-  const u32x2 lo = ds_read_tr16(base + tile_off<D>(tok0, d >> 3));
-  const u32x2 hi = ds_read_tr16(base + tile_off<D>(tok0 + 8, d >> 3));
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // s_waitcnt vmcnt(0) (global loads, including loads into LDS, complete).
