@@ -160,6 +160,53 @@ struct TileDma {
   }
 };
 
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format,
+// no swizzle, no thread-id addressing).
+constexpr int kBufWord3 = 0x00020000;
+
+// Direct-to-LDS tile loading like TileDma, through buffer loads: the tile's
+// first row is the resource base and the rows left in the matrix set its
+// size, so the per-lane offset is the same for every tile (no vector
+// arithmetic per piece) and rows past the end fail the buffer range check,
+// which writes zeros to LDS instead of reading out of bounds.
+template <int D, int NW, int TOK = kTileTokens>
+struct TileBufDma {
+  static constexpr int kPieces = TOK * D * 2 / 1024;
+  static constexpr int kRowsPerPiece = 1024 / (D * 2);
+  static constexpr int kPerWave = kPieces / NW;
+  static_assert(kPieces % NW == 0, "tile pieces must split evenly over waves");
+  uint32_t off[kPerWave];  // byte offset of this lane's 16 bytes from the tile's first row
+  int piece0;              // first piece of this wave
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int rin = (lane * 16) / (D * 2);
+    const int p = ((lane * 16) % (D * 2)) >> 4;
+    piece0 = wave * kPerWave;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int row = (piece0 + i) * kRowsPerPiece + rin;
+      off[i] = (uint32_t)(row * D * 2 + swz<D>(row, p) * 16);
+    }
+  }
+
+  // This wave's piece i of tokens t0 .. t0+TOK-1 of the [n, D] bf16 matrix
+  // at `mat` into `tile`; tokens at or past n read as zeros.  t0 >= 0 and
+  // the arguments other than the piece index are wave-uniform.
+  __device__ __forceinline__ void load_piece(int i, uint8_t* tile, const uint16_t* mat, int t0, int n) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int rows = n > t0 ? n - t0 : 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(mat) + (size_t)t0 * D, 0, rows * (D * 2), kBufWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + (piece0 + i) * 1024), 16, off[i], 0, 0, 0);
+#endif
+  }
+
+  __device__ __forceinline__ void load(uint8_t* tile, const uint16_t* mat, int t0, int n) const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) load_piece(i, tile, mat, t0, n);
+  }
+};
+
 // One ds_read_b64_tr_b16 at LDS byte address addr + OFF, as inline assembly:
 // the compiler cannot see which LDS buffer the intrinsic form reads, so it
 // would wait for every direct-to-LDS load in flight (into any buffer).  The

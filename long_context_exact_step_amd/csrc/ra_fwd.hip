@@ -27,9 +27,11 @@
 //    score spread over three slots so no instruction waits on its own slot.
 //  * LDS operands are read three MFMAs ahead with counted waits, and the
 //    stream runs on across tiles.
-//  * K and V tiles (64 keys) go global -> LDS with global_load_lds (no
-//    registers) into four buffers each, two tiles ahead of use, one 1 KB
-//    piece per MFMA slot; one block barrier per tile.
+//  * K and V tiles (64 keys) go global -> LDS with buffer loads into LDS
+//    (no registers; a per-tile buffer resource, so the per-lane offsets are
+//    constants and keys past the chunk read as zeros) into four buffers
+//    each, two tiles ahead of use, one 1 KB piece per MFMA slot; one block
+//    barrier per tile.
 //  * exp2 with scale*log2(e) folded into one FMA, against the running
 //    maximum; the tile maximum is only taken (and O rescaled) on the exact
 //    path: a row's first tile, masked tiles, and tiles whose row sums exceed
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   // Iteration t reads K(t+1) and V(t-1); step t loads V(t+1) and K(t+3),
   // one 1 KB piece per MFMA slot in DMA_SLOT, V pieces first.  A step ends
   // waiting for all but its K pieces, which have one more step to land.
-  using Dma = TileDma<D, NW, BC>;
+  using Dma = TileBufDma<D, NW, BC>;
   constexpr int NPIECE = Dma::kPerWave;  // pieces per tile per wave
   Dma dma;
   dma.init(wave, lane);
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
 
   // Piece k of step tt's loads: V(tt+1) replaces V(tt-3) and K(tt+3)
   // replaces K(tt-1), both last read in iteration tt - 2 or earlier.  Loads
-  // past the last tile read clamped rows and are never used.
+  // past the last tile read zeros and are never used.
   auto dma_piece = [&](int tt, auto ic, int k) __attribute__((always_inline)) {
     constexpr int I = decltype(ic)::value;
     if (k < NPIECE) dma.load_piece(k, vbuf((I + 1) % NB), vp, (tt + 1) * BC, Sk);
