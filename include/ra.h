@@ -120,8 +120,9 @@ int ra_lse_merge(float* o, float* lse, const float* o_partial,
 /*
  * Device workspace bytes ra_ring_fwd (bwd == 0) or ra_ring_bwd (bwd != 0)
  * needs for these sizes.  Double-buffer forward: two slots of one K and one
- * V chunk, 4 * B*H*C*d * 2 bytes.  Resident forward: 0.  Backward: the
- * per-row term rowsum(dO * O), B*H*C * 4 bytes.  Returns 0 for invalid sizes.
+ * V chunk, 4 * B*H*C*d * 2 bytes.  Resident forward: 0.  Backward: two fp32
+ * values per row, rowsum(dO * O) and lse * log2(e), 2 * B*H*C * 4 bytes.
+ * Returns 0 for invalid sizes.
  */
 size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d,
                                int ring_mode, int bwd);

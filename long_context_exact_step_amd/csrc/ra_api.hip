@@ -200,7 +200,7 @@ int ra_lse_merge(float* o, float* lse, const float* o_partial, const float* lse_
 size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d, int ring_mode, int bwd) {
   if (P < 1 || B < 1 || H < 1 || C < 1 || (d != 64 && d != 128)) return 0;
   const size_t elems = (size_t)B * H * C * d;
-  if (bwd) return (size_t)B * H * C * sizeof(float);
+  if (bwd) return 2 * (size_t)B * H * C * sizeof(float);  // D and lse2 per row
   if (ring_mode == RA_RING_DOUBLE_BUFFER) return 4 * elems * 2;  // 2 slots x (K, V) bf16
   return 0;
 }
@@ -325,14 +325,15 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v
   hipStream_t cs = static_cast<hipStream_t>(stream);
   float* Dbuf = static_cast<float*>(workspace);
   const int rows = B * H * C;
+  float* lse2 = Dbuf + rows;
   hipError_t e = traced(RA_TRACE_BWD_ROWDOT, cs, [&] {
-    return ra::launch_bwd_rowdot(static_cast<const uint16_t*>(dO), o, Dbuf, rows, d, cs);
+    return ra::launch_bwd_rowdot(static_cast<const uint16_t*>(dO), o, lse, Dbuf, lse2, rows, d, cs);
   });
   if (e == hipSuccess) e = traced(RA_TRACE_BWD_ZERO, cs, [&] { return ra::launch_zero_f32(dq, (size_t)rows * d, cs); });
   if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd preprocess");
   for (const Step& sp : steps) {
     ra::BwdStepArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_chunks[sp.j]),
-                      static_cast<const uint16_t*>(v_chunks[sp.j]), static_cast<const uint16_t*>(dO), lse, Dbuf, dq,
+                      static_cast<const uint16_t*>(v_chunks[sp.j]), static_cast<const uint16_t*>(dO), lse2, Dbuf, dq,
                       dk_chunks[sp.j], dv_chunks[sp.j], B * H, C, C, d, scale, sp.diag};
     e = traced(sp.diag ? RA_TRACE_BWD_DQ_DIAG : RA_TRACE_BWD_DQ_FULL, cs, [&] { return ra::launch_bwd_dq(a, cs); });
     if (e == hipSuccess)

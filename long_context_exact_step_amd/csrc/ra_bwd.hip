@@ -54,7 +54,7 @@ constexpr int kDqLookahead = 2;  // MFMAs whose LDS operands are read ahead
 template <int D, bool DIAG>
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
-    const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ Dg,
+    const uint16_t* __restrict__ dog, const float* __restrict__ lse2g, const float* __restrict__ Dg,
     float* __restrict__ dqg, int Sq, int Sk, int n_qtiles, int total_tiles, float scale_log2, float scale) {
   constexpr int NW = kDqWaves, NQW = kDqRowsPerWave, BR = NW * NQW, BC = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kDqLookahead;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
   const int wtiles = DIAG ? min(ntiles, max(0, (min(qw0 + NQW, Sq) - 1) / BC + 1)) : ntiles;
   const int lim = DIAG ? min(Sk, qq + 1) : Sk;  // keys at or past lim are masked
 
-  TileDma<D, NW, BC> dma;
+  TileBufDma<D, NW, BC> dma;
   dma.init(wave, lane);
   dma.load(kbuf(0), kp, 0, Sk);
   dma.load(kbuf(1), kp, BC, Sk);
@@ -108,8 +108,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
   }
   float lse2 = kPosInf, Dq = 0.f;
   if (qq < Sq) {
-    lse2 = lseg[(size_t)bh * Sq + qq] * kLog2e;
-    if (lse2 == kNegInf) lse2 = kPosInf;  // a row that saw no key has P = 0
+    lse2 = lse2g[(size_t)bh * Sq + qq];  // +inf for a row that saw no key: P = 0
     Dq = Dg[(size_t)bh * Sq + qq];
   }
   f32x16 acc[NDB];
@@ -193,16 +192,24 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
   // Vector phase of tile tt: dS^T = P^T (dP^T - D) into dsb.
   auto vector_phase = [&](int tt) __attribute__((always_inline)) {
     const int k0 = tt * BC;
-    const bool masked = (k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0);
-    const int r = lim - k0 - 4 * g;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lse2));
-        if (masked && 32 * kb + 8 * (i >> 2) + (i & 3) >= r) p = 0.f;
+        const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lse2));
         sacc[kb][i] = p * (pacc[kb][i] - Dq);
       }
+    // Masked tiles (the diagonal band, the ragged tail) zero the entries of
+    // keys at or past the lane's limit, whatever was computed for them, in a
+    // pass of their own that full tiles skip.
+    if ((k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0)) {
+      const int r = lim - k0 - 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kb + 8 * (i >> 2) + (i & 3) >= r) sacc[kb][i] = 0.f;
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       dsb[kb][0] = pack8(sacc[kb], 0);
@@ -282,7 +289,7 @@ constexpr int kKvLookahead = 2;  // MFMAs whose LDS operands are read ahead
 template <int D, bool DIAG, bool DK>
 __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
-    const uint16_t* __restrict__ dog, const float* __restrict__ lseg, const float* __restrict__ Dg,
+    const uint16_t* __restrict__ dog, const float* __restrict__ lse2g, const float* __restrict__ Dg,
     float* __restrict__ outg, int Sq, int Sk, int n_ktiles, int total_tiles, float scale_log2, float scale) {
   constexpr int NW = kKvWaves, NKW = kKvKeysPerWave, BK = NW * NKW, BQ = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NQB = BQ / 32, TILE = BQ * D * 2, LA = kKvLookahead;
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   const int kk = kw0 + l32;
   const uint16_t* __restrict__ qp = qg + (size_t)bh * Sq * D;
   const uint16_t* __restrict__ dp = dog + (size_t)bh * Sq * D;
-  const float* __restrict__ lp = lseg + (size_t)bh * Sq;
+  const float* __restrict__ lp = lse2g + (size_t)bh * Sq;
   const float* __restrict__ Dp = Dg + (size_t)bh * Sq;
 
   // Query tiles qs .. ntq-1; this wave's keys see tiles from ws on (causal:
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   const int ntq = (Sq + BQ - 1) / BQ;
   const int ws = DIAG ? min(max(qs, kw0 / BQ), ntq) : qs;
 
-  TileDma<D, NW, BQ> dma;
+  TileBufDma<D, NW, BQ> dma;
   dma.init(wave, lane);
   // lse and D of tile j (rows clamped to Sq - 1) into their LDS slots: one
   // 4-byte load per lane, issued by waves 0 and 1.
@@ -331,6 +338,14 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     dma.load(qbuf(j & 3), qp, j * BQ, Sq);
     dma.load(dbuf(j & 3), dp, j * BQ, Sq);
     load_rows(j);
+  };
+  // Piece k of tile j's loads: this wave's Q pieces, its dO pieces, then the
+  // lse / D rows (waves 0 and 1).
+  constexpr int NPW = decltype(dma)::kPerWave, NPC = 2 * NPW + 1;
+  auto load_piece = [&](int j, int k) __attribute__((always_inline)) {
+    if (k < NPW) dma.load_piece(k, qbuf(j & 3), qp, j * BQ, Sq);
+    else if (k < 2 * NPW) dma.load_piece(k - NPW, dbuf(j & 3), dp, j * BQ, Sq);
+    else load_rows(j);
   };
   if (qs < ntq) {
     load_tile(qs);
@@ -378,7 +393,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
 
   // MFMA phase: acc from the X buffer at xo (previous tile) and yb, then S
   // from the Q buffer at bo [and dP from the dO buffer at bo].
-  auto mfma_phase = [&](uint32_t xo, uint32_t bo) __attribute__((always_inline)) {
+  auto mfma_phase = [&](uint32_t xo, uint32_t bo, auto&& hook) __attribute__((always_inline)) {
     u32x2 lo[LA + 1], hi[LA + 1];
     u32x4 rq[LA + 1];
     auto reads_after = [](int m) {
@@ -419,6 +434,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
           else pacc[qb] = mfma32(rq[b], vf[s], pacc[qb]);
         }
       }
+      hook(mc);
     };
     static_for<LA>(issue);
     static_for<NOP>(run);
@@ -430,31 +446,52 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     const int q0 = tt * BQ;
     const bool masked = (q0 + BQ > Sq) || (DIAG && q0 < kw0 + NKW);
     const uint32_t lo_ = laddr + (uint32_t)((tt & 3) * BQ * 4);
+    // The lse (and D) values of accumulator qb's 32 rows, four rows per read,
+    // are requested JB row groups at a time and consumed in order with counted
+    // waits, so their LDS latency is paid once per batch, not once per read.
+    constexpr int R = DK ? 2 : 1;   // reads per row group
+    constexpr int JB = DK ? 2 : 4;  // row groups per batch (dk: fewer registers)
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
+      static_for<4 / JB>([&](auto bc) __attribute__((always_inline)) {
+      u32x4 lrs[JB], drs[JB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 lr = ds_read_b128_off<0>(lo_ + (qb * 32 + 8 * j) * 4);
+      for (int jj = 0; jj < JB; ++jj) {
+        const int j = decltype(bc)::value * JB + jj;
+        lrs[jj] = ds_read_b128_off<0>(lo_ + (qb * 32 + 8 * j) * 4);
+        if constexpr (DK) drs[jj] = ds_read_b128_off<DLOFF - LOFF>(lo_ + (qb * 32 + 8 * j) * 4);
+      }
+      static_for<JB>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int jj = decltype(jc)::value, j = decltype(bc)::value * JB + jj;
+        lgkm_wait<(JB - 1 - jj) * R>(lrs[jj]);
+        u32x4 lr = lrs[jj];
         u32x4 dr = {0, 0, 0, 0};
         if constexpr (DK) {
-          dr = ds_read_b128_off<DLOFF - LOFF>(lo_ + (qb * 32 + 8 * j) * 4);
-          lgkm_wait<0>(dr);
+          lgkm_wait<(JB - 1 - jj) * R>(drs[jj]);
+          dr = drs[jj];
         }
-        lgkm_wait<0>(lr);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * j + e;
-          float l2 = as_float(lr[e]) * kLog2e;
-          if (l2 == kNegInf) l2 = kPosInf;  // a row that saw no key has P = 0
-          float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -l2));
-          if (masked) {
-            const int qi = q0 + qb * 32 + 8 * j + 4 * g + e;
-            if (qi >= Sq || (DIAG && kk > qi)) p = 0.f;
-          }
+          // lse2 is +inf for a row that saw no key: P = 0.
+          const float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -as_float(lr[e])));
           if constexpr (DK) sacc[qb][i] = p * (pacc[qb][i] - as_float(dr[e]));
           else sacc[qb][i] = p;
         }
-      }
+      });
+      });
+    // Masked tiles (the diagonal band, the ragged tail) zero the entries of
+    // rows past the chunk or of keys after the query, whatever was computed
+    // for them, in a pass of their own that full tiles skip.
+    if (masked) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = q0 + qb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (qi >= Sq || (DIAG && kk > qi)) sacc[qb][i] = 0.f;
+        }
+    }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       yb[qb][0] = pack8(sacc[qb], 0);
@@ -465,22 +502,33 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   // Tile tt's MFMA phase runs for ws <= tt <= ntq: at tt = ws Y is still zero
   // (the X buffer it multiplies holds finite data), and at tt = ntq only its
   // product with the previous tile is used.
+  // The phase of tile tt also issues tile tt + 2's loads, one piece every
+  // EVERY MFMAs; a wave without that phase issues them all at once.  Tiles
+  // past the last one load zeros (or clamped rows) that nothing reads.
   auto mfma_tile = [&](int tt) __attribute__((always_inline)) {
-    if (tt >= ws && tt <= ntq)
-      mfma_phase((uint32_t)(((tt + 3) & 3) * TILE), (uint32_t)((tt & 3) * TILE));
+    constexpr int EVERY = NOP / NPC;
+    if (tt >= ws && tt <= ntq) {
+      mfma_phase((uint32_t)(((tt + 3) & 3) * TILE), (uint32_t)((tt & 3) * TILE),
+                 [&](auto mc) __attribute__((always_inline)) {
+                   constexpr int m = decltype(mc)::value;
+                   if constexpr (m % EVERY == EVERY / 2 && m / EVERY < NPC) load_piece(tt + 2, m / EVERY);
+                 });
+    } else {
+#pragma unroll
+      for (int k = 0; k < NPC; ++k) load_piece(tt + 2, k);
+    }
   };
   auto vector_tile = [&](int tt) __attribute__((always_inline)) {
     if (tt >= ws && tt < ntq) vector_phase(tt);
   };
   // Iteration u: MFMA phase of tile u (reads Q(u), dO(u) and X(u-1)), vector
-  // phase of tile u.  It starts by loading tile u + 2 into buffers whose last
+  // phase of tile u.  The MFMA phase loads tile u + 2 into buffers whose last
   // readers (tiles u - 2 and u - 1's products) finished two phases back for
-  // either wave group, and ends waiting for that load.
+  // either wave group; the iteration ends waiting for that load.
   wait_vmem();
   phase_barrier();
   if (!lead) phase_barrier();
   for (int u = qs; u <= ntq; ++u) {
-    if (u + 2 < ntq) load_tile(u + 2);
     mfma_tile(u);
     phase_barrier();
     vector_tile(u);
@@ -514,10 +562,10 @@ hipError_t launch_dq_d(const BwdStepArgs& a, hipStream_t stream) {
   const float sl2 = a.scale * kLog2e;
   if (a.diag)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(64 * kDqWaves), 0, stream, a.q, a.k,
-                       a.v, a.dO, a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
+                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(64 * kDqWaves), 0, stream, a.q, a.k,
-                       a.v, a.dO, a.lse, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
+                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
   return hipGetLastError();
 }
 
@@ -531,7 +579,7 @@ hipError_t launch_dkdv_d(const BwdStepArgs& a, hipStream_t stream) {
   const float sl2 = a.scale * kLog2e;
   const dim3 grid((unsigned)total), block(64 * kKvWaves);
 #define RA_KV_LAUNCH(DIAG, DK, OUT)                                                                               \
-  hipLaunchKernelGGL((bwd_kv_kernel<D, DIAG, DK>), grid, block, 0, stream, a.q, a.k, a.v, a.dO, a.lse, a.D, OUT, \
+  hipLaunchKernelGGL((bwd_kv_kernel<D, DIAG, DK>), grid, block, 0, stream, a.q, a.k, a.v, a.dO, a.lse2, a.D, OUT, \
                      a.Sq, a.Sk, nk, (int)total, sl2, a.scale)
   if (a.diag) {
     RA_KV_LAUNCH(true, false, a.dv);

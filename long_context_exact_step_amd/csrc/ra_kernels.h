@@ -26,17 +26,19 @@ hipError_t launch_fwd_step(const FwdStepArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(float* o, float* lse, const float* op, const float* lp,
                             int rows, int d, hipStream_t stream);
 
-// Backward: D = rowsum(dO * O) per row.
-hipError_t launch_bwd_rowdot(const uint16_t* dO, const float* o, float* D, int rows, int d,
-                             hipStream_t stream);
+// Backward: D = rowsum(dO * O) per row, and lse2 = lse * log2(e) per row
+// (+inf where lse is -inf).
+hipError_t launch_bwd_rowdot(const uint16_t* dO, const float* o, const float* lse, float* D, float* lse2,
+                             int rows, int d, hipStream_t stream);
 
-// Backward of one ring step against one KV chunk.  Uses the final lse and D.
+// Backward of one ring step against one KV chunk.  Uses the final lse (in
+// base 2) and D.
 struct BwdStepArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dO;
-  const float* lse;
+  const float* lse2;  // final lse * log2(e) per row, +inf for a row that saw no key
   const float* D;
   float* dq;   // accumulated (+=)
   float* dk;   // accumulated (+=)

@@ -47,11 +47,15 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(float* __restrict__ o, f
 }
 
 // D[row] = sum_d dO[row, d] * O[row, d]; 32 lanes per row (D = 128: 4 values
-// per lane; D = 64: 2), butterfly sum over the 32 lanes.
+// per lane; D = 64: 2), butterfly sum over the 32 lanes.  Also the row's lse
+// in base 2, lse * log2(e), with -inf (a row that saw no key) mapped to +inf
+// so that exp2(s - lse2) is 0 for it.
 template <int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ dO,
                                                      const float* __restrict__ o,
-                                                     float* __restrict__ out, int rows) {
+                                                     const float* __restrict__ lse,
+                                                     float* __restrict__ out, float* __restrict__ lse2,
+                                                     int rows) {
   constexpr int VPL = D / 32;
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = gid >> 5, c = gid & 31;
@@ -67,7 +71,11 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
   }
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
-  if (ok && c == 0) out[row] = acc;
+  if (ok && c == 0) {
+    out[row] = acc;
+    const float l2 = lse[row] * kLog2e;
+    lse2[row] = (l2 == -__builtin_inff()) ? __builtin_inff() : l2;
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, size_t n) {
@@ -91,14 +99,14 @@ hipError_t launch_lse_merge(float* o, float* lse, const float* op, const float* 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_rowdot(const uint16_t* dO, const float* o, float* D, int rows, int d,
-                             hipStream_t stream) {
+hipError_t launch_bwd_rowdot(const uint16_t* dO, const float* o, const float* lse, float* D, float* lse2,
+                             int rows, int d, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)(((long long)rows * 32 + 255) / 256);
   if (d == 128)
-    hipLaunchKernelGGL(rowdot_kernel<128>, dim3(blocks), dim3(256), 0, stream, dO, o, D, rows);
+    hipLaunchKernelGGL(rowdot_kernel<128>, dim3(blocks), dim3(256), 0, stream, dO, o, lse, D, lse2, rows);
   else if (d == 64)
-    hipLaunchKernelGGL(rowdot_kernel<64>, dim3(blocks), dim3(256), 0, stream, dO, o, D, rows);
+    hipLaunchKernelGGL(rowdot_kernel<64>, dim3(blocks), dim3(256), 0, stream, dO, o, lse, D, lse2, rows);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

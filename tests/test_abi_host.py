@@ -115,7 +115,7 @@ def test_workspace_sizes(L):
     # Double buffer: 2 slots x (K + V) x B*H*C*d bf16.
     assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 1, 0) == 2 * 2 * 32 * 32768 * 128 * 2
     assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 0, 0) == 0
-    assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 128, 0, 1) == 32 * 16384 * 4
+    assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 128, 0, 1) == 2 * 32 * 16384 * 4
     assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 96, 0, 1) == 0
 
 
