@@ -141,7 +141,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
   // and dsb, then S^T from the K buffer at kbo and dP^T from the V buffer at
   // vbo (offsets from the first buffer of each kind; the vector unit is idle
   // in this phase, so adding them per read costs nothing).
-  auto mfma_phase = [&](uint32_t kpo, uint32_t kbo, uint32_t vbo) __attribute__((always_inline)) {
+  auto mfma_phase = [&](uint32_t kpo, uint32_t kbo, uint32_t vbo, auto&& hook) __attribute__((always_inline)) {
     u32x2 lo[LA + 1], hi[LA + 1];
     u32x4 rq[LA + 1];
     auto reads_after = [](int m) {
@@ -184,6 +184,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
           else pacc[kb] = mfma32(rq[b], df[s], pacc[kb]);
         }
       }
+      hook(mc);
     };
     static_for<LA>(issue);
     static_for<NOP>(run);
@@ -220,26 +221,41 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
   // Tile tt's MFMA phase runs for 0 <= tt <= wtiles: at tt = 0 dS is still
   // zero (the K buffer it multiplies holds finite data), and at tt = wtiles
   // only its dq part is used.  One code shape for every tile.
+  // On full chunks the phase also issues tile tt + 2's loads (this wave's K
+  // pieces, then its V pieces), one piece every EVERY MFMAs.  Tiles past the
+  // chunk load zeros that nothing reads.  On the diagonal chunk, where waves
+  // run different tile counts, the loads go out together at the start of
+  // the iteration (the per-wave branch costs the spread version registers).
+  constexpr int NPW = decltype(dma)::kPerWave, NPC = 2 * NPW;
+  auto load_piece = [&](int j, int k) __attribute__((always_inline)) {
+    if (k < NPW) dma.load_piece(k, kbuf(j & 3), kp, j * BC, Sk);
+    else dma.load_piece(k - NPW, vbuf(j % 3), vp, j * BC, Sk);
+  };
   auto mfma_tile = [&](int tt) __attribute__((always_inline)) {
+    constexpr int EVERY = NOP / NPC;
     if (tt <= wtiles)
-      mfma_phase((uint32_t)(((tt + 3) & 3) * TILE), (uint32_t)((tt & 3) * TILE), (uint32_t)((tt % 3) * TILE));
+      mfma_phase((uint32_t)(((tt + 3) & 3) * TILE), (uint32_t)((tt & 3) * TILE), (uint32_t)((tt % 3) * TILE),
+                 [&](auto mc) __attribute__((always_inline)) {
+                   constexpr int m = decltype(mc)::value;
+                   if constexpr (!DIAG && m % EVERY == EVERY / 2 && m / EVERY < NPC) load_piece(tt + 2, m / EVERY);
+                 });
   };
   auto vector_tile = [&](int tt) __attribute__((always_inline)) {
     if (tt >= 0 && tt < wtiles) vector_phase(tt);
   };
   // Iteration u: MFMA phase of tile u (reads K(u-1), K(u), V(u)), vector
-  // phase of tile u.  It starts by loading tile u + 2 into the K and V
+  // phase of tile u.  The MFMA phase loads tile u + 2 into the K and V
   // buffers of tiles u - 2 and u - 1, whose last readers finished in the
-  // MFMA phase of tile u - 1 two phases back (for either wave group), and
-  // ends waiting for that load; the barrier after the trailing group's wait
-  // comes two phases before anyone reads tile u + 2.
+  // MFMA phase of tile u - 1 two phases back (for either wave group); the
+  // iteration ends waiting for that load, and the barrier after the trailing
+  // group's wait comes two phases before anyone reads tile u + 2.
   wait_vmem();
   phase_barrier();
   if (!lead) phase_barrier();
   for (int u = 0; u <= ntiles; ++u) {
-    if (u + 2 < ntiles) {
-      dma.load(kbuf((u + 2) & 3), kp, (u + 2) * BC, Sk);
-      dma.load(vbuf((u + 2) % 3), vp, (u + 2) * BC, Sk);
+    if (DIAG && u + 2 < ntiles) {
+#pragma unroll
+      for (int k = 0; k < NPC; ++k) load_piece(u + 2, k);
     }
     mfma_tile(u);
     phase_barrier();
