@@ -35,6 +35,8 @@ def run_step(q, k, v, step, causal, scale):
     (2, 1, 293, 517, 64, False),
     (1, 2, 1, 700, 128, False),
     (1, 1, 256, 256, 128, False),
+    (1, 2, 600, 600, 128, True),
+    (1, 1, 520, 1000, 64, False),
 ])
 def test_step_fwd_matches_oracle(B, H, Sq, Sk, d, diag):
     print(f"step_fwd B={B} H={H} Sq={Sq} Sk={Sk} d={d} diag={diag}", flush=True)
@@ -166,7 +168,9 @@ def _bwd_case(P, C, d, causal, rank, B=1, H=2, wid=105):
 
 
 @pytest.mark.parametrize("P,C,d,causal", [(3, 100, 128, True), (2, 129, 64, True), (3, 64, 128, False),
-                                          (1, 200, 128, True)])
+                                          (1, 200, 128, True),
+                                          # several 256-row blocks and 64-row tiles, ragged tails
+                                          (2, 600, 128, True), (2, 300, 64, True), (2, 520, 128, False)])
 def test_ring_bwd_matches_oracle(P, C, d, causal):
     for rank in range(P):
         print(f"ring_bwd P={P} C={C} d={d} causal={causal} rank={rank}", flush=True)
