@@ -16,7 +16,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWave = 64;
 constexpr int kXcds = 8;  // MI355X: 8 XCDs x 32 CUs; workgroups go round-robin over XCDs
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -108,67 +107,20 @@ __device__ __forceinline__ int tile_off(int row, int c) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Direct-to-LDS loading of 64-token tiles with global_load_lds (16 bytes per
-// lane, 1 KB per instruction, no registers).  Wave `wave` of NW issues its
-// share of the tile's 1 KB pieces; piece p fills LDS bytes [1024p, 1024p+1024)
-// of the tile in lane order, so lane l loads the global chunk that belongs
-// at physical slot l of the piece.  The per-lane byte offset inside a tile's
-// rows is fixed, so a full tile needs only a uniform base address.
-template <int D, int NW, int TOK = kTileTokens>
-struct TileDma {
-  static constexpr int kPieces = TOK * D * 2 / 1024;
-  static constexpr int kRowsPerPiece = 1024 / (D * 2);
-  static constexpr int kPerWave = kPieces / NW;
-  static_assert(kPieces % NW == 0, "tile pieces must split evenly over waves");
-  uint32_t off[kPerWave];  // byte offset of this lane's 16 bytes from the tile's first row
-  int piece0;              // first piece of this wave
-
-  __device__ __forceinline__ void init(int wave, int lane) {
-    const int rin = (lane * 16) / (D * 2);
-    const int p = ((lane * 16) % (D * 2)) >> 4;
-    piece0 = wave * kPerWave;
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      const int row = (piece0 + i) * kRowsPerPiece + rin;
-      off[i] = (uint32_t)(row * D * 2 + swz<D>(row, p) * 16);
-    }
-  }
-
-  // This wave's piece i of tokens t0 .. t0+TOK-1 of the [n, D] bf16 matrix
-  // at `mat` into `tile`.  Tokens past n - 1 read row n - 1 (in bounds; the
-  // kernels mask them), so any t0 >= 0 is safe.
-  __device__ __forceinline__ void load_piece(int i, uint8_t* tile, const uint16_t* mat, int t0, int n) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    // Branch-free (it is issued from inside MFMA streams): the row is clamped
-    // to n - 1 with a min, a no-op on full tiles.
-    uint32_t o = off[i];
-    asm volatile("" : "+v"(o));  // keeps a 32-bit offset (no hoisted 64-bit address)
-    const uint32_t row = o / (D * 2);
-    const uint32_t tok = min((uint32_t)t0 + row, (uint32_t)(n - 1));
-    const uint8_t* g = reinterpret_cast<const uint8_t*>(mat) + (tok * (uint32_t)(D * 2) + (o - row * (D * 2)));
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)(tile + (piece0 + i) * 1024), 16, 0, 0);
-#endif
-  }
-
-  // Tokens t0 .. t0+TOK-1 of the [n, D] bf16 matrix at `mat` into `tile`.
-  // Tokens past n - 1 read row n - 1 (in bounds; the kernels mask them).
-  __device__ __forceinline__ void load(uint8_t* tile, const uint16_t* mat, int t0, int n) const {
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) load_piece(i, tile, mat, t0, n);
-  }
-};
 
 // Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format,
 // no swizzle, no thread-id addressing).
 constexpr int kBufWord3 = 0x00020000;
 
-// Direct-to-LDS tile loading like TileDma, through buffer loads: the tile's
-// first row is the resource base and the rows left in the matrix set its
-// size, so the per-lane offset is the same for every tile (no vector
-// arithmetic per piece) and rows past the end fail the buffer range check,
-// which writes zeros to LDS instead of reading out of bounds.
+// Direct-to-LDS loading of 64-token tiles with buffer loads into LDS (16
+// bytes per lane, 1 KB per instruction, no registers).  Wave `wave` of NW
+// issues its share of the tile's 1 KB pieces; piece p fills LDS bytes
+// [1024p, 1024p+1024) of the tile in lane order, so lane l loads the global
+// chunk that belongs at physical slot l of the piece.  The tile's first row
+// is the buffer resource's base and the rows left in the matrix set its size,
+// so the per-lane offset is the same for every tile (no vector arithmetic per
+// piece), and rows past the end fail the buffer range check, which writes
+// zeros to LDS instead of reading out of bounds.
 template <int D, int NW, int TOK = kTileTokens>
 struct TileBufDma {
   static constexpr int kPieces = TOK * D * 2 / 1024;
