@@ -14,6 +14,12 @@ What it computes, and the passage each function follows:
   Models Without OOM: Ring Attention", section "Ring Attention Demystified",
   item 5 "Ring Completion"; "Context Parallelism", section 2 "Ring Attention",
   "How It Works").  The oracle therefore is the plain definition, not the ring.
+  Key/value tensors may carry fewer heads than the queries (grouped-query
+  attention, named in "Training Long-Context Models Without OOM: Ring
+  Attention", "Ring Attention vs. DeepSpeed Ulysses (All-to-All)"): query
+  head h reads key/value head h // (H / Hk), and the backward sums a key/value
+  head's gradient over its group.  Pinned against the library's attention
+  with grouped heads, forward and autograd.
 * ``attention.attention_bwd`` / ``attention_bwd_key_rows`` -- the textbook
   gradient of softmax attention.  The pages give no backward formula; the
   reading (recompute P from the final log-sum-exp) is listed in the design doc.

@@ -17,6 +17,17 @@ import numpy as np
 NEG_INF = -np.inf
 
 
+def _kv_group(H, Hk):
+    """Query heads per key/value head.  Grouped-query attention: query head h
+    reads key/value head h // (H / Hk) (contiguous groups; the pages name GQA
+    in "Training Long-Context Models Without OOM: Ring Attention", "Ring
+    Attention vs. DeepSpeed Ulysses (All-to-All)", but not its head order).
+    Hk == H is ordinary multi-head attention."""
+    if Hk < 1 or H % Hk:
+        raise ValueError(f"{H} query heads do not split into groups over {Hk} key/value heads")
+    return H // Hk
+
+
 def _visible_mask(q_pos, k_pos):
     """[nq, nk] bool: key k visible to query q under causal masking (k <= q)."""
     return k_pos[None, :] <= q_pos[:, None]
@@ -35,7 +46,8 @@ def attention_fwd(q, k, v, scale, causal, q_pos=None, k_pos=None, block=512):
     chunking and no merge: each block of query rows meets every visible key at
     once.
 
-    q: [B, H, Sq, d]; k, v: [B, H, Sk, d].
+    q: [B, H, Sq, d]; k, v: [B, Hk, Sk, d] with H a multiple of Hk (query
+    head h uses key/value head h // (H / Hk)).
     q_pos: [Sq] global positions of the query rows (default 0..Sq-1).
     k_pos: [Sk] global positions of the keys (default 0..Sk-1).
     Returns (O [B, H, Sq, d], lse [B, H, Sq]).  A row with no visible key gets
@@ -43,6 +55,7 @@ def attention_fwd(q, k, v, scale, causal, q_pos=None, k_pos=None, block=512):
     """
     B, H, Sq, d = q.shape
     Sk = k.shape[2]
+    grp = _kv_group(H, k.shape[1])
     if q_pos is None:
         q_pos = np.arange(Sq)
     if k_pos is None:
@@ -63,8 +76,8 @@ def attention_fwd(q, k, v, scale, causal, q_pos=None, k_pos=None, block=512):
                     order = np.arange(Sk)
                 if order.size == 0:
                     continue
-                kb = k[b, h, order]
-                vb = v[b, h, order]
+                kb = k[b, h // grp, order]
+                vb = v[b, h // grp, order]
                 s = scale * (qb @ kb.T)
                 if causal:
                     vis = _visible_mask(q_pos[r0:r1], k_pos[order])
@@ -165,13 +178,15 @@ def attention_bwd(q, k, v, do, scale, causal, q_pos=None, block=512):
     P = softmax(scale q k^T) over visible keys,
       dV = P^T dO;  dP = dO V^T;  D = rowsum(dO * O) = rowsum(P * dP);
       dS = P * (dP - D);  dQ = scale dS K;  dK = scale dS^T Q.
-    q, do: [B, H, Sq, d] (the local rows); k, v: [B, H, Sk, d] (the global
-    sequence).  Returns (dq [B,H,Sq,d], dk [B,H,Sk,d], dv [B,H,Sk,d]); only the
-    given query rows contribute to dk, dv.  Every query row must see at least
-    one key.
+    q, do: [B, H, Sq, d] (the local rows); k, v: [B, Hk, Sk, d] (the global
+    sequence; query head h uses key/value head h // (H / Hk)).  Returns
+    (dq [B,H,Sq,d], dk [B,Hk,Sk,d], dv [B,Hk,Sk,d]); only the given query rows
+    contribute to dk, dv, and a key/value head's gradient sums over the query
+    heads of its group.  Every query row must see at least one key.
     """
     B, H, Sq, d = q.shape
     Sk = k.shape[2]
+    grp = _kv_group(H, k.shape[1])
     if q_pos is None:
         q_pos = np.arange(Sq)
     q_pos = np.asarray(q_pos)
@@ -185,7 +200,8 @@ def attention_bwd(q, k, v, do, scale, causal, q_pos=None, block=512):
                 r1 = min(Sq, r0 + block)
                 nk = int(q_pos[r0:r1].max()) + 1 if causal else Sk
                 nk = min(nk, Sk)
-                kb, vb = k[b, h, :nk], v[b, h, :nk]
+                kh = h // grp
+                kb, vb = k[b, kh, :nk], v[b, kh, :nk]
                 vis = _visible_mask(q_pos[r0:r1], k_pos[:nk]) if causal else None
                 _, p, _, ob = _fwd_block_stats(q[b, h, r0:r1], kb, vb, scale, vis)
                 dob = do[b, h, r0:r1]
@@ -193,8 +209,8 @@ def attention_bwd(q, k, v, do, scale, causal, q_pos=None, block=512):
                 D = (dob * ob).sum(axis=1)
                 ds = p * (dp - D[:, None])
                 dq[b, h, r0:r1] = scale * (ds @ kb)
-                dk[b, h, :nk] += scale * (ds.T @ q[b, h, r0:r1])
-                dv[b, h, :nk] += p.T @ dob
+                dk[b, kh, :nk] += scale * (ds.T @ q[b, h, r0:r1])
+                dv[b, kh, :nk] += p.T @ dob
     return dq, dk, dv
 
 
@@ -204,21 +220,24 @@ def attention_bwd_key_rows(q, k, v, do, scale, causal, key_rows, q_pos=None, blo
     forward over all query rows is computed; only the columns of P, dP and dS
     that belong to ``key_rows`` are formed.
 
-    Returns (dk_rows [B,H,len(key_rows),d], dv_rows [B,H,len(key_rows),d]).
+    Returns (dk_rows [B,Hk,len(key_rows),d], dv_rows [B,Hk,len(key_rows),d]).
     """
     B, H, Sq, d = q.shape
+    Hk = k.shape[1]
+    grp = _kv_group(H, Hk)
     if q_pos is None:
         q_pos = np.arange(Sq)
     q_pos = np.asarray(q_pos)
     key_rows = np.asarray(key_rows)
     o, lse = attention_fwd(q, k, v, scale, causal, q_pos=q_pos, block=block)
     nr = key_rows.size
-    dk_r = np.zeros((B, H, nr, d))
-    dv_r = np.zeros((B, H, nr, d))
+    dk_r = np.zeros((B, Hk, nr, d))
+    dv_r = np.zeros((B, Hk, nr, d))
     for b in range(B):
         for h in range(H):
-            ks = k[b, h, key_rows]
-            vs = v[b, h, key_rows]
+            kh = h // grp
+            ks = k[b, kh, key_rows]
+            vs = v[b, kh, key_rows]
             for r0 in range(0, Sq, block):
                 r1 = min(Sq, r0 + block)
                 s = scale * (q[b, h, r0:r1] @ ks.T)
@@ -229,6 +248,6 @@ def attention_bwd_key_rows(q, k, v, do, scale, causal, key_rows, q_pos=None, blo
                 dp = dob @ vs.T
                 D = (dob * o[b, h, r0:r1]).sum(axis=1)
                 ds = p * (dp - D[:, None])
-                dk_r[b, h] += scale * (ds.T @ q[b, h, r0:r1])
-                dv_r[b, h] += p.T @ dob
+                dk_r[b, kh] += scale * (ds.T @ q[b, h, r0:r1])
+                dv_r[b, kh] += p.T @ dob
     return dk_r, dv_r

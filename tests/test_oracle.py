@@ -69,6 +69,22 @@ def pin_sdpa(fwd):
     return None
 
 
+def pin_sdpa_gqa(fwd):
+    """Grouped-query attention (fewer key/value heads than query heads): the
+    library's fp64 attention with enable_gqa, which repeats each key/value
+    head over a contiguous group of query heads."""
+    for H, Hk in ((6, 2), (6, 3), (4, 1)):
+        q, k, v = rnd(1, H, 23, 8, seed=70 + H), rnd(1, Hk, 23, 8, seed=71 + Hk), rnd(1, Hk, 23, 8, seed=72)
+        for causal in (False, True):
+            o, _ = fwd(q, k, v, 0.35, causal)
+            tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk, tv, is_causal=causal, scale=0.35, enable_gqa=True).numpy()
+            if not np.allclose(o, ref, atol=TIGHT, rtol=0):
+                return f"sdpa gqa H={H} Hk={Hk} causal={causal} err={np.abs(o - ref).max()}"
+    return None
+
+
 def brute(q, k, v, scale, causal, q_pos):
     """Attention straight from its definition, scalar by scalar."""
     B, H, Sq, d = q.shape
@@ -213,6 +229,28 @@ def pin_bwd_autograd(bwd):
     return None
 
 
+def pin_bwd_autograd_gqa(bwd):
+    """Grouped-query backward: autograd through the library's fp64 attention
+    with enable_gqa; a key/value head's gradient sums over its query heads."""
+    P, C, d, H, Hk = 3, 6, 8, 6, 2
+    qa = rnd(1, H, P * C, d, seed=80)
+    k, v = rnd(1, Hk, P * C, d, seed=81), rnd(1, Hk, P * C, d, seed=82)
+    do = rnd(1, H, C, d, seed=83)
+    for rank in (0, 2):
+        pos = rank * C + np.arange(C)
+        q = qa[:, :, rank * C:(rank + 1) * C]
+        dq, dk, dv = bwd(q, k, v, do, 0.3, True, q_pos=pos)
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        mask = torch.from_numpy(np.arange(P * C)[None, :] <= pos[:, None])
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.3,
+                                                             enable_gqa=True)
+        (o * torch.from_numpy(do)).sum().backward()
+        for a, b in ((dq, tq.grad.numpy()), (dk, tk.grad.numpy()), (dv, tv.grad.numpy())):
+            if a.shape != b.shape or not np.allclose(a, b, atol=1e-11, rtol=0):
+                return f"autograd gqa rank={rank}"
+    return None
+
+
 def pin_bwd_fd(bwd):
     """Central finite differences of L = sum(dO * O) in fp64, tiny sizes."""
     P, C, d, h = 2, 3, 4, 1e-6
@@ -265,6 +303,29 @@ def pin_bwd_sums(bwd):
 
 def test_fwd_equals_library_sdpa():
     assert pin_sdpa(attention_fwd) is None
+
+
+def test_fwd_gqa_equals_library_sdpa():
+    assert pin_sdpa_gqa(attention_fwd) is None
+
+
+def test_bwd_gqa_equals_library_autograd():
+    assert pin_bwd_autograd_gqa(attention_bwd) is None
+
+
+def test_bwd_gqa_key_rows_match_full():
+    H, Hk, C, d = 4, 2, 20, 8
+    q, k, v = rnd(1, H, C, d, seed=90), rnd(1, Hk, C, d, seed=91), rnd(1, Hk, C, d, seed=92)
+    do = rnd(1, H, C, d, seed=93)
+    _, dk, dv = attention_bwd(q, k, v, do, 0.4, True)
+    rows = np.array([0, 7, 19])
+    dkr, dvr = attention_bwd_key_rows(q, k, v, do, 0.4, True, rows)
+    assert np.allclose(dkr, dk[:, :, rows], atol=1e-12) and np.allclose(dvr, dv[:, :, rows], atol=1e-12)
+
+
+def test_gqa_rejects_uneven_groups():
+    with pytest.raises(ValueError):
+        attention_fwd(rnd(1, 5, 4, 8), rnd(1, 2, 4, 8), rnd(1, 2, 4, 8), 0.5, False)
 
 
 def test_fwd_bruteforce_tiny():
@@ -460,7 +521,15 @@ def _fwd_mutants():
         kp = None if kp is None else np.asarray(kp)[:-1]
         return f(q, k[:, :, :-1], v[:, :, :-1], scale, causal, k_pos=kp, **kw)
 
-    return [no_scale, strict_mask, lse_log2, q_k_swapped, v_time_reversed, drop_last_key]
+    def gqa_interleaved(q, k, v, scale, causal, **kw):
+        """Query head h on key/value head h % Hk instead of h // (H / Hk)."""
+        H, Hk = q.shape[1], k.shape[1]
+        if Hk in (1, H):
+            return f(q, k, v, scale, causal, **kw)
+        idx = np.arange(H) % Hk
+        return f(q, k[:, idx], v[:, idx], scale, causal, **kw)
+
+    return [no_scale, strict_mask, lse_log2, q_k_swapped, v_time_reversed, drop_last_key, gqa_interleaved]
 
 
 def _merge_mutants():
@@ -505,20 +574,48 @@ def _bwd_mutants():
         dq, dk, dv = b(q, k, v, do, scale, causal, **kw)
         return dq, dv, dk
 
-    return [dq_unscaled, no_D_term, dk_dv_swapped]
+    def gqa_first_head_only(q, k, v, do, scale, causal, **kw):
+        """A key/value head's gradient from the first query head of its group
+        alone, not the group's sum."""
+        H, Hk = q.shape[1], k.shape[1]
+        if Hk == H:
+            return b(q, k, v, do, scale, causal, **kw)
+        grp = H // Hk
+        idx = np.arange(H) // grp
+        dq, dk_full, dv_full = b(q, k[:, idx], v[:, idx], do, scale, causal, **kw)
+        return dq, dk_full[:, ::grp], dv_full[:, ::grp]
+
+    return [dq_unscaled, no_D_term, dk_dv_swapped, gqa_first_head_only]
+
+
+def _run_pin(pin, *args):
+    """A pin's verdict on an altered oracle; a mutant that raises fails it."""
+    try:
+        return pin(*args)
+    except Exception as e:  # noqa: BLE001 -- any exception is a failed pin
+        return f"raised {type(e).__name__}"
 
 
 def test_mutants_fail_a_pin():
     for m in _fwd_mutants():
-        fails = [p(m) for p in (pin_sdpa, pin_bruteforce, pin_q_zero, pin_dominant_key, pin_v_constant)]
-        fails.append(pin_chunk_merge(m, lse_merge))
+        fails = [_run_pin(p, m) for p in (pin_sdpa, pin_sdpa_gqa, pin_bruteforce, pin_q_zero,
+                                          pin_dominant_key, pin_v_constant)]
+        fails.append(_run_pin(pin_chunk_merge, m, lse_merge))
         assert any(x is not None for x in fails), f"forward mutant {m.__name__} passed every pin"
     for m in _merge_mutants():
-        fails = [pin_chunk_merge(attention_fwd, m), pin_merge_order(attention_fwd, m)]
+        fails = [_run_pin(pin_chunk_merge, attention_fwd, m), _run_pin(pin_merge_order, attention_fwd, m)]
         assert any(x is not None for x in fails), f"merge mutant {m.__name__} passed every pin"
     for m in _bwd_mutants():
-        fails = [pin_bwd_autograd(m), pin_bwd_sums(m)]
+        fails = [_run_pin(p, m) for p in (pin_bwd_autograd, pin_bwd_autograd_gqa, pin_bwd_sums)]
         assert any(x is not None for x in fails), f"backward mutant {m.__name__} passed every pin"
+
+
+def test_gqa_mutants_fail_the_gqa_pins():
+    """The grouping mistakes are caught by the GQA pins specifically."""
+    fm = {m.__name__: m for m in _fwd_mutants()}
+    bm = {m.__name__: m for m in _bwd_mutants()}
+    assert _run_pin(pin_sdpa_gqa, fm["gqa_interleaved"]) is not None
+    assert _run_pin(pin_bwd_autograd_gqa, bm["gqa_first_head_only"]) is not None
 
 
 def test_oracle_header_marks_it_test_infrastructure():
