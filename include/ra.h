@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define RA_VERSION 1
+#define RA_VERSION 2
 
 enum ra_status {
   RA_OK = 0,
@@ -180,12 +180,54 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Grouped-query attention (GQA): key/value tensors carry H_kv heads for the
+ * H query heads, H_kv dividing H, and query head h reads key/value head
+ * h / (H / H_kv) (contiguous groups).  Ring attention's per-GPU work does not
+ * depend on the head count, which is its stated advantage over all-to-all
+ * sequence parallelism for GQA models ("Training Long-Context Models Without
+ * OOM: Ring Attention", "Ring Attention vs. DeepSpeed Ulysses (All-to-All)").
+ * Each *_gqa entry point is the call of the same name without the suffix,
+ * with H_kv inserted after H; the suffix-free calls are these with
+ * H_kv == H.  The differences:
+ *   - k, v, k_chunks[j], v_chunks[j] are [B,H_kv,*,d] bf16; q, dO, o, lse,
+ *     dq, o_partial, lse_partial keep H heads.
+ *   - dk_chunks[j], dv_chunks[j] are [B,H_kv,C,d] fp32 accumulators; each
+ *     key/value head's gradient sums over the query heads of its group.
+ *   - The double-buffer workspace holds H_kv-head chunks:
+ *     4 * B*H_kv*C*d * 2 bytes.  The backward workspace is unchanged
+ *     (2 * B*H*C * 4 bytes).
+ *   - H_kv < 1, or H not a multiple of H_kv, is RA_ERR_SHAPE (and 0 bytes
+ *     from ra_ring_workspace_bytes_gqa).  Every other contract (ownership,
+ *     validation before enqueueing, asynchrony, status codes) is as for the
+ *     suffix-free call.
+ */
+int ra_step_fwd_gqa(const void* q, const void* k, const void* v,
+                    float* o_partial, float* lse_partial,
+                    int B, int H, int H_kv, int Sq, int Sk, int d,
+                    float scale, int step, int causal, void* stream);
+size_t ra_ring_workspace_bytes_gqa(int P, int B, int H, int H_kv, int C,
+                                   int d, int ring_mode, int bwd);
+int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks,
+                    const void* const* v_chunks, int P, float* o, float* lse,
+                    int rank, int causal, float scale, int B, int H, int H_kv,
+                    int C, int d, int ring_mode, void* workspace,
+                    size_t workspace_bytes, void* stream, void* copy_stream);
+int ra_ring_bwd_gqa(const void* q, const void* const* k_chunks,
+                    const void* const* v_chunks, int P, const float* o,
+                    const float* lse, const void* dO, float* dq,
+                    float* const* dk_chunks, float* const* dv_chunks, int rank,
+                    int causal, float scale, int B, int H, int H_kv, int C,
+                    int d, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
  * Per-launch tracing, for profiling.  The pages define no such facility; it
  * exists so that a caller can time each kernel of a ring walk with its own
  * events, on the stream the kernel runs on.
  *
  * ra_trace_begin arms tracing on the calling thread.  Every kernel that
- * ra_step_fwd, ra_lse_merge, ra_ring_fwd or ra_ring_bwd then launch on their
+ * ra_step_fwd, ra_lse_merge, ra_ring_fwd or ra_ring_bwd (or their *_gqa
+ * forms) then launch on their
  * compute stream is bracketed by hipEventRecord(start_events[n], stream)
  * and hipEventRecord(end_events[n], stream), and kinds[n] receives its
  * RA_TRACE_* kind, for the n-th such launch while n < capacity (later

@@ -66,6 +66,14 @@ def lib():
         L.ra_ring_fwd.argtypes = [vp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, i, vp, sz, vp, vp]
         L.ra_ring_bwd.restype = i
         L.ra_ring_bwd.argtypes = [vp, vpp, vpp, i, vp, vp, vp, vp, vpp, vpp, i, i, f, i, i, i, i, vp, sz, vp]
+        L.ra_step_fwd_gqa.restype = i
+        L.ra_step_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        L.ra_ring_workspace_bytes_gqa.restype = sz
+        L.ra_ring_workspace_bytes_gqa.argtypes = [i, i, i, i, i, i, i, i]
+        L.ra_ring_fwd_gqa.restype = i
+        L.ra_ring_fwd_gqa.argtypes = [vp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, i, i, vp, sz, vp, vp]
+        L.ra_ring_bwd_gqa.restype = i
+        L.ra_ring_bwd_gqa.argtypes = [vp, vpp, vpp, i, vp, vp, vp, vp, vpp, vpp, i, i, f, i, i, i, i, i, vp, sz, vp]
         L.ra_trace_begin.restype = i
         L.ra_trace_begin.argtypes = [vpp, vpp, ctypes.POINTER(ctypes.c_int), i]
         L.ra_trace_end.restype = i
@@ -114,15 +122,20 @@ def version():
 
 
 def step_fwd(q, k, v, o_partial, lse_partial, step, causal, scale=None, stream=None):
-    """ra_step_fwd: one ring step's normalised partial and its lse."""
+    """ra_step_fwd: one ring step's normalised partial and its lse.  k and v
+    may carry fewer heads than q (grouped-query attention, ra_step_fwd_gqa)."""
     import torch
     _need(q, torch.bfloat16, "q"); _need(k, torch.bfloat16, "k"); _need(v, torch.bfloat16, "v")
     _need(o_partial, torch.float32, "o_partial"); _need(lse_partial, torch.float32, "lse_partial")
     B, H, Sq, d = q.shape
-    Sk = k.shape[2]
+    Hk, Sk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib().ra_step_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o_partial), _ptr(lse_partial),
-                             B, H, Sq, Sk, d, scale, int(step), int(bool(causal)), _stream(stream, q)))
+    args = (int(step), int(bool(causal)), _stream(stream, q))
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(o_partial), _ptr(lse_partial))
+    if Hk == H:
+        _check(lib().ra_step_fwd(*ptrs, B, H, Sq, Sk, d, scale, *args))
+    else:
+        _check(lib().ra_step_fwd_gqa(*ptrs, B, H, Hk, Sq, Sk, d, scale, *args))
 
 
 def lse_merge(o, lse, o_partial, lse_partial, stream=None):
@@ -137,13 +150,17 @@ def lse_merge(o, lse, o_partial, lse_partial, stream=None):
                               B, H, S, d, _stream(stream, o)))
 
 
-def workspace_bytes(P, B, H, C, d, ring_mode="double_buffer", bwd=False):
-    return int(lib().ra_ring_workspace_bytes(P, B, H, C, d, _MODES[ring_mode], int(bool(bwd))))
+def workspace_bytes(P, B, H, C, d, ring_mode="double_buffer", bwd=False, H_kv=None):
+    """ra_ring_workspace_bytes (ra_ring_workspace_bytes_gqa when H_kv differs from H)."""
+    if H_kv is None or H_kv == H:
+        return int(lib().ra_ring_workspace_bytes(P, B, H, C, d, _MODES[ring_mode], int(bool(bwd))))
+    return int(lib().ra_ring_workspace_bytes_gqa(P, B, H, H_kv, C, d, _MODES[ring_mode], int(bool(bwd))))
 
 
 def ring_fwd(q, k_chunks, v_chunks, o, lse, rank, causal, scale=None, ring_mode="double_buffer",
              workspace=None, stream=None, copy_stream=None):
-    """ra_ring_fwd: rank's whole ring walk; overwrites (o, lse).
+    """ra_ring_fwd: rank's whole ring walk; overwrites (o, lse).  The chunks
+    may carry fewer heads than q (grouped-query attention, ra_ring_fwd_gqa).
 
     workspace: a uint8 GPU tensor of at least workspace_bytes(...) bytes (only
     for ring_mode "double_buffer"); allocated here if not given.
@@ -155,24 +172,30 @@ def ring_fwd(q, k_chunks, v_chunks, o, lse, rank, causal, scale=None, ring_mode=
     for n, t in enumerate(list(k_chunks) + list(v_chunks)):
         _need(t, torch.bfloat16, f"chunk{n}")
     B, H, C, d = q.shape
+    Hk = k_chunks[0].shape[1]
     P = len(k_chunks)
     mode = _MODES[ring_mode]
-    need = workspace_bytes(P, B, H, C, d, mode, False)
+    need = workspace_bytes(P, B, H, C, d, mode, False, H_kv=Hk)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     ka, va = _ptr_array(k_chunks), _ptr_array(v_chunks)
     cs = None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
-    _check(lib().ra_ring_fwd(_ptr(q), ka, va, P, _ptr(o), _ptr(lse), int(rank), int(bool(causal)), scale,
-                             B, H, C, d, mode, _ptr(workspace),
-                             0 if workspace is None else workspace.numel() * workspace.element_size(),
-                             _stream(stream, q), cs))
+    head = (_ptr(q), ka, va, P, _ptr(o), _ptr(lse), int(rank), int(bool(causal)), scale, B, H)
+    tail = (C, d, mode, _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(stream, q), cs)
+    if Hk == H:
+        _check(lib().ra_ring_fwd(*head, *tail))
+    else:
+        _check(lib().ra_ring_fwd_gqa(*head, Hk, *tail))
     return workspace
 
 
 def ring_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, causal, scale=None,
              workspace=None, stream=None):
-    """ra_ring_bwd: rank's backward walk; dq overwritten, dk/dv chunks += ."""
+    """ra_ring_bwd: rank's backward walk; dq overwritten, dk/dv chunks += .
+    The chunks and their gradients may carry fewer heads than q (grouped-query
+    attention, ra_ring_bwd_gqa)."""
     import torch
     _need(q, torch.bfloat16, "q"); _need(dO, torch.bfloat16, "dO")
     _need(o, torch.float32, "o"); _need(lse, torch.float32, "lse"); _need(dq, torch.float32, "dq")
@@ -182,15 +205,19 @@ def ring_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, 
         if t is not None:
             _need(t, torch.float32, f"grad_chunk{n}")
     B, H, C, d = q.shape
+    Hk = k_chunks[0].shape[1]
     P = len(k_chunks)
-    need = workspace_bytes(P, B, H, C, d, "resident", True)
+    need = workspace_bytes(P, B, H, C, d, "resident", True, H_kv=Hk)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib().ra_ring_bwd(_ptr(q), _ptr_array(k_chunks), _ptr_array(v_chunks), P, _ptr(o), _ptr(lse),
-                             _ptr(dO), _ptr(dq), _ptr_array(dk_chunks), _ptr_array(dv_chunks), int(rank),
-                             int(bool(causal)), scale, B, H, C, d, _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(stream, q)))
+    head = (_ptr(q), _ptr_array(k_chunks), _ptr_array(v_chunks), P, _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+            _ptr_array(dk_chunks), _ptr_array(dv_chunks), int(rank), int(bool(causal)), scale, B, H)
+    tail = (C, d, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q))
+    if Hk == H:
+        _check(lib().ra_ring_bwd(*head, *tail))
+    else:
+        _check(lib().ra_ring_bwd_gqa(*head, Hk, *tail))
     return workspace
 
 

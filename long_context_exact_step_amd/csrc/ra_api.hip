@@ -41,6 +41,13 @@ int check_dims(int B, int H, int S, int d, const char* what) {
   return RA_OK;
 }
 
+// Grouped-query heads: H query heads over H_kv key/value heads, H_kv | H.
+int check_groups(int H, int H_kv, const char* what) {
+  if (H_kv < 1 || H % H_kv)
+    return fail(RA_ERR_SHAPE, "%s: H=%d query heads do not split evenly over H_kv=%d key/value heads", what, H, H_kv);
+  return RA_OK;
+}
+
 int hip_fail(hipError_t e, const char* what) {
   return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -162,12 +169,14 @@ const char* ra_status_string(int status) {
 
 const char* ra_last_error(void) { return g_err; }
 
-int ra_step_fwd(const void* q, const void* k, const void* v, float* o_partial, float* lse_partial, int B, int H,
-                int Sq, int Sk, int d, float scale, int step, int causal, void* stream) {
+int ra_step_fwd_gqa(const void* q, const void* k, const void* v, float* o_partial, float* lse_partial, int B,
+                    int H, int H_kv, int Sq, int Sk, int d, float scale, int step, int causal, void* stream) {
   if (!q || !k || !v || !o_partial || !lse_partial) return fail(RA_ERR_NULL, "ra_step_fwd: NULL pointer");
   int st = check_dims(B, H, Sq, d, "ra_step_fwd(q)");
   if (st) return st;
-  st = check_dims(B, H, Sk, d, "ra_step_fwd(k)");
+  st = check_dims(B, H_kv, Sk, d, "ra_step_fwd(k)");
+  if (st) return st;
+  st = check_groups(H, H_kv, "ra_step_fwd");
   if (st) return st;
   if (step < 0) return fail(RA_ERR_SHAPE, "ra_step_fwd: step=%d < 0", step);
   const bool diag = causal != 0 && step == 0;
@@ -175,10 +184,16 @@ int ra_step_fwd(const void* q, const void* k, const void* v, float* o_partial, f
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_partial) || !aligned16(lse_partial))
     return fail(RA_ERR_ALIGN, "ra_step_fwd: device pointers must be 16-byte aligned");
   ra::FwdStepArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                    static_cast<const uint16_t*>(v), o_partial, lse_partial, B * H, Sq, Sk, d, scale, diag, false};
+                    static_cast<const uint16_t*>(v), o_partial, lse_partial, B * H, Sq, Sk, d, scale, diag, false,
+                    H / H_kv};
   const hipError_t e = fwd_step(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ra_step_fwd launch");
   return ok();
+}
+
+int ra_step_fwd(const void* q, const void* k, const void* v, float* o_partial, float* lse_partial, int B, int H,
+                int Sq, int Sk, int d, float scale, int step, int causal, void* stream) {
+  return ra_step_fwd_gqa(q, k, v, o_partial, lse_partial, B, H, H, Sq, Sk, d, scale, step, causal, stream);
 }
 
 int ra_lse_merge(float* o, float* lse, const float* o_partial, const float* lse_partial, int B, int H, int S, int d,
@@ -197,20 +212,26 @@ int ra_lse_merge(float* o, float* lse, const float* o_partial, const float* lse_
   return ok();
 }
 
-size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d, int ring_mode, int bwd) {
-  if (P < 1 || B < 1 || H < 1 || C < 1 || (d != 64 && d != 128)) return 0;
-  const size_t elems = (size_t)B * H * C * d;
-  if (bwd) return 2 * (size_t)B * H * C * sizeof(float);  // D and lse2 per row
-  if (ring_mode == RA_RING_DOUBLE_BUFFER) return 4 * elems * 2;  // 2 slots x (K, V) bf16
+size_t ra_ring_workspace_bytes_gqa(int P, int B, int H, int H_kv, int C, int d, int ring_mode, int bwd) {
+  if (P < 1 || B < 1 || H < 1 || H_kv < 1 || H % H_kv || C < 1 || (d != 64 && d != 128)) return 0;
+  const size_t kv_elems = (size_t)B * H_kv * C * d;
+  if (bwd) return 2 * (size_t)B * H * C * sizeof(float);  // D and lse2 per query row
+  if (ring_mode == RA_RING_DOUBLE_BUFFER) return 4 * kv_elems * 2;  // 2 slots x (K, V) bf16
   return 0;
 }
 
-int ra_ring_fwd(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, float* o, float* lse,
-                int rank, int causal, float scale, int B, int H, int C, int d, int ring_mode, void* workspace,
-                size_t workspace_bytes, void* stream, void* copy_stream) {
+size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d, int ring_mode, int bwd) {
+  return ra_ring_workspace_bytes_gqa(P, B, H, H, C, d, ring_mode, bwd);
+}
+
+int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, float* o,
+                    float* lse, int rank, int causal, float scale, int B, int H, int H_kv, int C, int d,
+                    int ring_mode, void* workspace, size_t workspace_bytes, void* stream, void* copy_stream) {
   if (!q || !k_chunks || !v_chunks || !o || !lse) return fail(RA_ERR_NULL, "ra_ring_fwd: NULL pointer");
   if (P < 1) return fail(RA_ERR_SHAPE, "ra_ring_fwd: P=%d < 1", P);
   int st = check_dims(B, H, C, d, "ra_ring_fwd");
+  if (st) return st;
+  st = check_groups(H, H_kv, "ra_ring_fwd");
   if (st) return st;
   if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "ra_ring_fwd: rank=%d outside [0, %d)", rank, P);
   if (ring_mode != RA_RING_RESIDENT && ring_mode != RA_RING_DOUBLE_BUFFER)
@@ -222,7 +243,7 @@ int ra_ring_fwd(const void* q, const void* const* k_chunks, const void* const* v
   }
   if (!aligned16(q) || !aligned16(o) || !aligned16(lse))
     return fail(RA_ERR_ALIGN, "ra_ring_fwd: device pointers must be 16-byte aligned");
-  const size_t need = ra_ring_workspace_bytes(P, B, H, C, d, ring_mode, 0);
+  const size_t need = ra_ring_workspace_bytes_gqa(P, B, H, H_kv, C, d, ring_mode, 0);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(RA_ERR_WORKSPACE, "ra_ring_fwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
                 need);
@@ -231,11 +252,11 @@ int ra_ring_fwd(const void* q, const void* const* k_chunks, const void* const* v
   hipStream_t cs = static_cast<hipStream_t>(stream);
   hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
   const std::vector<Step> steps = visible_steps(rank, P, causal != 0);
-  const size_t chunk_bytes = (size_t)B * H * C * d * 2;
+  const size_t chunk_bytes = (size_t)B * H_kv * C * d * 2;
   const uint16_t* qh = static_cast<const uint16_t*>(q);
   auto step_args = [&](const void* kp, const void* vp, bool diag, bool merge) {
     return ra::FwdStepArgs{qh, static_cast<const uint16_t*>(kp), static_cast<const uint16_t*>(vp), o, lse, B * H,
-                           C, C, d, scale, diag, merge};
+                           C, C, d, scale, diag, merge, H / H_kv};
   };
 
   if (ring_mode == RA_RING_RESIDENT) {
@@ -296,14 +317,23 @@ int ra_ring_fwd(const void* q, const void* const* k_chunks, const void* const* v
   return ok();
 }
 
-int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,
-                const float* lse, const void* dO, float* dq, float* const* dk_chunks, float* const* dv_chunks,
-                int rank, int causal, float scale, int B, int H, int C, int d, void* workspace,
-                size_t workspace_bytes, void* stream) {
+int ra_ring_fwd(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, float* o, float* lse,
+                int rank, int causal, float scale, int B, int H, int C, int d, int ring_mode, void* workspace,
+                size_t workspace_bytes, void* stream, void* copy_stream) {
+  return ra_ring_fwd_gqa(q, k_chunks, v_chunks, P, o, lse, rank, causal, scale, B, H, H, C, d, ring_mode, workspace,
+                         workspace_bytes, stream, copy_stream);
+}
+
+int ra_ring_bwd_gqa(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,
+                    const float* lse, const void* dO, float* dq, float* const* dk_chunks, float* const* dv_chunks,
+                    int rank, int causal, float scale, int B, int H, int H_kv, int C, int d, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   if (!q || !k_chunks || !v_chunks || !o || !lse || !dO || !dq || !dk_chunks || !dv_chunks)
     return fail(RA_ERR_NULL, "ra_ring_bwd: NULL pointer");
   if (P < 1) return fail(RA_ERR_SHAPE, "ra_ring_bwd: P=%d < 1", P);
   int st = check_dims(B, H, C, d, "ra_ring_bwd");
+  if (st) return st;
+  st = check_groups(H, H_kv, "ra_ring_bwd");
   if (st) return st;
   if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "ra_ring_bwd: rank=%d outside [0, %d)", rank, P);
   const std::vector<Step> steps = visible_steps(rank, P, causal != 0);
@@ -316,7 +346,7 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v
   }
   if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || !aligned16(dO) || !aligned16(dq))
     return fail(RA_ERR_ALIGN, "ra_ring_bwd: device pointers must be 16-byte aligned");
-  const size_t need = ra_ring_workspace_bytes(P, B, H, C, d, 0, 1);
+  const size_t need = ra_ring_workspace_bytes_gqa(P, B, H, H_kv, C, d, 0, 1);
   if (!workspace || workspace_bytes < need)
     return fail(RA_ERR_WORKSPACE, "ra_ring_bwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
                 need);
@@ -334,7 +364,7 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v
   for (const Step& sp : steps) {
     ra::BwdStepArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_chunks[sp.j]),
                       static_cast<const uint16_t*>(v_chunks[sp.j]), static_cast<const uint16_t*>(dO), lse2, Dbuf, dq,
-                      dk_chunks[sp.j], dv_chunks[sp.j], B * H, C, C, d, scale, sp.diag};
+                      dk_chunks[sp.j], dv_chunks[sp.j], B * H, C, C, d, scale, sp.diag, H / H_kv};
     e = traced(sp.diag ? RA_TRACE_BWD_DQ_DIAG : RA_TRACE_BWD_DQ_FULL, cs, [&] { return ra::launch_bwd_dq(a, cs); });
     if (e == hipSuccess)
       e = traced(sp.diag ? RA_TRACE_BWD_DKDV_DIAG : RA_TRACE_BWD_DKDV_FULL, cs,
@@ -342,6 +372,14 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v
     if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd step");
   }
   return ok();
+}
+
+int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,
+                const float* lse, const void* dO, float* dq, float* const* dk_chunks, float* const* dv_chunks,
+                int rank, int causal, float scale, int B, int H, int C, int d, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return ra_ring_bwd_gqa(q, k_chunks, v_chunks, P, o, lse, dO, dq, dk_chunks, dv_chunks, rank, causal, scale, B, H,
+                         H, C, d, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -55,7 +55,8 @@ template <int D, bool DIAG>
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lse2g, const float* __restrict__ Dg,
-    float* __restrict__ dqg, int Sq, int Sk, int n_qtiles, int total_tiles, float scale_log2, float scale) {
+    float* __restrict__ dqg, int Sq, int Sk, int n_qtiles, int total_tiles, float scale_log2, float scale,
+    int group) {
   constexpr int NW = kDqWaves, NQW = kDqRowsPerWave, BR = NW * NQW, BC = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kDqLookahead;
   constexpr int NQ = 4 * NDB, NS = 2 * NKS * NKB, NOP = NQ + NS;  // dq ops, then S and dP ops
@@ -79,8 +80,9 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * NQW;
   const int qq = qw0 + l32;
-  const uint16_t* __restrict__ kp = kg + (size_t)bh * Sk * D;
-  const uint16_t* __restrict__ vp = vg + (size_t)bh * Sk * D;
+  // Grouped-query attention: query head row bh reads key/value head bh / group.
+  const uint16_t* __restrict__ kp = kg + (size_t)(bh / group) * Sk * D;
+  const uint16_t* __restrict__ vp = vg + (size_t)(bh / group) * Sk * D;
 
   int kend = Sk;
   if (DIAG) kend = min(kend, q0 + BR);
@@ -306,7 +308,8 @@ template <int D, bool DIAG, bool DK>
 __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lse2g, const float* __restrict__ Dg,
-    float* __restrict__ outg, int Sq, int Sk, int n_ktiles, int total_tiles, float scale_log2, float scale) {
+    float* __restrict__ outg, int Sq, int Sk, int n_ktiles, int total_tiles, float scale_log2, float scale,
+    int group) {
   constexpr int NW = kKvWaves, NKW = kKvKeysPerWave, BK = NW * NKW, BQ = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NQB = BQ / 32, TILE = BQ * D * 2, LA = kKvLookahead;
   constexpr int NX = 4 * NDB, NS = (DK ? 2 : 1) * NKS * NQB, NOP = NX + NS;
@@ -322,15 +325,16 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   const int l32 = lane & 31, g = lane >> 5;
   const bool lead = wave < NW / 2;  // waves 4..7 run one phase behind
   const int t = xcd_remap(blockIdx.x, total_tiles);
-  const int bh = t / n_ktiles;
-  const int kt = t - bh * n_ktiles;  // low key tiles see the most queries: they go first
+  const int bhk = t / n_ktiles;  // key/value head row; its query heads are bhk * group + [0, group)
+  const int kt = t - bhk * n_ktiles;  // low key tiles see the most queries: they go first
   const int kb0 = kt * BK;
   const int kw0 = kb0 + wave * NKW;
   const int kk = kw0 + l32;
-  const uint16_t* __restrict__ qp = qg + (size_t)bh * Sq * D;
-  const uint16_t* __restrict__ dp = dog + (size_t)bh * Sq * D;
-  const float* __restrict__ lp = lse2g + (size_t)bh * Sq;
-  const float* __restrict__ Dp = Dg + (size_t)bh * Sq;
+  // Query-side rows of the query head being walked (set per head below).
+  const uint16_t* __restrict__ qp = qg;
+  const uint16_t* __restrict__ dp = dog;
+  const float* __restrict__ lp = lse2g;
+  const float* __restrict__ Dp = Dg;
 
   // Query tiles qs .. ntq-1; this wave's keys see tiles from ws on (causal:
   // query q sees keys <= q).
@@ -363,17 +367,11 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     else if (k < 2 * NPW) dma.load_piece(k - NPW, dbuf(j & 3), dp, j * BQ, Sq);
     else load_rows(j);
   };
-  if (qs < ntq) {
-    load_tile(qs);
-    if (qs + 1 < ntq) load_tile(qs + 1);
-    // Finite data for the Y = 0 product of the first tile.
-    dma.load(DK ? qbuf((qs + 3) & 3) : dbuf((qs + 3) & 3), DK ? qp : dp, qs * BQ, Sq);
-  }
 
   u32x4 kf[NKS], vf[DK ? NKS : 1];
   {
-    const uint16_t* krow = kg + ((size_t)bh * Sk + kk) * D;
-    const uint16_t* vrow = vg + ((size_t)bh * Sk + kk) * D;
+    const uint16_t* krow = kg + ((size_t)bhk * Sk + kk) * D;
+    const uint16_t* vrow = vg + ((size_t)bhk * Sk + kk) * D;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       kf[s] = (kk < Sk) ? ld16(krow + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
@@ -387,8 +385,6 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   f32x16 sacc[NQB], pacc[DK ? NQB : 1];
   u32x4 yb[NQB][2];  // P or dS of the last vector phase, bf16 (B operand of the product)
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) yb[qb][0] = yb[qb][1] = u32x4{0, 0, 0, 0};
 
   const uint32_t base = lds_addr(smem);
   uint32_t raddr[NKS];  // row-major operand (Q or dO) of row l32, chunk pair s
@@ -537,24 +533,44 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   auto vector_tile = [&](int tt) __attribute__((always_inline)) {
     if (tt >= ws && tt < ntq) vector_phase(tt);
   };
-  // Iteration u: MFMA phase of tile u (reads Q(u), dO(u) and X(u-1)), vector
-  // phase of tile u.  The MFMA phase loads tile u + 2 into buffers whose last
-  // readers (tiles u - 2 and u - 1's products) finished two phases back for
-  // either wave group; the iteration ends waiting for that load.
-  wait_vmem();
-  phase_barrier();
-  if (!lead) phase_barrier();
-  for (int u = qs; u <= ntq; ++u) {
-    mfma_tile(u);
-    phase_barrier();
-    vector_tile(u);
+  // Grouped-query attention: the block's keys serve `group` query heads, walked
+  // one after the other into the same accumulators (dk, dv sum over them).
+  // The last barrier of a head's walk comes after every wave's last LDS read
+  // of it, so the next head's first loads may reuse any buffer.
+  for (int gh = 0; gh < group; ++gh) {
+    const int bh = bhk * group + gh;
+    qp = qg + (size_t)bh * Sq * D;
+    dp = dog + (size_t)bh * Sq * D;
+    lp = lse2g + (size_t)bh * Sq;
+    Dp = Dg + (size_t)bh * Sq;
+    if (qs < ntq) {
+      load_tile(qs);
+      if (qs + 1 < ntq) load_tile(qs + 1);
+      // Finite data for the Y = 0 product of the first tile.
+      dma.load(DK ? qbuf((qs + 3) & 3) : dbuf((qs + 3) & 3), DK ? qp : dp, qs * BQ, Sq);
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) yb[qb][0] = yb[qb][1] = u32x4{0, 0, 0, 0};
+    // Iteration u: MFMA phase of tile u (reads Q(u), dO(u) and X(u-1)),
+    // vector phase of tile u.  The MFMA phase loads tile u + 2 into buffers
+    // whose last readers (tiles u - 2 and u - 1's products) finished two
+    // phases back for either wave group; the iteration ends waiting for that
+    // load.
     wait_vmem();
     phase_barrier();
+    if (!lead) phase_barrier();
+    for (int u = qs; u <= ntq; ++u) {
+      mfma_tile(u);
+      phase_barrier();
+      vector_tile(u);
+      wait_vmem();
+      phase_barrier();
+    }
+    if (lead) phase_barrier();
   }
-  if (lead) phase_barrier();
 
   if (kk < Sk) {
-    float* row = outg + ((size_t)bh * Sk + kk) * D;
+    float* row = outg + ((size_t)bhk * Sk + kk) * D;
     const float f = DK ? scale : 1.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -572,16 +588,17 @@ template <int D>
 hipError_t launch_dq_d(const BwdStepArgs& a, hipStream_t stream) {
   constexpr int BR = kDqWaves * kDqRowsPerWave;
   const int nq = (a.Sq + BR - 1) / BR;
+  if (a.group < 1 || a.BH % a.group) return hipErrorInvalidValue;
   const long long total = (long long)nq * a.BH;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   if (total == 0) return hipSuccess;
   const float sl2 = a.scale * kLog2e;
   if (a.diag)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(64 * kDqWaves), 0, stream, a.q, a.k,
-                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
+                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale, a.group);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(64 * kDqWaves), 0, stream, a.q, a.k,
-                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale);
+                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale, a.group);
   return hipGetLastError();
 }
 
@@ -589,14 +606,15 @@ template <int D>
 hipError_t launch_dkdv_d(const BwdStepArgs& a, hipStream_t stream) {
   constexpr int BK = kKvWaves * kKvKeysPerWave;
   const int nk = (a.Sk + BK - 1) / BK;
-  const long long total = (long long)nk * a.BH;
+  if (a.group < 1 || a.BH % a.group) return hipErrorInvalidValue;
+  const long long total = (long long)nk * (a.BH / a.group);  // blocks per key/value head
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   if (total == 0) return hipSuccess;
   const float sl2 = a.scale * kLog2e;
   const dim3 grid((unsigned)total), block(64 * kKvWaves);
 #define RA_KV_LAUNCH(DIAG, DK, OUT)                                                                               \
   hipLaunchKernelGGL((bwd_kv_kernel<D, DIAG, DK>), grid, block, 0, stream, a.q, a.k, a.v, a.dO, a.lse2, a.D, OUT, \
-                     a.Sq, a.Sk, nk, (int)total, sl2, a.scale)
+                     a.Sq, a.Sk, nk, (int)total, sl2, a.scale, a.group)
   if (a.diag) {
     RA_KV_LAUNCH(true, false, a.dv);
     RA_KV_LAUNCH(true, true, a.dk);

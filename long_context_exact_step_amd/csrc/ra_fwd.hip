@@ -132,7 +132,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
                                                                   float* __restrict__ og,
                                                                   float* __restrict__ lseg, int Sq, int Sk,
                                                                   int n_qtiles, int total_tiles,
-                                                                  float scale_log2) {
+                                                                  float scale_log2, int group) {
   constexpr int NW = kFwdWaves, NQW = kFwdRowsPerWave, BR = NW * NQW, BC = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kFwdLookahead;
   constexpr int NB = kFwdBuffers;
@@ -164,8 +164,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   const int qw0 = q0 + wave * NQW;
   const int qq = qw0 + l32;
   const uint16_t* __restrict__ qp = qg + (size_t)bh * Sq * D;
-  const uint16_t* __restrict__ kp = kg + (size_t)bh * Sk * D;
-  const uint16_t* __restrict__ vp = vg + (size_t)bh * Sk * D;
+  // Grouped-query attention: query head row bh reads key/value head bh / group.
+  const uint16_t* __restrict__ kp = kg + (size_t)(bh / group) * Sk * D;
+  const uint16_t* __restrict__ vp = vg + (size_t)(bh / group) * Sk * D;
 
   int kend = Sk;
   if (DIAG) kend = min(kend, q0 + BR);
@@ -427,6 +428,7 @@ template <int D>
 hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
   constexpr int BR = kFwdWaves * kFwdRowsPerWave;
   const int n_qtiles = (a.Sq + BR - 1) / BR;
+  if (a.group < 1 || a.BH % a.group) return hipErrorInvalidValue;
   const long long total = (long long)n_qtiles * a.BH;
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -434,7 +436,7 @@ hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)total), block(64 * kFwdWaves);
 #define RA_FWD_LAUNCH(DIAG, MERGE)                                                                         \
   hipLaunchKernelGGL((fwd_step_kernel<D, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, a.v, a.o, \
-                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2)
+                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group)
   if (a.diag) {
     if (a.merge) RA_FWD_LAUNCH(true, true);
     else RA_FWD_LAUNCH(true, false);

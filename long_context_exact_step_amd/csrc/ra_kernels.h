@@ -7,8 +7,10 @@
 namespace ra {
 
 // One ring step, forward: query block [BH, Sq, d] against one KV chunk
-// [BH, Sk, d] (bf16), written into (o, lse) fp32 -- overwritten when
-// merge == false, folded into the running values when merge == true.
+// [BH / group, Sk, d] (bf16), written into (o, lse) fp32 -- overwritten when
+// merge == false, folded into the running values when merge == true.  Query
+// head row bh reads key/value head bh / group (grouped-query attention with
+// `group` query heads per key/value head; 1 = multi-head).
 struct FwdStepArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -19,6 +21,7 @@ struct FwdStepArgs {
   float scale;
   bool diag;   // diagonal mask: local query t sees local keys <= t (Sq == Sk)
   bool merge;  // fold into the running (o, lse) instead of overwriting
+  int group;   // query heads per key/value head (>= 1, divides BH)
 };
 hipError_t launch_fwd_step(const FwdStepArgs& a, hipStream_t stream);
 
@@ -32,7 +35,8 @@ hipError_t launch_bwd_rowdot(const uint16_t* dO, const float* o, const float* ls
                              int rows, int d, hipStream_t stream);
 
 // Backward of one ring step against one KV chunk.  Uses the final lse (in
-// base 2) and D.
+// base 2) and D.  Query head row bh reads key/value head bh / group; dk, dv
+// ([BH / group, Sk, d]) sum over the group's query heads.
 struct BwdStepArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -46,6 +50,7 @@ struct BwdStepArgs {
   int BH, Sq, Sk, d;
   float scale;
   bool diag;
+  int group;  // query heads per key/value head (>= 1, divides BH)
 };
 hipError_t launch_bwd_dq(const BwdStepArgs& a, hipStream_t stream);    // dq += ...
 hipError_t launch_bwd_dkdv(const BwdStepArgs& a, hipStream_t stream);  // dk, dv += ...

@@ -25,12 +25,14 @@ def gen(wid, kind, j, B, H, C, d):
     return inputs.chunk(wid, kind, j, B, H, C, d)
 
 
-def ring_tensors(wid, B, H, P, C, d, with_do=False, ranks=None):
-    """CPU bf16 chunks: q_chunks[r], k_chunks[j], v_chunks[j] (and dO)."""
+def ring_tensors(wid, B, H, P, C, d, with_do=False, ranks=None, H_kv=None):
+    """CPU bf16 chunks: q_chunks[r], k_chunks[j], v_chunks[j] (and dO).  The
+    key/value chunks carry H_kv heads (default H)."""
     ranks = range(P) if ranks is None else ranks
+    Hk = H if H_kv is None else H_kv
     q = {r: gen(wid, inputs.Q, r, B, H, C, d) for r in ranks}
-    k = [gen(wid, inputs.K, j, B, H, C, d) for j in range(P)]
-    v = [gen(wid, inputs.V, j, B, H, C, d) for j in range(P)]
+    k = [gen(wid, inputs.K, j, B, Hk, C, d) for j in range(P)]
+    v = [gen(wid, inputs.V, j, B, Hk, C, d) for j in range(P)]
     do = {r: gen(wid, inputs.DO, r, B, H, C, d) for r in ranks} if with_do else None
     return q, k, v, do
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ra_version() == 1
+    assert L.ra_version() == 2  # 2: grouped-query (*_gqa) entry points
     assert L.ra_status_string(RA_OK) == b"RA_OK"
     assert L.ra_status_string(RA_ERR_WORKSPACE) == b"RA_ERR_WORKSPACE"
     assert L.ra_status_string(12345) == b"RA_ERR_UNKNOWN"
@@ -117,6 +117,31 @@ def test_workspace_sizes(L):
     assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 0, 0) == 0
     assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 128, 0, 1) == 2 * 32 * 16384 * 4
     assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 96, 0, 1) == 0
+
+
+def test_gqa_workspace_sizes(L):
+    # Double buffer holds H_kv-head chunks; the backward's per-row values keep H heads.
+    assert L.ra_ring_workspace_bytes_gqa(4, 1, 32, 8, 32768, 128, 1, 0) == 2 * 2 * 8 * 32768 * 128 * 2
+    assert L.ra_ring_workspace_bytes_gqa(4, 1, 32, 8, 16384, 128, 0, 1) == 2 * 32 * 16384 * 4
+    assert L.ra_ring_workspace_bytes_gqa(4, 1, 32, 32, 32768, 128, 1, 0) == L.ra_ring_workspace_bytes(
+        4, 1, 32, 32768, 128, 1, 0)
+    assert L.ra_ring_workspace_bytes_gqa(4, 1, 32, 5, 32768, 128, 1, 0) == 0  # 5 does not divide 32
+    assert L.ra_ring_workspace_bytes_gqa(4, 1, 32, 0, 32768, 128, 1, 0) == 0
+
+
+def test_gqa_validation(L):
+    P, C, d = 4, 64, 128
+    arr = (ctypes.c_void_p * P)(*([FAKE] * P))
+    for H, Hk in ((6, 4), (4, 0), (3, 6)):
+        assert L.ra_step_fwd_gqa(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, H, Hk, 64, 64, d, 0.1,
+                                 1, 1, None) == RA_ERR_SHAPE
+        assert L.ra_ring_fwd_gqa(vp(FAKE), arr, arr, P, vp(FAKE), vp(FAKE), 3, 1, 0.1, 1, H, Hk, C, d, 0,
+                                 None, 0, None, None) == RA_ERR_SHAPE
+        assert L.ra_ring_bwd_gqa(vp(FAKE), arr, arr, P, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), arr, arr, 3, 1,
+                                 0.1, 1, H, Hk, C, d, vp(FAKE), 1 << 20, None) == RA_ERR_SHAPE
+    # A valid grouping gets past the head check to the next one (here: the rank).
+    assert L.ra_ring_fwd_gqa(vp(FAKE), arr, arr, P, vp(FAKE), vp(FAKE), 9, 1, 0.1, 1, 8, 2, C, d, 0,
+                             None, 0, None, None) == RA_ERR_RANK
 
 
 def test_python_binding_rejects_cpu_tensors():

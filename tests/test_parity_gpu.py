@@ -221,3 +221,69 @@ def test_repeat_runs_bit_identical():
         outs.append([t.cpu() for t in [dq, *dk, *dv]])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query attention: key/value chunks with fewer heads than the queries.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,Hk,Sq,Sk,d,diag", [
+    (4, 2, 100, 100, 128, True), (6, 3, 293, 517, 64, False), (4, 1, 300, 300, 128, True),
+])
+def test_step_fwd_gqa_matches_oracle(H, Hk, Sq, Sk, d, diag):
+    print(f"step_fwd gqa H={H} Hk={Hk} Sq={Sq} Sk={Sk} d={d} diag={diag}", flush=True)
+    q = gen(108, inputs.Q, 0, 1, H, Sq, d)
+    k = gen(108, inputs.K, 0, 1, Hk, Sk, d)
+    v = gen(108, inputs.V, 0, 1, Hk, Sk, d)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_step(q, k, v, 0 if diag else 2, diag, scale)
+    ro, rl = oracle.step_partial(f64(q), f64(k), f64(v), scale, diagonal=diag)
+    assert_close(f64(o), ro, TOL_O, "o_partial")
+    assert_close(f64(lse), rl, TOL_LSE, "lse_partial", rel=None)
+
+
+@pytest.mark.parametrize("mode", ["resident", "double_buffer"])
+def test_ring_fwd_gqa_every_rank(mode):
+    P, C, d, H, Hk = 3, 300, 128, 4, 2
+    q, k, v, _ = ring_tensors(109, 1, H, P, C, d, H_kv=Hk)
+    kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
+    scale = 1 / math.sqrt(d)
+    kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
+    for rank in range(P):
+        print(f"ring_fwd gqa mode={mode} rank={rank}", flush=True)
+        o = torch.full((1, H, C, d), float("nan"), device=dev())
+        lse = torch.full((1, H, C), float("nan"), device=dev())
+        ra.ring_fwd(q[rank].to(dev()), kd, vd, o, lse, rank, True, scale, ring_mode=mode)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attention_fwd(f64(q[rank]), kf, vf, scale, True, q_pos=rank * C + np.arange(C))
+        assert_close(f64(o), ro, TOL_O, f"o rank {rank}")
+        assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)
+
+
+@pytest.mark.parametrize("P,C,d,H,Hk", [(2, 300, 128, 4, 2), (3, 100, 64, 6, 3), (2, 130, 128, 4, 1)])
+def test_ring_bwd_gqa_matches_oracle(P, C, d, H, Hk):
+    q, k, v, do = ring_tensors(110, 1, H, P, C, d, with_do=True, H_kv=Hk)
+    kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
+    scale = 1 / math.sqrt(d)
+    kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
+    for rank in range(P):
+        print(f"ring_bwd gqa P={P} C={C} d={d} H={H} Hk={Hk} rank={rank}", flush=True)
+        qd = q[rank].to(dev())
+        o = torch.empty(1, H, C, d, device=dev())
+        lse = torch.empty(1, H, C, device=dev())
+        ra.ring_fwd(qd, kd, vd, o, lse, rank, True, scale, ring_mode="resident")
+        dq = torch.full((1, H, C, d), float("nan"), device=dev())
+        dk = [torch.zeros(1, Hk, C, d, device=dev()) for _ in range(P)]
+        dv = [torch.zeros(1, Hk, C, d, device=dev()) for _ in range(P)]
+        ra.ring_bwd(qd, kd, vd, o, lse, do[rank].to(dev()), dq, dk, dv, rank, True, scale)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.attention_bwd(f64(q[rank]), kf, vf, f64(do[rank]), scale, True,
+                                          q_pos=rank * C + np.arange(C))
+        assert_close(f64(dq), rq, TOL_GRAD, "dq")
+        for j in range(P):
+            if j > rank:
+                assert not dk[j].any() and not dv[j].any(), "skipped chunk was touched"
+                continue
+            sl = slice(j * C, (j + 1) * C)
+            assert_close(f64(dk[j]), rk[:, :, sl], TOL_GRAD, f"dk chunk {j}")
+            assert_close(f64(dv[j]), rv[:, :, sl], TOL_GRAD, f"dv chunk {j}")
