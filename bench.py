@@ -10,13 +10,15 @@ seeded synthetic bf16 N(0,1) tensors resident in HBM before timing starts.
 
 Also reported (unless --no-train): the training share (C = 16384, P = 4,
 rank 3, H = 32, d = 128, causal), one step = forward walk + backward walk.
+And (unless --no-gqa): both walks again with grouped-query key/value chunks of
+H/4 heads (4 query heads per key/value head), under "gqa".
 
 Prints ONE JSON line: throughput in algorithmic TFLOP/s (4*d flops per
 visible (query, key) pair forward, 10*d backward), tokens/s, the roofline of
 the dominant kernel timed live with HIP events on its own stream, and the
 fp64 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-train] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-train] [--no-cpu] [--no-gqa]
 """
 
 import argparse
@@ -123,7 +125,9 @@ def kernel_stats(rec, w, kind_flops):
     return out
 
 
-def run_fwd(w, steps, warmup, ring_mode):
+def run_fwd(w, steps, warmup, ring_mode, H_kv=None):
+    """The forward walk of workload w; H_kv < H runs it with grouped-query
+    key/value chunks of H_kv heads."""
     import torch
     import long_context_exact_step_amd as ra
     from long_context_exact_step_amd import inputs
@@ -131,12 +135,14 @@ def run_fwd(w, steps, warmup, ring_mode):
 
     dev = torch.device("cuda", 0)
     B, H, C, d, P = w.B, w.H, w.C, w.d, w.P
+    Hk = H if H_kv is None else H_kv
     qs = {r: inputs.chunk(w.id, inputs.Q, r, B, H, C, d).to(dev) for r in w.ranks}
-    ks = [inputs.chunk(w.id, inputs.K, j, B, H, C, d).to(dev) for j in range(P)]
-    vs = [inputs.chunk(w.id, inputs.V, j, B, H, C, d).to(dev) for j in range(P)]
+    ks = [inputs.chunk(w.id, inputs.K, j, B, Hk, C, d).to(dev) for j in range(P)]
+    vs = [inputs.chunk(w.id, inputs.V, j, B, Hk, C, d).to(dev) for j in range(P)]
     o = {r: torch.empty(B, H, C, d, device=dev) for r in w.ranks}
     lse = {r: torch.empty(B, H, C, device=dev) for r in w.ranks}
-    ws = torch.empty(max(1, ra.workspace_bytes(P, B, H, C, d, ring_mode)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, ra.workspace_bytes(P, B, H, C, d, ring_mode, H_kv=Hk)), dtype=torch.uint8,
+                     device=dev)
     copy_stream = torch.cuda.Stream(dev) if ring_mode == "double_buffer" else None
     n_launch = sum(sum(k != "skip" for *_, k in step_kinds(r, P, w.causal)) for r in w.ranks)
 
@@ -152,12 +158,15 @@ def run_fwd(w, steps, warmup, ring_mode):
         "tflops": flops * steps / secs / 1e12,
         "tokens_per_s": B * C * len(w.ranks) * steps / secs,
         "kernels": kernel_stats(rec, w, lambda k: 4 * d),
+        "kv_bytes_per_ring_step": 2 * B * Hk * C * d * 2,
         "rec": rec,
     }
     return res, (qs, ks, vs, o, lse)
 
 
-def run_train(w, steps, warmup):
+def run_train(w, steps, warmup, H_kv=None):
+    """Forward + backward walk of workload w; H_kv < H runs it with
+    grouped-query key/value chunks of H_kv heads."""
     import torch
     import long_context_exact_step_amd as ra
     from long_context_exact_step_amd import inputs
@@ -165,18 +174,21 @@ def run_train(w, steps, warmup):
 
     dev = torch.device("cuda", 0)
     B, H, C, d, P = w.B, w.H, w.C, w.d, w.P
+    Hk = H if H_kv is None else H_kv
     r = w.ranks[0]
     q = inputs.chunk(w.id, inputs.Q, r, B, H, C, d).to(dev)
     do = inputs.chunk(w.id, inputs.DO, r, B, H, C, d).to(dev)
-    ks = [inputs.chunk(w.id, inputs.K, j, B, H, C, d).to(dev) for j in range(P)]
-    vs = [inputs.chunk(w.id, inputs.V, j, B, H, C, d).to(dev) for j in range(P)]
+    ks = [inputs.chunk(w.id, inputs.K, j, B, Hk, C, d).to(dev) for j in range(P)]
+    vs = [inputs.chunk(w.id, inputs.V, j, B, Hk, C, d).to(dev) for j in range(P)]
     o = torch.empty(B, H, C, d, device=dev)
     lse = torch.empty(B, H, C, device=dev)
     dq = torch.empty(B, H, C, d, device=dev)
-    dk = [torch.zeros(B, H, C, d, device=dev) for _ in range(P)]
-    dv = [torch.zeros(B, H, C, d, device=dev) for _ in range(P)]
-    ws_f = torch.empty(ra.workspace_bytes(P, B, H, C, d, "double_buffer"), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(ra.workspace_bytes(P, B, H, C, d, "resident", bwd=True), dtype=torch.uint8, device=dev)
+    dk = [torch.zeros(B, Hk, C, d, device=dev) for _ in range(P)]
+    dv = [torch.zeros(B, Hk, C, d, device=dev) for _ in range(P)]
+    ws_f = torch.empty(ra.workspace_bytes(P, B, H, C, d, "double_buffer", H_kv=Hk), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(ra.workspace_bytes(P, B, H, C, d, "resident", bwd=True, H_kv=Hk), dtype=torch.uint8,
+                       device=dev)
     copy_stream = torch.cuda.Stream(dev)
     nvis = sum(k != "skip" for *_, k in step_kinds(r, P, w.causal))
     n_launch = nvis + 2 + 2 * nvis
@@ -266,6 +278,7 @@ def main():
     ap.add_argument("--ring-mode", default="double_buffer", choices=["double_buffer", "resident"])
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query (H_kv = H/4) measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -326,6 +339,26 @@ def main():
         out["train"] = tr
         print(f"[bench] train: {tr['ms_per_step']:.3f} ms/step, {tr['tflops_fwd_bwd']:.1f} TFLOP/s", file=sys.stderr,
               flush=True)
+    if not args.no_gqa and w.H % 4 == 0:
+        # Grouped-query attention, 4 query heads per key/value head: the same
+        # attention flops, a quarter of the key/value bytes each ring step moves.
+        Hk = w.H // 4
+        g, _ = run_fwd(w, args.steps, args.warmup, args.ring_mode, H_kv=Hk)
+        out["gqa"] = {
+            "H": w.H, "H_kv": Hk, "fwd_ms_per_step": round(g["ms_per_step"], 4),
+            "fwd_tflops": round(g["tflops"], 2), "kernels": g["kernels"],
+            "kv_bytes_per_ring_step": g["kv_bytes_per_ring_step"],
+            "kv_bytes_per_ring_step_mha": fwd["kv_bytes_per_ring_step"],
+        }
+        print(f"[bench] gqa fwd H_kv={Hk}: {g['ms_per_step']:.3f} ms/step, {g['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        wt = WORKLOADS[5]
+        if not args.no_train and wt.H % 4 == 0:
+            gt = run_train(wt, max(3, args.steps // 2), max(1, args.warmup), H_kv=wt.H // 4)
+            out["gqa"]["train"] = gt
+            print(f"[bench] gqa train H_kv={wt.H // 4}: {gt['ms_per_step']:.3f} ms/step, "
+                  f"{gt['tflops_fwd_bwd']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     print(json.dumps(out))
 
 
