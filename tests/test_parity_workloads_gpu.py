@@ -12,6 +12,10 @@ stream).
   rows per head, dK/dV on 256 sampled key rows per chunk for 4 heads, and on
   every key the sums that hold exactly: sum_k dK_k = 0 and
   sum_k dV_k = sum_q dO_q.
+* Grouped-query attention (key/value chunks of H/4 heads): the 128K/CP=4
+  share on sampled rows, and the training share's dQ on sampled rows, dK/dV
+  (summed over each group's query heads) on sampled key rows of two
+  key/value heads, and the gradient sums on every key.
 
 The oracle runs on the host, fanned out over heads with one BLAS thread per
 task.
@@ -38,11 +42,12 @@ def say(msg):
     print(msg, flush=True)
 
 
-def gen_workload(w, ranks=None, with_do=False):
+def gen_workload(w, ranks=None, with_do=False, H_kv=None):
     ranks = w.ranks if ranks is None else ranks
+    Hk = w.H if H_kv is None else H_kv
     q = {r: inputs.chunk(w.id, inputs.Q, r, w.B, w.H, w.C, w.d) for r in ranks}
-    k = [inputs.chunk(w.id, inputs.K, j, w.B, w.H, w.C, w.d) for j in range(w.P)]
-    v = [inputs.chunk(w.id, inputs.V, j, w.B, w.H, w.C, w.d) for j in range(w.P)]
+    k = [inputs.chunk(w.id, inputs.K, j, w.B, Hk, w.C, w.d) for j in range(w.P)]
+    v = [inputs.chunk(w.id, inputs.V, j, w.B, Hk, w.C, w.d) for j in range(w.P)]
     do = {r: inputs.chunk(w.id, inputs.DO, r, w.B, w.H, w.C, w.d) for r in ranks} if with_do else None
     return q, k, v, do
 
@@ -66,13 +71,14 @@ def fan_out(fn, items):
         return list(ex.map(fn, items))
 
 
-def check_rows(w, rank, q, k, v, o, lse, rows_of_head, label):
-    """Oracle on rows_of_head(h) of every head vs the GPU (o, lse)."""
+def check_rows(w, rank, q, k, v, o, lse, rows_of_head, label, grp=1):
+    """Oracle on rows_of_head(h) of every head vs the GPU (o, lse).  grp > 1:
+    grouped-query key/value chunks, query head h reads key/value head h // grp."""
     o_c, l_c = o.cpu(), lse.cpu()
 
     def one(h):
         rows = rows_of_head(h)
-        kh, vh = head_full(k, h), head_full(v, h)
+        kh, vh = head_full(k, h // grp), head_full(v, h // grp)
         qh = f64(q[:, h:h + 1, rows])
         ro, rl = oracle.attention_fwd(qh, kh, vh, w.scale, w.causal, q_pos=rank * w.C + rows)
         go, gl = f64(o_c[:, h:h + 1, rows]), f64(l_c[:, h:h + 1, rows])
@@ -282,4 +288,122 @@ def test_train_gradient_sums_every_key(train_run):
     r_k = (sum_dk.abs() / scale_k.clamp_min(1e-30)).max().item()
     r_v = ((sum_dv - sum_do).abs().max() / sum_do.abs().max()).item()
     say(f"{w.name}: max|sum dK|/sum|dK|={r_k:.2e}  max|sum dV - sum dO|/max|sum dO|={r_v:.2e}")
+    assert r_k <= 1e-3 and r_v <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query attention at full size: the 128K/CP=4 share and the training
+# share with key/value chunks of H/4 = 8 heads (the bench's gqa runs).
+# ---------------------------------------------------------------------------
+
+GQA_GROUP = 4
+
+
+@pytest.mark.timeout(600)
+def test_gqa_local_share_sampled_rows():
+    w = WORKLOADS[2]
+    r = w.ranks[0]
+    Hk = w.H // GQA_GROUP
+    say(f"{w.name}, H_kv={Hk}: inputs and GPU walk")
+    q, k, v, _ = gen_workload(w, H_kv=Hk)
+    kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
+    o, lse = gpu_ring_fwd(w, r, q[r], kd, vd)
+    del kd, vd
+    check_rows(w, r, q[r], k, v, o, lse, lambda h: inputs.query_row_sample(w.id, h, w.C),
+               f"{w.name} H_kv={Hk} sampled rows", grp=GQA_GROUP)
+
+
+@pytest.fixture(scope="module")
+def train_run_gqa():
+    w = WORKLOADS[5]
+    r = w.ranks[0]
+    Hk = w.H // GQA_GROUP
+    say(f"{w.name}, H_kv={Hk}: inputs")
+    q, k, v, do = gen_workload(w, with_do=True, H_kv=Hk)
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    o, lse = gpu_ring_fwd(w, r, q[r], kd, vd)
+    dq = torch.full_like(o, float("nan"))
+    dk = [torch.zeros(w.B, Hk, w.C, w.d, device=dev()) for _ in range(w.P)]
+    dv = [torch.zeros(w.B, Hk, w.C, w.d, device=dev()) for _ in range(w.P)]
+    say(f"{w.name}, H_kv={Hk}: GPU backward walk")
+    ra.ring_bwd(q[r].to(dev()), kd, vd, o, lse, do[r].to(dev()), dq, dk, dv, r, w.causal, w.scale)
+    torch.cuda.synchronize()
+    out = dict(w=w, r=r, Hk=Hk, q=q[r], k=k, v=v, do=do[r], o=o.cpu(), lse=lse.cpu(), dq=dq.cpu(),
+               dk=[t.cpu() for t in dk], dv=[t.cpu() for t in dv])
+    del kd, vd, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return out
+
+
+@pytest.mark.timeout(600)
+def test_gqa_train_dq_sampled_rows(train_run_gqa):
+    t = train_run_gqa
+    w, r = t["w"], t["r"]
+
+    def one(h):
+        rows = inputs.query_row_sample(w.id, h, w.C)
+        kh, vh = head_full(t["k"], h // GQA_GROUP), head_full(t["v"], h // GQA_GROUP)
+        qh, doh = f64(t["q"][:, h:h + 1, rows]), f64(t["do"][:, h:h + 1, rows])
+        pos = r * w.C + rows
+        rq, _, _ = oracle.attention_bwd(qh, kh, vh, doh, w.scale, True, q_pos=pos)
+        gq = f64(t["dq"][:, h:h + 1, rows])
+        return np.abs(gq - rq).max(), np.linalg.norm(gq - rq) ** 2, np.linalg.norm(rq) ** 2
+
+    say(f"{w.name}, H_kv={t['Hk']}: oracle dQ on 256 rows x {w.H} heads")
+    res = fan_out(one, range(w.H))
+    e_q = max(x[0] for x in res)
+    rel = math.sqrt(sum(x[1] for x in res) / sum(x[2] for x in res))
+    say(f"  max|ddQ|={e_q:.2e} rel={rel:.2e}")
+    assert e_q <= TOL_GRAD and rel <= TOL_REL
+
+
+@pytest.mark.timeout(900)
+def test_gqa_train_dk_dv_sampled_key_rows(train_run_gqa):
+    """dK/dV of a key/value head sum over the 4 query heads of its group."""
+    t = train_run_gqa
+    w, r = t["w"], t["r"]
+    kv_heads = [0, t["Hk"] - 1]
+    pos = r * w.C + np.arange(w.C)
+
+    def one(hk):
+        kh, vh = head_full(t["k"], hk), head_full(t["v"], hk)
+        grp = slice(hk * GQA_GROUP, (hk + 1) * GQA_GROUP)
+        qg, dog = f64(t["q"][:, grp]), f64(t["do"][:, grp])
+        per_chunk = [inputs.key_row_sample(w.id, hk, j, w.C) for j in range(w.P)]
+        all_rows = np.concatenate([j * w.C + rows for j, rows in enumerate(per_chunk)])
+        rk, rv = oracle.attention_bwd_key_rows(qg, kh, vh, dog, w.scale, True, all_rows, q_pos=pos)
+        errs = []
+        n0 = 0
+        for j, rows in enumerate(per_chunk):
+            sl = slice(n0, n0 + len(rows))
+            n0 += len(rows)
+            gk, gv = f64(t["dk"][j][:, hk:hk + 1, rows]), f64(t["dv"][j][:, hk:hk + 1, rows])
+            errs.append((np.abs(gk - rk[:, :, sl]).max(), np.abs(gv - rv[:, :, sl]).max(),
+                         np.linalg.norm(gk - rk[:, :, sl]) ** 2 + np.linalg.norm(gv - rv[:, :, sl]) ** 2,
+                         np.linalg.norm(rk[:, :, sl]) ** 2 + np.linalg.norm(rv[:, :, sl]) ** 2))
+        return errs
+
+    say(f"{w.name}, H_kv={t['Hk']}: oracle dK/dV on 256 key rows x {w.P} chunks x key/value heads {kv_heads}")
+    res = [e for per_head in fan_out(one, kv_heads) for e in per_head]
+    e_k, e_v = max(x[0] for x in res), max(x[1] for x in res)
+    rel = math.sqrt(sum(x[2] for x in res) / sum(x[3] for x in res))
+    say(f"  max|ddK|={e_k:.2e} max|ddV|={e_v:.2e} rel={rel:.2e}")
+    assert e_k <= TOL_GRAD and e_v <= TOL_GRAD and rel <= TOL_REL
+
+
+def test_gqa_train_gradient_sums_every_key(train_run_gqa):
+    """Per key/value head: sum_k dK_k = 0, and sum_k dV_k = the sum of dO over
+    the query rows of every query head in its group."""
+    t = train_run_gqa
+    w = t["w"]
+    dk = torch.cat(t["dk"], dim=2).double()
+    dv = torch.cat(t["dv"], dim=2).double()
+    sum_dk = dk.sum(dim=2)
+    scale_k = dk.abs().sum(dim=2)
+    do = t["do"].double()
+    sum_do = do.reshape(w.B, t["Hk"], GQA_GROUP, w.C, w.d).sum(dim=(2, 3))
+    r_k = (sum_dk.abs() / scale_k.clamp_min(1e-30)).max().item()
+    r_v = ((dv.sum(dim=2) - sum_do).abs().max() / sum_do.abs().max()).item()
+    say(f"{w.name}, H_kv={t['Hk']}: max|sum dK|/sum|dK|={r_k:.2e}  max|sum dV - sum dO|/max|sum dO|={r_v:.2e}")
     assert r_k <= 1e-3 and r_v <= 1e-3
