@@ -29,6 +29,12 @@ What it computes, and the passage each function follows:
   statistics; "Context Parallelism", 2 "How It Works", last sentence).  Used by
   the tests only to check invariants of the method, never as the expected
   value of a GPU output.
+* ``ulysses.ulysses_share`` / ``ulysses_gather`` / ``ulysses_scatter`` -- one
+  rank's share of head-partitioned (Ulysses) sequence parallelism: the
+  all-to-all regrouping by head, full attention for the rank's heads over the
+  whole sequence, and the regrouping back ("Context Parallelism", 3 "Ulysses
+  (DeepSpeed)", steps 1-4).  Pinned against the library's attention and
+  against the ring walk (``tests/test_oracle_ulysses.py``).
 * ``schedule.ring_schedule`` -- which KV chunk a rank uses at each step
   ("Context Parallelism", 2 "How It Works": step s uses K_{i-s}, V_{i-s};
   "Training Long-Context Models Without OOM", "Ring Attention Demystified",
