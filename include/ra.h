@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define RA_VERSION 2
+#define RA_VERSION 3
 
 enum ra_status {
   RA_OK = 0,
@@ -221,13 +221,38 @@ int ra_ring_bwd_gqa(const void* q, const void* const* k_chunks,
                     void* stream);
 
 /*
+ * ra_ulysses_fwd -- one GPU's share of head-partitioned (Ulysses) sequence
+ * parallelism, forward ("Context Parallelism", 3 "Ulysses (DeepSpeed)";
+ * "Training Long-Context Models Without OOM: Ring Attention", "Ring
+ * Attention vs. DeepSpeed Ulysses (All-to-All)").  The sequence is split in
+ * P chunks of C tokens (q_chunks[j], k_chunks[j], v_chunks[j]: HOST arrays of
+ * P device pointers to [B,H,C,d] bf16, chunk j = global tokens [jC,(j+1)C)).
+ * Rank `rank` regroups its heads rank*H/P .. (rank+1)*H/P-1 of every chunk
+ * into workspace (on one GPU this stands in for the all-to-all of step 2),
+ * then computes exact attention for those heads over the whole sequence of
+ * S = P*C tokens (step 3; causal != 0 masks key positions after the query's).
+ * Writes o [B,H/P,S,d] and lse [B,H/P,S] fp32 (overwritten), the rank's
+ * head-partitioned output; step 4's all-to-all back to sequence chunks is the
+ * exchange between GPUs and is not performed.  Needs H % P == 0
+ * (RA_ERR_SHAPE) and ra_ulysses_workspace_bytes(P,B,H,C,d) bytes of
+ * 16-byte-aligned workspace (RA_ERR_WORKSPACE).  Other contracts as for
+ * ra_ring_fwd.
+ */
+size_t ra_ulysses_workspace_bytes(int P, int B, int H, int C, int d);
+int ra_ulysses_fwd(const void* const* q_chunks, const void* const* k_chunks,
+                   const void* const* v_chunks, int P, float* o, float* lse,
+                   int rank, int causal, float scale, int B, int H, int C,
+                   int d, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
  * Per-launch tracing, for profiling.  The pages define no such facility; it
  * exists so that a caller can time each kernel of a ring walk with its own
  * events, on the stream the kernel runs on.
  *
  * ra_trace_begin arms tracing on the calling thread.  Every kernel that
- * ra_step_fwd, ra_lse_merge, ra_ring_fwd or ra_ring_bwd (or their *_gqa
- * forms) then launch on their
+ * ra_step_fwd, ra_lse_merge, ra_ring_fwd, ra_ring_bwd (or their *_gqa
+ * forms) or ra_ulysses_fwd then launch on their
  * compute stream is bracketed by hipEventRecord(start_events[n], stream)
  * and hipEventRecord(end_events[n], stream), and kinds[n] receives its
  * RA_TRACE_* kind, for the n-th such launch while n < capacity (later

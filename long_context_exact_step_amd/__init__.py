@@ -16,6 +16,7 @@ import os
 __all__ = [
     "RAError", "lib", "version", "step_fwd", "lse_merge", "ring_fwd", "ring_bwd",
     "workspace_bytes", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH", "trace_begin", "trace_end",
+    "ulysses_fwd", "ulysses_workspace_bytes",
     "TRACE_KINDS",
 ]
 
@@ -74,6 +75,10 @@ def lib():
         L.ra_ring_fwd_gqa.argtypes = [vp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, i, i, vp, sz, vp, vp]
         L.ra_ring_bwd_gqa.restype = i
         L.ra_ring_bwd_gqa.argtypes = [vp, vpp, vpp, i, vp, vp, vp, vp, vpp, vpp, i, i, f, i, i, i, i, i, vp, sz, vp]
+        L.ra_ulysses_workspace_bytes.restype = sz
+        L.ra_ulysses_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.ra_ulysses_fwd.restype = i
+        L.ra_ulysses_fwd.argtypes = [vpp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, vp, sz, vp]
         L.ra_trace_begin.restype = i
         L.ra_trace_begin.argtypes = [vpp, vpp, ctypes.POINTER(ctypes.c_int), i]
         L.ra_trace_end.restype = i
@@ -218,6 +223,32 @@ def ring_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, 
         _check(lib().ra_ring_bwd(*head, *tail))
     else:
         _check(lib().ra_ring_bwd_gqa(*head, Hk, *tail))
+    return workspace
+
+
+def ulysses_workspace_bytes(P, B, H, C, d):
+    return int(lib().ra_ulysses_workspace_bytes(P, B, H, C, d))
+
+
+def ulysses_fwd(q_chunks, k_chunks, v_chunks, o, lse, rank, causal, scale=None, workspace=None, stream=None):
+    """ra_ulysses_fwd: one rank's share of head-partitioned (Ulysses) sequence
+    parallelism.  q/k/v_chunks: P tensors [B,H,C,d] bf16 (the sequence split in
+    chunks); o [B,H/P,P*C,d], lse [B,H/P,P*C] fp32 receive attention of the
+    rank's heads over the whole sequence."""
+    import torch
+    for n, t in enumerate(list(q_chunks) + list(k_chunks) + list(v_chunks)):
+        _need(t, torch.bfloat16, f"chunk{n}")
+    _need(o, torch.float32, "o")
+    _need(lse, torch.float32, "lse")
+    B, H, C, d = q_chunks[0].shape
+    P = len(q_chunks)
+    need = ulysses_workspace_bytes(P, B, H, C, d)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=o.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().ra_ulysses_fwd(_ptr_array(q_chunks), _ptr_array(k_chunks), _ptr_array(v_chunks), P, _ptr(o),
+                                _ptr(lse), int(rank), int(bool(causal)), scale, B, H, C, d, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream, o)))
     return workspace
 
 

@@ -382,4 +382,64 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v
                          H, C, d, workspace, workspace_bytes, stream);
 }
 
+size_t ra_ulysses_workspace_bytes(int P, int B, int H, int C, int d) {
+  if (P < 1 || B < 1 || H < 1 || H % P || C < 1 || (d != 64 && d != 128)) return 0;
+  return 3 * (size_t)B * (H / P) * ((size_t)P * C) * d * 2;  // regrouped Q, K, V (bf16)
+}
+
+int ra_ulysses_fwd(const void* const* q_chunks, const void* const* k_chunks, const void* const* v_chunks, int P,
+                   float* o, float* lse, int rank, int causal, float scale, int B, int H, int C, int d,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_chunks || !k_chunks || !v_chunks || !o || !lse) return fail(RA_ERR_NULL, "ra_ulysses_fwd: NULL pointer");
+  if (P < 1) return fail(RA_ERR_SHAPE, "ra_ulysses_fwd: P=%d < 1", P);
+  int st = check_dims(B, H, C, d, "ra_ulysses_fwd");
+  if (st) return st;
+  if (H % P) return fail(RA_ERR_SHAPE, "ra_ulysses_fwd: H=%d heads do not split over P=%d ranks", H, P);
+  if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "ra_ulysses_fwd: rank=%d outside [0, %d)", rank, P);
+  const int Hs = H / P;
+  const long long S = (long long)P * C;
+  if ((long long)B * Hs * S > 0x7fffffffLL) return fail(RA_ERR_SHAPE, "ra_ulysses_fwd: B*H/P*P*C exceeds 2^31-1");
+  for (int j = 0; j < P; ++j) {
+    if (!q_chunks[j] || !k_chunks[j] || !v_chunks[j])
+      return fail(RA_ERR_NULL, "ra_ulysses_fwd: chunk %d pointer is NULL", j);
+    if (!aligned16(q_chunks[j]) || !aligned16(k_chunks[j]) || !aligned16(v_chunks[j]))
+      return fail(RA_ERR_ALIGN, "ra_ulysses_fwd: chunk %d pointer not 16-byte aligned", j);
+  }
+  if (!aligned16(o) || !aligned16(lse)) return fail(RA_ERR_ALIGN, "ra_ulysses_fwd: outputs not 16-byte aligned");
+  const size_t need = ra_ulysses_workspace_bytes(P, B, H, C, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "ra_ulysses_fwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  if (!aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_ulysses_fwd: workspace not 16-byte aligned");
+
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  // Step 2 for this rank: heads rank*Hs .. rank*Hs+Hs-1 of every sequence
+  // chunk into [B, Hs, S, d] buffers.  Within a chunk those heads are one
+  // contiguous run of Hs rows of C*d values; in the regrouped buffer each
+  // head's C tokens land at sequence offset j*C.
+  const size_t tok = (size_t)d * 2;
+  const size_t part = (size_t)B * Hs * S * tok;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const void* const* srcs[3] = {q_chunks, k_chunks, v_chunks};
+  for (int x = 0; x < 3; ++x) {
+    for (int j = 0; j < P; ++j) {
+      for (int b = 0; b < B; ++b) {
+        const uint8_t* src = static_cast<const uint8_t*>(srcs[x][j]) + ((size_t)b * H + (size_t)rank * Hs) * C * tok;
+        uint8_t* dst = ws + x * part + ((size_t)b * Hs * S + (size_t)j * C) * tok;
+        const hipError_t e = hipMemcpy2DAsync(dst, S * tok, src, C * tok, C * tok, Hs, hipMemcpyDeviceToDevice, cs);
+        if (e != hipSuccess) return hip_fail(e, "ra_ulysses_fwd regroup");
+      }
+    }
+  }
+  // Step 3: full attention of the regrouped heads over the whole sequence
+  // (the causal mask over global positions is the diagonal mask at S).
+  const uint16_t* qr = reinterpret_cast<const uint16_t*>(ws);
+  const uint16_t* kr = reinterpret_cast<const uint16_t*>(ws + part);
+  const uint16_t* vr = reinterpret_cast<const uint16_t*>(ws + 2 * part);
+  const ra::FwdStepArgs a{qr, kr, vr, o, lse, B * Hs, (int)S, (int)S, d, scale, causal != 0, false, 1};
+  const hipError_t e = fwd_step(a, cs);
+  if (e != hipSuccess) return hip_fail(e, "ra_ulysses_fwd attention");
+  return ok();
+}
+
 }  // extern "C"

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ra_version() == 2  # 2: grouped-query (*_gqa) entry points
+    assert L.ra_version() == 3  # 2: grouped-query (*_gqa) entry points; 3: ra_ulysses_fwd
     assert L.ra_status_string(RA_OK) == b"RA_OK"
     assert L.ra_status_string(RA_ERR_WORKSPACE) == b"RA_ERR_WORKSPACE"
     assert L.ra_status_string(12345) == b"RA_ERR_UNKNOWN"
@@ -142,6 +142,22 @@ def test_gqa_validation(L):
     # A valid grouping gets past the head check to the next one (here: the rank).
     assert L.ra_ring_fwd_gqa(vp(FAKE), arr, arr, P, vp(FAKE), vp(FAKE), 9, 1, 0.1, 1, 8, 2, C, d, 0,
                              None, 0, None, None) == RA_ERR_RANK
+
+
+def test_ulysses_workspace_and_validation(L):
+    assert L.ra_ulysses_workspace_bytes(4, 1, 32, 32768, 128) == 3 * 8 * 131072 * 128 * 2
+    assert L.ra_ulysses_workspace_bytes(3, 1, 32, 64, 128) == 0  # 32 heads do not split over 3
+    P, C, d = 4, 64, 128
+    arr = (ctypes.c_void_p * P)(*([FAKE] * P))
+    need = L.ra_ulysses_workspace_bytes(P, 1, 8, C, d)
+    call = lambda H=8, rank=1, ws=FAKE, wsb=need, chunks=arr: L.ra_ulysses_fwd(
+        chunks, chunks, chunks, P, vp(FAKE), vp(FAKE), rank, 1, 0.1, 1, H, C, d, vp(ws), wsb, None)
+    assert call(H=6) == RA_ERR_SHAPE
+    assert call(rank=4) == RA_ERR_RANK
+    assert call(ws=0) == RA_ERR_WORKSPACE
+    assert call(wsb=need - 16) == RA_ERR_WORKSPACE
+    assert call(chunks=(ctypes.c_void_p * P)(FAKE, FAKE, 0, FAKE)) == RA_ERR_NULL
+    assert call(chunks=(ctypes.c_void_p * P)(FAKE, MIS, FAKE, FAKE)) == RA_ERR_ALIGN
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -287,3 +287,26 @@ def test_ring_bwd_gqa_matches_oracle(P, C, d, H, Hk):
             sl = slice(j * C, (j + 1) * C)
             assert_close(f64(dk[j]), rk[:, :, sl], TOL_GRAD, f"dk chunk {j}")
             assert_close(f64(dv[j]), rv[:, :, sl], TOL_GRAD, f"dv chunk {j}")
+
+
+# ---------------------------------------------------------------------------
+# Head-partitioned (Ulysses) share: regroup by head, full-sequence attention.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P,C,H,d,causal", [(2, 100, 4, 128, True), (4, 37, 8, 64, True),
+                                            (3, 129, 3, 128, False), (2, 300, 2, 128, True)])
+def test_ulysses_share_every_rank(P, C, H, d, causal):
+    from oracle.ulysses import ulysses_share
+    q, k, v, _ = ring_tensors(111, 1, H, P, C, d)
+    qc = [q[r] for r in range(P)]
+    qd, kd, vd = ([t.to(dev()) for t in x] for x in (qc, k, v))
+    scale = 1 / math.sqrt(d)
+    for rank in range(P):
+        print(f"ulysses P={P} C={C} H={H} d={d} causal={causal} rank={rank}", flush=True)
+        o = torch.full((1, H // P, P * C, d), float("nan"), device=dev())
+        lse = torch.full((1, H // P, P * C), float("nan"), device=dev())
+        ra.ulysses_fwd(qd, kd, vd, o, lse, rank, causal, scale)
+        torch.cuda.synchronize()
+        ro, rl = ulysses_share([f64(t) for t in qc], [f64(t) for t in k], [f64(t) for t in v], rank, causal, scale)
+        assert_close(f64(o), ro, TOL_O, f"o rank {rank}")
+        assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)

@@ -12,6 +12,8 @@ stream).
   rows per head, dK/dV on 256 sampled key rows per chunk for 4 heads, and on
   every key the sums that hold exactly: sum_k dK_k = 0 and
   sum_k dV_k = sum_q dO_q.
+* Head-partitioned (Ulysses) share of the 128K/CP=4 sequence: ranks 0 and 3,
+  H/4 = 8 heads over all 131072 tokens, 256 sampled rows per head.
 * Grouped-query attention (key/value chunks of H/4 heads): the 128K/CP=4
   share on sampled rows, and the training share's dQ on sampled rows, dK/dV
   (summed over each group's query heads) on sampled key rows of two
@@ -407,3 +409,43 @@ def test_gqa_train_gradient_sums_every_key(train_run_gqa):
     r_v = ((dv.sum(dim=2) - sum_do).abs().max() / sum_do.abs().max()).item()
     say(f"{w.name}, H_kv={t['Hk']}: max|sum dK|/sum|dK|={r_k:.2e}  max|sum dV - sum dO|/max|sum dO|={r_v:.2e}")
     assert r_k <= 1e-3 and r_v <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Head-partitioned (Ulysses) share of the 128K/CP=4 sequence.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.timeout(600)
+def test_ulysses_share_128k_sampled_rows():
+    w = WORKLOADS[2]
+    P, C = w.P, w.C
+    S = P * C
+    Hs = w.H // P
+    say(f"{w.name}: Ulysses inputs (every chunk)")
+    q, k, v, _ = gen_workload(w, ranks=range(P))
+    qc = [q[r] for r in range(P)]
+    qd, kd, vd = ([t.to(dev()) for t in x] for x in (qc, k, v))
+    for rank in (0, P - 1):
+        say(f"{w.name}: Ulysses share of rank {rank} ({Hs} heads x {S} tokens)")
+        o = torch.full((w.B, Hs, S, w.d), float("nan"), device=dev())
+        lse = torch.full((w.B, Hs, S), float("nan"), device=dev())
+        ra.ulysses_fwd(qd, kd, vd, o, lse, rank, w.causal, w.scale)
+        torch.cuda.synchronize()
+        o_c, l_c = o.cpu(), lse.cpu()
+
+        def one(i):
+            h = rank * Hs + i  # global head
+            rows = inputs.query_row_sample(w.id, h, S)
+            kh, vh = head_full(k, h), head_full(v, h)
+            qh = np.concatenate([f64(c[:, h:h + 1]) for c in qc], axis=2)[:, :, rows]
+            ro, rl = oracle.attention_fwd(qh, kh, vh, w.scale, w.causal, q_pos=rows)
+            go, gl = f64(o_c[:, i:i + 1, rows]), f64(l_c[:, i:i + 1, rows])
+            return np.abs(go - ro).max(), np.abs(gl - rl).max(), np.isfinite(go).all()
+
+        res = fan_out(one, range(Hs))
+        e_o, e_l = max(r_[0] for r_ in res), max(r_[1] for r_ in res)
+        say(f"  max|dO|={e_o:.2e} max|dlse|={e_l:.2e}")
+        assert all(r_[2] for r_ in res) and e_o <= TOL_O and e_l <= TOL_LSE
+        del o, lse
+    del qd, kd, vd
+    torch.cuda.empty_cache()
