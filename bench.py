@@ -11,7 +11,9 @@ seeded synthetic bf16 N(0,1) tensors resident in HBM before timing starts.
 Also reported (unless --no-train): the training share (C = 16384, P = 4,
 rank 3, H = 32, d = 128, causal), one step = forward walk + backward walk.
 And (unless --no-gqa): both walks again with grouped-query key/value chunks of
-H/4 heads (4 query heads per key/value head), under "gqa".
+H/4 heads (4 query heads per key/value head), under "gqa".  And (unless
+--no-ulysses): one rank's share of head-partitioned (Ulysses) sequence
+parallelism on the same sequence, under "ulysses".
 
 Prints ONE JSON line: throughput in algorithmic TFLOP/s (4*d flops per
 visible (query, key) pair forward, 10*d backward), tokens/s, the roofline of
@@ -218,6 +220,39 @@ def run_train(w, steps, warmup, H_kv=None):
     }
 
 
+def run_ulysses(w, steps, warmup, rank=0):
+    """One rank's share of head-partitioned (Ulysses) sequence parallelism on
+    workload w's sequence: regroup its H/P heads of every chunk (the copies
+    that stand in for the all-to-all), then attention over all P*C tokens."""
+    import torch
+    import long_context_exact_step_amd as ra
+    from long_context_exact_step_amd import inputs
+
+    dev = torch.device("cuda", 0)
+    B, H, C, d, P = w.B, w.H, w.C, w.d, w.P
+    S, Hs = P * C, H // P
+    qc = [inputs.chunk(w.id, inputs.Q, j, B, H, C, d).to(dev) for j in range(P)]
+    kc = [inputs.chunk(w.id, inputs.K, j, B, H, C, d).to(dev) for j in range(P)]
+    vc = [inputs.chunk(w.id, inputs.V, j, B, H, C, d).to(dev) for j in range(P)]
+    o = torch.empty(B, Hs, S, d, device=dev)
+    lse = torch.empty(B, Hs, S, device=dev)
+    ws = torch.empty(ra.ulysses_workspace_bytes(P, B, H, C, d), dtype=torch.uint8, device=dev)
+
+    def step():
+        ra.ulysses_fwd(qc, kc, vc, o, lse, rank, w.causal, w.scale, workspace=ws)
+
+    secs, rec = timed_steps(step, 1, steps, warmup)
+    pairs = B * Hs * (S * (S + 1) // 2 if w.causal else S * S)
+    flops = 4 * d * pairs
+    k_ms = sum(m for _, m in rec) / max(1, len(rec))
+    return {
+        "rank": rank, "heads": Hs, "tokens": S, "ms_per_step": round(secs / steps * 1e3, 4),
+        "tflops": round(flops * steps / secs / 1e12, 2),
+        "attention_kernel_ms": round(k_ms, 4), "attention_kernel_tflops": round(flops / (k_ms * 1e-3) / 1e12, 2),
+        "regroup_bytes_per_step": 2 * 3 * B * Hs * S * d * 2,
+    }
+
+
 def cpu_baseline(w, tensors, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample: 256 seeded query
     rows per head of the measured rank, heads taken in order until the time
@@ -279,6 +314,7 @@ def main():
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query (H_kv = H/4) measurements")
+    ap.add_argument("--no-ulysses", action="store_true", help="skip the head-partitioned (Ulysses) share")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -359,6 +395,13 @@ def main():
             out["gqa"]["train"] = gt
             print(f"[bench] gqa train H_kv={wt.H // 4}: {gt['ms_per_step']:.3f} ms/step, "
                   f"{gt['tflops_fwd_bwd']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if not args.no_ulysses and w.H % w.P == 0:
+        torch.cuda.empty_cache()
+        u = run_ulysses(w, max(3, args.steps // 2), max(1, args.warmup))
+        u["ring_rank_ms_per_step"] = out["ms_per_step"]
+        out["ulysses"] = u
+        print(f"[bench] ulysses share ({u['heads']} heads x {u['tokens']} tokens): {u['ms_per_step']:.3f} ms/step, "
+              f"{u['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     print(json.dumps(out))
 
 
