@@ -234,16 +234,36 @@ int ra_ring_bwd_gqa(const void* q, const void* const* k_chunks,
  * Writes o [B,H/P,S,d] and lse [B,H/P,S] fp32 (overwritten), the rank's
  * head-partitioned output; step 4's all-to-all back to sequence chunks is the
  * exchange between GPUs and is not performed.  Needs H % P == 0
- * (RA_ERR_SHAPE) and ra_ulysses_workspace_bytes(P,B,H,C,d) bytes of
+ * (RA_ERR_SHAPE) and ra_ulysses_workspace_bytes(P,B,H,C,d,0) bytes of
  * 16-byte-aligned workspace (RA_ERR_WORKSPACE).  Other contracts as for
  * ra_ring_fwd.
+ *
+ * ra_ulysses_bwd -- the same share's backward (the softmax-attention
+ * gradient with P recomputed from the share's final lse, as ra_ring_bwd).
+ * dO_chunks: HOST array of P device pointers to [B,H,C,d] bf16, split by
+ * sequence like q_chunks and regrouped the same way; o [B,H/P,S,d] and lse
+ * [B,H/P,S] are ra_ulysses_fwd's outputs.  dq, dk, dv [B,H/P,S,d] fp32 are
+ * overwritten with the gradients of the rank's heads over the whole sequence
+ * (complete: every query of those heads is local).  Workspace:
+ * ra_ulysses_workspace_bytes(P,B,H,C,d,1) bytes.
+ *
+ * ra_ulysses_workspace_bytes: bwd == 0: regrouped Q, K, V,
+ * 3 * B*(H/P)*P*C*d * 2 bytes; bwd != 0: regrouped Q, K, V, dO and two fp32
+ * values per row, 4 * B*(H/P)*P*C*d * 2 + 2 * B*(H/P)*P*C * 4 bytes.  0 for
+ * invalid sizes.
  */
-size_t ra_ulysses_workspace_bytes(int P, int B, int H, int C, int d);
+size_t ra_ulysses_workspace_bytes(int P, int B, int H, int C, int d, int bwd);
 int ra_ulysses_fwd(const void* const* q_chunks, const void* const* k_chunks,
                    const void* const* v_chunks, int P, float* o, float* lse,
                    int rank, int causal, float scale, int B, int H, int C,
                    int d, void* workspace, size_t workspace_bytes,
                    void* stream);
+int ra_ulysses_bwd(const void* const* q_chunks, const void* const* k_chunks,
+                   const void* const* v_chunks, const void* const* dO_chunks,
+                   int P, const float* o, const float* lse, float* dq,
+                   float* dk, float* dv, int rank, int causal, float scale,
+                   int B, int H, int C, int d, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /*
  * Per-launch tracing, for profiling.  The pages define no such facility; it
@@ -252,7 +272,7 @@ int ra_ulysses_fwd(const void* const* q_chunks, const void* const* k_chunks,
  *
  * ra_trace_begin arms tracing on the calling thread.  Every kernel that
  * ra_step_fwd, ra_lse_merge, ra_ring_fwd, ra_ring_bwd (or their *_gqa
- * forms) or ra_ulysses_fwd then launch on their
+ * forms), ra_ulysses_fwd or ra_ulysses_bwd then launch on their
  * compute stream is bracketed by hipEventRecord(start_events[n], stream)
  * and hipEventRecord(end_events[n], stream), and kinds[n] receives its
  * RA_TRACE_* kind, for the n-th such launch while n < capacity (later

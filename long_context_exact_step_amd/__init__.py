@@ -16,7 +16,7 @@ import os
 __all__ = [
     "RAError", "lib", "version", "step_fwd", "lse_merge", "ring_fwd", "ring_bwd",
     "workspace_bytes", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH", "trace_begin", "trace_end",
-    "ulysses_fwd", "ulysses_workspace_bytes",
+    "ulysses_fwd", "ulysses_bwd", "ulysses_workspace_bytes",
     "TRACE_KINDS",
 ]
 
@@ -76,7 +76,9 @@ def lib():
         L.ra_ring_bwd_gqa.restype = i
         L.ra_ring_bwd_gqa.argtypes = [vp, vpp, vpp, i, vp, vp, vp, vp, vpp, vpp, i, i, f, i, i, i, i, i, vp, sz, vp]
         L.ra_ulysses_workspace_bytes.restype = sz
-        L.ra_ulysses_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.ra_ulysses_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.ra_ulysses_bwd.restype = i
+        L.ra_ulysses_bwd.argtypes = [vpp, vpp, vpp, vpp, i, vp, vp, vp, vp, vp, i, i, f, i, i, i, i, vp, sz, vp]
         L.ra_ulysses_fwd.restype = i
         L.ra_ulysses_fwd.argtypes = [vpp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, vp, sz, vp]
         L.ra_trace_begin.restype = i
@@ -226,8 +228,8 @@ def ring_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, 
     return workspace
 
 
-def ulysses_workspace_bytes(P, B, H, C, d):
-    return int(lib().ra_ulysses_workspace_bytes(P, B, H, C, d))
+def ulysses_workspace_bytes(P, B, H, C, d, bwd=False):
+    return int(lib().ra_ulysses_workspace_bytes(P, B, H, C, d, int(bool(bwd))))
 
 
 def ulysses_fwd(q_chunks, k_chunks, v_chunks, o, lse, rank, causal, scale=None, workspace=None, stream=None):
@@ -248,6 +250,30 @@ def ulysses_fwd(q_chunks, k_chunks, v_chunks, o, lse, rank, causal, scale=None, 
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _check(lib().ra_ulysses_fwd(_ptr_array(q_chunks), _ptr_array(k_chunks), _ptr_array(v_chunks), P, _ptr(o),
                                 _ptr(lse), int(rank), int(bool(causal)), scale, B, H, C, d, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream, o)))
+    return workspace
+
+
+def ulysses_bwd(q_chunks, k_chunks, v_chunks, dO_chunks, o, lse, dq, dk, dv, rank, causal, scale=None,
+                workspace=None, stream=None):
+    """ra_ulysses_bwd: the Ulysses share's backward.  dO_chunks split by
+    sequence like q_chunks; o, lse from ulysses_fwd; dq, dk, dv [B,H/P,P*C,d]
+    fp32 are overwritten."""
+    import torch
+    for n, t in enumerate(list(q_chunks) + list(k_chunks) + list(v_chunks) + list(dO_chunks)):
+        _need(t, torch.bfloat16, f"chunk{n}")
+    for t, n in ((o, "o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, torch.float32, n)
+    _need(lse, torch.float32, "lse")
+    B, H, C, d = q_chunks[0].shape
+    P = len(q_chunks)
+    need = ulysses_workspace_bytes(P, B, H, C, d, bwd=True)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=o.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().ra_ulysses_bwd(_ptr_array(q_chunks), _ptr_array(k_chunks), _ptr_array(v_chunks),
+                                _ptr_array(dO_chunks), P, _ptr(o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                int(rank), int(bool(causal)), scale, B, H, C, d, _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream, o)))
     return workspace
 

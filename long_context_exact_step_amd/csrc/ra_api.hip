@@ -130,6 +130,43 @@ hipError_t traced(int kind, hipStream_t stream, F&& launch) {
   return e;
 }
 
+// Step 2 of the head-partitioned scheme for one rank: heads rank*Hs ..
+// rank*Hs+Hs-1 of every sequence chunk of `chunks` into a [B, Hs, P*C, d] bf16
+// buffer.  Within a chunk those heads are one contiguous run of Hs rows of
+// C*d values; in the regrouped buffer each head's C tokens land at sequence
+// offset j*C.
+hipError_t ulysses_regroup(const void* const* chunks, uint8_t* dst0, int P, int rank, int B, int H, int C, int d,
+                           hipStream_t s) {
+  const int Hs = H / P;
+  const size_t S = (size_t)P * C, tok = (size_t)d * 2;
+  for (int j = 0; j < P; ++j) {
+    for (int b = 0; b < B; ++b) {
+      const uint8_t* src = static_cast<const uint8_t*>(chunks[j]) + ((size_t)b * H + (size_t)rank * Hs) * C * tok;
+      uint8_t* dst = dst0 + ((size_t)b * Hs * S + (size_t)j * C) * tok;
+      const hipError_t e = hipMemcpy2DAsync(dst, S * tok, src, C * tok, C * tok, Hs, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+// Validation shared by the two head-partitioned entry points.
+int ulysses_check(const void* const* const* chunk_sets, int n_sets, int P, int rank, int B, int H, int C, int d,
+                  const char* what) {
+  if (P < 1) return fail(RA_ERR_SHAPE, "%s: P=%d < 1", what, P);
+  int st = check_dims(B, H, C, d, what);
+  if (st) return st;
+  if (H % P) return fail(RA_ERR_SHAPE, "%s: H=%d heads do not split over P=%d ranks", what, H, P);
+  if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "%s: rank=%d outside [0, %d)", what, rank, P);
+  if ((long long)B * (H / P) * P * C > 0x7fffffffLL) return fail(RA_ERR_SHAPE, "%s: B*H/P*P*C exceeds 2^31-1", what);
+  for (int x = 0; x < n_sets; ++x)
+    for (int j = 0; j < P; ++j) {
+      if (!chunk_sets[x][j]) return fail(RA_ERR_NULL, "%s: chunk %d pointer is NULL", what, j);
+      if (!aligned16(chunk_sets[x][j])) return fail(RA_ERR_ALIGN, "%s: chunk %d pointer not 16-byte aligned", what, j);
+    }
+  return RA_OK;
+}
+
 hipError_t fwd_step(const ra::FwdStepArgs& a, hipStream_t s) {
   return traced(a.diag ? RA_TRACE_FWD_DIAG : RA_TRACE_FWD_FULL, s, [&] { return ra::launch_fwd_step(a, s); });
 }
@@ -382,63 +419,88 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v
                          H, C, d, workspace, workspace_bytes, stream);
 }
 
-size_t ra_ulysses_workspace_bytes(int P, int B, int H, int C, int d) {
+size_t ra_ulysses_workspace_bytes(int P, int B, int H, int C, int d, int bwd) {
   if (P < 1 || B < 1 || H < 1 || H % P || C < 1 || (d != 64 && d != 128)) return 0;
-  return 3 * (size_t)B * (H / P) * ((size_t)P * C) * d * 2;  // regrouped Q, K, V (bf16)
+  const size_t rows = (size_t)B * (H / P) * ((size_t)P * C);
+  if (bwd) return 4 * rows * d * 2 + 2 * rows * sizeof(float);  // regrouped Q, K, V, dO; D and lse2 per row
+  return 3 * rows * d * 2;                                        // regrouped Q, K, V (bf16)
 }
+
 
 int ra_ulysses_fwd(const void* const* q_chunks, const void* const* k_chunks, const void* const* v_chunks, int P,
                    float* o, float* lse, int rank, int causal, float scale, int B, int H, int C, int d,
                    void* workspace, size_t workspace_bytes, void* stream) {
   if (!q_chunks || !k_chunks || !v_chunks || !o || !lse) return fail(RA_ERR_NULL, "ra_ulysses_fwd: NULL pointer");
-  if (P < 1) return fail(RA_ERR_SHAPE, "ra_ulysses_fwd: P=%d < 1", P);
-  int st = check_dims(B, H, C, d, "ra_ulysses_fwd");
+  const void* const* sets[3] = {q_chunks, k_chunks, v_chunks};
+  int st = ulysses_check(sets, 3, P, rank, B, H, C, d, "ra_ulysses_fwd");
   if (st) return st;
-  if (H % P) return fail(RA_ERR_SHAPE, "ra_ulysses_fwd: H=%d heads do not split over P=%d ranks", H, P);
-  if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "ra_ulysses_fwd: rank=%d outside [0, %d)", rank, P);
-  const int Hs = H / P;
-  const long long S = (long long)P * C;
-  if ((long long)B * Hs * S > 0x7fffffffLL) return fail(RA_ERR_SHAPE, "ra_ulysses_fwd: B*H/P*P*C exceeds 2^31-1");
-  for (int j = 0; j < P; ++j) {
-    if (!q_chunks[j] || !k_chunks[j] || !v_chunks[j])
-      return fail(RA_ERR_NULL, "ra_ulysses_fwd: chunk %d pointer is NULL", j);
-    if (!aligned16(q_chunks[j]) || !aligned16(k_chunks[j]) || !aligned16(v_chunks[j]))
-      return fail(RA_ERR_ALIGN, "ra_ulysses_fwd: chunk %d pointer not 16-byte aligned", j);
-  }
   if (!aligned16(o) || !aligned16(lse)) return fail(RA_ERR_ALIGN, "ra_ulysses_fwd: outputs not 16-byte aligned");
-  const size_t need = ra_ulysses_workspace_bytes(P, B, H, C, d);
+  const size_t need = ra_ulysses_workspace_bytes(P, B, H, C, d, 0);
   if (!workspace || workspace_bytes < need)
     return fail(RA_ERR_WORKSPACE, "ra_ulysses_fwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
                 need);
   if (!aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_ulysses_fwd: workspace not 16-byte aligned");
 
   hipStream_t cs = static_cast<hipStream_t>(stream);
-  // Step 2 for this rank: heads rank*Hs .. rank*Hs+Hs-1 of every sequence
-  // chunk into [B, Hs, S, d] buffers.  Within a chunk those heads are one
-  // contiguous run of Hs rows of C*d values; in the regrouped buffer each
-  // head's C tokens land at sequence offset j*C.
-  const size_t tok = (size_t)d * 2;
-  const size_t part = (size_t)B * Hs * S * tok;
+  const int Hs = H / P, S = P * C;
+  const size_t part = (size_t)B * Hs * S * d * 2;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const void* const* srcs[3] = {q_chunks, k_chunks, v_chunks};
   for (int x = 0; x < 3; ++x) {
-    for (int j = 0; j < P; ++j) {
-      for (int b = 0; b < B; ++b) {
-        const uint8_t* src = static_cast<const uint8_t*>(srcs[x][j]) + ((size_t)b * H + (size_t)rank * Hs) * C * tok;
-        uint8_t* dst = ws + x * part + ((size_t)b * Hs * S + (size_t)j * C) * tok;
-        const hipError_t e = hipMemcpy2DAsync(dst, S * tok, src, C * tok, C * tok, Hs, hipMemcpyDeviceToDevice, cs);
-        if (e != hipSuccess) return hip_fail(e, "ra_ulysses_fwd regroup");
-      }
-    }
+    const hipError_t e = ulysses_regroup(sets[x], ws + x * part, P, rank, B, H, C, d, cs);
+    if (e != hipSuccess) return hip_fail(e, "ra_ulysses_fwd regroup");
   }
   // Step 3: full attention of the regrouped heads over the whole sequence
   // (the causal mask over global positions is the diagonal mask at S).
-  const uint16_t* qr = reinterpret_cast<const uint16_t*>(ws);
-  const uint16_t* kr = reinterpret_cast<const uint16_t*>(ws + part);
-  const uint16_t* vr = reinterpret_cast<const uint16_t*>(ws + 2 * part);
-  const ra::FwdStepArgs a{qr, kr, vr, o, lse, B * Hs, (int)S, (int)S, d, scale, causal != 0, false, 1};
+  const ra::FwdStepArgs a{reinterpret_cast<const uint16_t*>(ws), reinterpret_cast<const uint16_t*>(ws + part),
+                          reinterpret_cast<const uint16_t*>(ws + 2 * part), o, lse, B * Hs, S, S, d, scale,
+                          causal != 0, false, 1};
   const hipError_t e = fwd_step(a, cs);
   if (e != hipSuccess) return hip_fail(e, "ra_ulysses_fwd attention");
+  return ok();
+}
+
+int ra_ulysses_bwd(const void* const* q_chunks, const void* const* k_chunks, const void* const* v_chunks,
+                   const void* const* dO_chunks, int P, const float* o, const float* lse, float* dq, float* dk,
+                   float* dv, int rank, int causal, float scale, int B, int H, int C, int d, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!q_chunks || !k_chunks || !v_chunks || !dO_chunks || !o || !lse || !dq || !dk || !dv)
+    return fail(RA_ERR_NULL, "ra_ulysses_bwd: NULL pointer");
+  const void* const* sets[4] = {q_chunks, k_chunks, v_chunks, dO_chunks};
+  int st = ulysses_check(sets, 4, P, rank, B, H, C, d, "ra_ulysses_bwd");
+  if (st) return st;
+  if (!aligned16(o) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(RA_ERR_ALIGN, "ra_ulysses_bwd: device pointers must be 16-byte aligned");
+  const size_t need = ra_ulysses_workspace_bytes(P, B, H, C, d, 1);
+  if (!workspace || workspace_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "ra_ulysses_bwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  if (!aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_ulysses_bwd: workspace not 16-byte aligned");
+
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  const int Hs = H / P, S = P * C;
+  const int rows = B * Hs * S;
+  const size_t part = (size_t)rows * d * 2;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  for (int x = 0; x < 4; ++x) {
+    const hipError_t e = ulysses_regroup(sets[x], ws + x * part, P, rank, B, H, C, d, cs);
+    if (e != hipSuccess) return hip_fail(e, "ra_ulysses_bwd regroup");
+  }
+  const uint16_t* qr = reinterpret_cast<const uint16_t*>(ws);
+  const uint16_t* dOr = reinterpret_cast<const uint16_t*>(ws + 3 * part);
+  float* Dbuf = reinterpret_cast<float*>(ws + 4 * part);
+  float* lse2 = Dbuf + rows;
+  hipError_t e = traced(RA_TRACE_BWD_ROWDOT, cs, [&] { return ra::launch_bwd_rowdot(dOr, o, lse, Dbuf, lse2, rows, d, cs); });
+  for (float* g : {dq, dk, dv})
+    if (e == hipSuccess) e = traced(RA_TRACE_BWD_ZERO, cs, [&] { return ra::launch_zero_f32(g, (size_t)rows * d, cs); });
+  if (e != hipSuccess) return hip_fail(e, "ra_ulysses_bwd preprocess");
+  // The whole sequence is one step: the diagonal (causal) or a full chunk.
+  const ra::BwdStepArgs a{qr, reinterpret_cast<const uint16_t*>(ws + part),
+                          reinterpret_cast<const uint16_t*>(ws + 2 * part), dOr, lse2, Dbuf, dq, dk, dv,
+                          B * Hs, S, S, d, scale, causal != 0, 1};
+  e = traced(causal ? RA_TRACE_BWD_DQ_DIAG : RA_TRACE_BWD_DQ_FULL, cs, [&] { return ra::launch_bwd_dq(a, cs); });
+  if (e == hipSuccess)
+    e = traced(causal ? RA_TRACE_BWD_DKDV_DIAG : RA_TRACE_BWD_DKDV_FULL, cs, [&] { return ra::launch_bwd_dkdv(a, cs); });
+  if (e != hipSuccess) return hip_fail(e, "ra_ulysses_bwd step");
   return ok();
 }
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ra_version() == 3  # 2: grouped-query (*_gqa) entry points; 3: ra_ulysses_fwd
+    assert L.ra_version() == 3  # 2: grouped-query (*_gqa) entry points; 3: ra_ulysses_fwd, ra_ulysses_bwd
     assert L.ra_status_string(RA_OK) == b"RA_OK"
     assert L.ra_status_string(RA_ERR_WORKSPACE) == b"RA_ERR_WORKSPACE"
     assert L.ra_status_string(12345) == b"RA_ERR_UNKNOWN"
@@ -145,11 +145,12 @@ def test_gqa_validation(L):
 
 
 def test_ulysses_workspace_and_validation(L):
-    assert L.ra_ulysses_workspace_bytes(4, 1, 32, 32768, 128) == 3 * 8 * 131072 * 128 * 2
-    assert L.ra_ulysses_workspace_bytes(3, 1, 32, 64, 128) == 0  # 32 heads do not split over 3
+    assert L.ra_ulysses_workspace_bytes(4, 1, 32, 32768, 128, 0) == 3 * 8 * 131072 * 128 * 2
+    assert L.ra_ulysses_workspace_bytes(4, 1, 32, 32768, 128, 1) == 4 * 8 * 131072 * 128 * 2 + 2 * 8 * 131072 * 4
+    assert L.ra_ulysses_workspace_bytes(3, 1, 32, 64, 128, 0) == 0  # 32 heads do not split over 3
     P, C, d = 4, 64, 128
     arr = (ctypes.c_void_p * P)(*([FAKE] * P))
-    need = L.ra_ulysses_workspace_bytes(P, 1, 8, C, d)
+    need = L.ra_ulysses_workspace_bytes(P, 1, 8, C, d, 0)
     call = lambda H=8, rank=1, ws=FAKE, wsb=need, chunks=arr: L.ra_ulysses_fwd(
         chunks, chunks, chunks, P, vp(FAKE), vp(FAKE), rank, 1, 0.1, 1, H, C, d, vp(ws), wsb, None)
     assert call(H=6) == RA_ERR_SHAPE
@@ -158,6 +159,14 @@ def test_ulysses_workspace_and_validation(L):
     assert call(wsb=need - 16) == RA_ERR_WORKSPACE
     assert call(chunks=(ctypes.c_void_p * P)(FAKE, FAKE, 0, FAKE)) == RA_ERR_NULL
     assert call(chunks=(ctypes.c_void_p * P)(FAKE, MIS, FAKE, FAKE)) == RA_ERR_ALIGN
+    need_b = L.ra_ulysses_workspace_bytes(P, 1, 8, C, d, 1)
+    bwd = lambda H=8, rank=1, wsb=need_b, dO=arr: L.ra_ulysses_bwd(
+        arr, arr, arr, dO, P, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), rank, 1, 0.1, 1, H, C, d,
+        vp(FAKE), wsb, None)
+    assert bwd(H=6) == RA_ERR_SHAPE
+    assert bwd(rank=-1) == RA_ERR_RANK
+    assert bwd(wsb=need_b - 16) == RA_ERR_WORKSPACE
+    assert bwd(dO=(ctypes.c_void_p * P)(FAKE, FAKE, FAKE, 0)) == RA_ERR_NULL
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -310,3 +310,26 @@ def test_ulysses_share_every_rank(P, C, H, d, causal):
         ro, rl = ulysses_share([f64(t) for t in qc], [f64(t) for t in k], [f64(t) for t in v], rank, causal, scale)
         assert_close(f64(o), ro, TOL_O, f"o rank {rank}")
         assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)
+
+
+@pytest.mark.parametrize("P,C,H,d,causal", [(2, 100, 4, 128, True), (4, 37, 8, 64, True), (3, 129, 3, 128, False)])
+def test_ulysses_bwd_every_rank(P, C, H, d, causal):
+    from oracle.ulysses import ulysses_gather
+    q, k, v, do = ring_tensors(112, 1, H, P, C, d, with_do=True)
+    qc, dc = [q[r] for r in range(P)], [do[r] for r in range(P)]
+    qd, kd, vd, dd = ([t.to(dev()) for t in x] for x in (qc, k, v, dc))
+    scale = 1 / math.sqrt(d)
+    Hs, S = H // P, P * C
+    for rank in range(P):
+        print(f"ulysses bwd P={P} C={C} H={H} d={d} causal={causal} rank={rank}", flush=True)
+        o = torch.empty(1, Hs, S, d, device=dev())
+        lse = torch.empty(1, Hs, S, device=dev())
+        ra.ulysses_fwd(qd, kd, vd, o, lse, rank, causal, scale)
+        dq, dk, dv = (torch.full((1, Hs, S, d), float("nan"), device=dev()) for _ in range(3))
+        ra.ulysses_bwd(qd, kd, vd, dd, o, lse, dq, dk, dv, rank, causal, scale)
+        torch.cuda.synchronize()
+        g = lambda cs: ulysses_gather([f64(t) for t in cs], rank)
+        rq, rk, rv = oracle.attention_bwd(g(qc), g(k), g(v), g(dc), scale, causal)
+        assert_close(f64(dq), rq, TOL_GRAD, "dq")
+        assert_close(f64(dk), rk, TOL_GRAD, "dk")
+        assert_close(f64(dv), rv, TOL_GRAD, "dv")

@@ -13,7 +13,9 @@ stream).
   every key the sums that hold exactly: sum_k dK_k = 0 and
   sum_k dV_k = sum_q dO_q.
 * Head-partitioned (Ulysses) share of the 128K/CP=4 sequence: ranks 0 and 3,
-  H/4 = 8 heads over all 131072 tokens, 256 sampled rows per head.
+  H/4 = 8 heads over all 131072 tokens, 256 sampled rows per head; its
+  backward: dQ on 256 sampled rows per head and the gradient sums on every
+  key.
 * Grouped-query attention (key/value chunks of H/4 heads): the 128K/CP=4
   share on sampled rows, and the training share's dQ on sampled rows, dK/dV
   (summed over each group's query heads) on sampled key rows of two
@@ -449,3 +451,42 @@ def test_ulysses_share_128k_sampled_rows():
         del o, lse
     del qd, kd, vd
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_ulysses_bwd_128k_sampled_rows_and_sums():
+    from oracle.ulysses import ulysses_gather
+    w = WORKLOADS[2]
+    P, C = w.P, w.C
+    S, Hs, rank = P * C, w.H // P, 1
+    say(f"{w.name}: Ulysses backward inputs (every chunk)")
+    q, k, v, do = gen_workload(w, ranks=range(P), with_do=True)
+    qc, dc = [q[r] for r in range(P)], [do[r] for r in range(P)]
+    qd, kd, vd, dd = ([t.to(dev()) for t in x] for x in (qc, k, v, dc))
+    o = torch.empty(w.B, Hs, S, w.d, device=dev())
+    lse = torch.empty(w.B, Hs, S, device=dev())
+    ra.ulysses_fwd(qd, kd, vd, o, lse, rank, w.causal, w.scale)
+    dq, dk, dv = (torch.full((w.B, Hs, S, w.d), float("nan"), device=dev()) for _ in range(3))
+    say(f"{w.name}: Ulysses backward of rank {rank} ({Hs} heads x {S} tokens)")
+    ra.ulysses_bwd(qd, kd, vd, dd, o, lse, dq, dk, dv, rank, w.causal, w.scale)
+    torch.cuda.synchronize()
+    dq_c, dk_c, dv_c = dq.cpu(), dk.double().cpu(), dv.double().cpu()
+    del qd, kd, vd, dd, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    gq, gk, gv, gd = (ulysses_gather([f64(t) for t in cs], rank) for cs in (qc, k, v, dc))
+
+    def one(i):
+        rows = inputs.query_row_sample(w.id, rank * Hs + i, S)
+        rq, _, _ = oracle.attention_bwd(gq[:, i:i + 1, rows], gk[:, i:i + 1], gv[:, i:i + 1], gd[:, i:i + 1, rows],
+                                        w.scale, w.causal, q_pos=rows)
+        got = f64(dq_c[:, i:i + 1, rows])
+        return np.abs(got - rq).max(), np.linalg.norm(got - rq) ** 2, np.linalg.norm(rq) ** 2
+
+    res = fan_out(one, range(Hs))
+    e_q = max(x[0] for x in res)
+    rel = math.sqrt(sum(x[1] for x in res) / sum(x[2] for x in res))
+    r_k = (dk_c.sum(dim=2).abs() / dk_c.abs().sum(dim=2).clamp_min(1e-30)).max().item()
+    sum_do = torch.from_numpy(gd).sum(dim=2)
+    r_v = ((dv_c.sum(dim=2) - sum_do).abs().max() / sum_do.abs().max()).item()
+    say(f"  max|ddQ|={e_q:.2e} rel={rel:.2e}  max|sum dK|/sum|dK|={r_k:.2e}  sum dV vs sum dO={r_v:.2e}")
+    assert e_q <= TOL_GRAD and rel <= TOL_REL and r_k <= 1e-3 and r_v <= 1e-3
