@@ -245,12 +245,30 @@ def run_ulysses(w, steps, warmup, rank=0):
     pairs = B * Hs * (S * (S + 1) // 2 if w.causal else S * S)
     flops = 4 * d * pairs
     k_ms = sum(m for _, m in rec) / max(1, len(rec))
-    return {
+    out = {
         "rank": rank, "heads": Hs, "tokens": S, "ms_per_step": round(secs / steps * 1e3, 4),
         "tflops": round(flops * steps / secs / 1e12, 2),
         "attention_kernel_ms": round(k_ms, 4), "attention_kernel_tflops": round(flops / (k_ms * 1e-3) / 1e12, 2),
         "regroup_bytes_per_step": 2 * 3 * B * Hs * S * d * 2,
     }
+    # Training step of the share: forward + backward (10*d flop per pair backward).
+    dc = [inputs.chunk(w.id, inputs.DO, j, B, H, C, d).to(dev) for j in range(P)]
+    dq, dk, dv = (torch.empty(B, Hs, S, d, device=dev) for _ in range(3))
+    ws_b = torch.empty(ra.ulysses_workspace_bytes(P, B, H, C, d, bwd=True), dtype=torch.uint8, device=dev)
+
+    def train_step():
+        ra.ulysses_fwd(qc, kc, vc, o, lse, rank, w.causal, w.scale, workspace=ws)
+        ra.ulysses_bwd(qc, kc, vc, dc, o, lse, dq, dk, dv, rank, w.causal, w.scale, workspace=ws_b)
+
+    n_launch = 1 + 1 + 3 + 2
+    t_secs, t_rec = timed_steps(train_step, n_launch, max(2, steps // 2), 1)
+    t_steps = max(2, steps // 2)
+    bwd_ms = sum(m for k_, m in t_rec if k_.startswith("bwd")) / t_steps
+    out["train_ms_per_step"] = round(t_secs / t_steps * 1e3, 4)
+    out["train_tflops_fwd_bwd"] = round(14 * d * pairs * t_steps / t_secs / 1e12, 2)
+    out["bwd_kernels_ms"] = round(bwd_ms, 4)
+    out["bwd_tflops_kernels_algorithmic"] = round(10 * d * pairs / (bwd_ms * 1e-3) / 1e12, 1)
+    return out
 
 
 def cpu_baseline(w, tensors, budget_s):
