@@ -337,7 +337,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the ring on a single MI355X; multi-GPU runs "
-              "(--gpus > 1) are not part of this build.", file=sys.stderr)
+              "(--gpus > 1) are not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch

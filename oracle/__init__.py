@@ -21,8 +21,9 @@ What it computes, and the passage each function follows:
   head's gradient over its group.  Pinned against the library's attention
   with grouped heads, forward and autograd.
 * ``attention.attention_bwd`` / ``attention_bwd_key_rows`` -- the textbook
-  gradient of softmax attention.  The pages give no backward formula; the
-  reading (recompute P from the final log-sum-exp) is listed in the design doc.
+  gradient of softmax attention.  The pages give no backward formula; this
+  is the plain one, with P recomputed from the final log-sum-exp of each
+  query row.
 * ``attention.lse_merge`` / ``ring_fwd_chunked`` -- the online-softmax merge of
   partial results ("Training Long-Context Models Without OOM: Ring
   Attention", "Ring Attention Demystified", paragraph on running softmax
