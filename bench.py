@@ -366,6 +366,8 @@ def main():
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+        # HBM bytes per launch (counters) over the live launch time: achieved HBM bandwidth.
+        "traffic_gbps": None if traffic is None else round(traffic / (dk["avg_ms"] * 1e-3) / 1e9, 1),
         "kernel": f"fwd_step_kernel ({dom}), {dk['launches']} launches, avg {dk['avg_ms']} ms",
         "flops_per_launch": dom_flops,
     }
