@@ -36,6 +36,13 @@ What it computes, and the passage each function follows:
   whole sequence, and the regrouping back ("Context Parallelism", 3 "Ulysses
   (DeepSpeed)", steps 1-4).  Pinned against the library's attention and
   against the ring walk (``tests/test_oracle_ulysses.py``).
+* ``allgather.allgather_share_fwd`` / ``allgather_share_bwd`` /
+  ``allgather_kv`` -- one rank's share of all-gather sequence parallelism:
+  the key/value chunks gathered in index order, then exact attention of the
+  rank's query chunk (at its global positions) over them, and its gradient
+  (the page on sequence parallelism for 1M-token training, "How Sequence
+  Parallelism Works").  Pinned against the library's attention, its
+  autograd and the ring walk (``tests/test_oracle_allgather.py``).
 * ``schedule.ring_schedule`` -- which KV chunk a rank uses at each step
   ("Context Parallelism", 2 "How It Works": step s uses K_{i-s}, V_{i-s};
   "Training Long-Context Models Without OOM", "Ring Attention Demystified",
