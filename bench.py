@@ -13,7 +13,10 @@ rank 3, H = 32, d = 128, causal), one step = forward walk + backward walk.
 And (unless --no-gqa): both walks again with grouped-query key/value chunks of
 H/4 heads (4 query heads per key/value head), under "gqa".  And (unless
 --no-ulysses): one rank's share of head-partitioned (Ulysses) sequence
-parallelism on the same sequence, under "ulysses".
+parallelism on the same sequence, under "ulysses".  And (unless
+--no-allgather): the same rank's share of all-gather sequence parallelism
+(gathered key/value chunks, one pass at a causal offset), forward and
+training step, under "allgather".
 
 Prints ONE JSON line: throughput in algorithmic TFLOP/s (4*d flops per
 visible (query, key) pair forward, 10*d backward), tokens/s, the roofline of
@@ -271,6 +274,76 @@ def run_ulysses(w, steps, warmup, rank=0):
     return out
 
 
+def run_allgather(w, steps, warmup, wt):
+    """One rank's share of all-gather sequence parallelism: copy the P key/value
+    chunks into one gathered sequence (the copies stand in for the all-gather),
+    then one attention pass of the rank's queries over it at a causal offset.
+    Forward on workload w's rank, training step (forward + backward) on
+    workload wt's rank."""
+    import torch
+    import long_context_exact_step_amd as ra
+    from long_context_exact_step_amd import inputs
+    from long_context_exact_step_amd.workloads import bwd_flops, fwd_flops
+
+    dev = torch.device("cuda", 0)
+
+    def tensors(x, with_do):
+        B, H, C, d, P = x.B, x.H, x.C, x.d, x.P
+        r = x.ranks[0]
+        q = inputs.chunk(x.id, inputs.Q, r, B, H, C, d).to(dev)
+        ks = [inputs.chunk(x.id, inputs.K, j, B, H, C, d).to(dev) for j in range(P)]
+        vs = [inputs.chunk(x.id, inputs.V, j, B, H, C, d).to(dev) for j in range(P)]
+        do = inputs.chunk(x.id, inputs.DO, r, B, H, C, d).to(dev) if with_do else None
+        return r, q, ks, vs, do, torch.empty(B, H, C, d, device=dev), torch.empty(B, H, C, device=dev)
+
+    r, q, ks, vs, _, o, lse = tensors(w, False)
+    ws = torch.empty(ra.allgather_workspace_bytes(w.P, w.B, w.H, w.C, w.d), dtype=torch.uint8, device=dev)
+
+    def step():
+        ra.allgather_fwd(q, ks, vs, o, lse, r, w.causal, w.scale, workspace=ws)
+
+    secs, rec = timed_steps(step, 1, steps, warmup)
+    flops = fwd_flops(w, [r])
+    k_ms = sum(m for _, m in rec) / max(1, len(rec))
+    out = {
+        "rank": r, "ms_per_step": round(secs / steps * 1e3, 4), "tflops": round(flops * steps / secs / 1e12, 2),
+        "tokens_per_s": round(w.B * w.C * steps / secs, 1),
+        "attention_kernel_ms": round(k_ms, 4), "attention_kernel_tflops": round(flops / (k_ms * 1e-3) / 1e12, 2),
+        "gather_bytes_per_step": 2 * 2 * w.B * w.H * w.P * w.C * w.d * 2,
+    }
+    del q, ks, vs, o, lse, ws
+    torch.cuda.empty_cache()
+
+    r, q, ks, vs, do, o, lse = tensors(wt, True)
+    S = wt.P * wt.C
+    dq = torch.empty(wt.B, wt.H, wt.C, wt.d, device=dev)
+    dk, dv = (torch.empty(wt.B, wt.H, S, wt.d, device=dev) for _ in range(2))
+    ws_f = torch.empty(ra.allgather_workspace_bytes(wt.P, wt.B, wt.H, wt.C, wt.d), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(ra.allgather_workspace_bytes(wt.P, wt.B, wt.H, wt.C, wt.d, bwd=True), dtype=torch.uint8,
+                       device=dev)
+
+    def train_step():
+        ra.allgather_fwd(q, ks, vs, o, lse, r, wt.causal, wt.scale, workspace=ws_f)
+        ra.allgather_bwd(q, ks, vs, o, lse, do, dq, dk, dv, r, wt.causal, wt.scale, workspace=ws_b)
+
+    t_steps = max(2, steps)
+    # Launches per step: attention; rowdot, three fills, the dq kernel, the dk/dv pair.
+    t_secs, t_rec = timed_steps(train_step, 7, t_steps, 1)
+    fl_f, fl_b = fwd_flops(wt, [r]), bwd_flops(wt, [r])
+    fwd_ms = sum(m for k_, m in t_rec if k_.startswith("fwd")) / t_steps
+    bwd_ms = sum(m for k_, m in t_rec if k_.startswith("bwd")) / t_steps
+    out["train"] = {
+        "workload": wt.name, "rank": r, "steps": t_steps, "ms_per_step": round(t_secs / t_steps * 1e3, 4),
+        "tflops_fwd_bwd": round((fl_f + fl_b) * t_steps / t_secs / 1e12, 2),
+        "tokens_per_s": round(wt.B * wt.C * t_steps / t_secs, 1),
+        "fwd_kernels_ms_per_step": round(fwd_ms, 3), "bwd_kernels_ms_per_step": round(bwd_ms, 3),
+        "bwd_tflops_kernels_algorithmic": round(fl_b / (bwd_ms * 1e-3) / 1e12, 1),
+    }
+    del q, ks, vs, do, o, lse, dq, dk, dv, ws_f, ws_b
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, tensors, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample: 256 seeded query
     rows per head of the measured rank, heads taken in order until the time
@@ -333,6 +406,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query (H_kv = H/4) measurements")
     ap.add_argument("--no-ulysses", action="store_true", help="skip the head-partitioned (Ulysses) share")
+    ap.add_argument("--no-allgather", action="store_true", help="skip the all-gather sequence-parallel share")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -422,6 +496,13 @@ def main():
         out["ulysses"] = u
         print(f"[bench] ulysses share ({u['heads']} heads x {u['tokens']} tokens): {u['ms_per_step']:.3f} ms/step, "
               f"{u['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if not args.no_allgather:
+        torch.cuda.empty_cache()
+        a = run_allgather(w, args.steps, args.warmup, WORKLOADS[5])
+        a["ring_rank_ms_per_step"] = out["ms_per_step"]
+        out["allgather"] = a
+        print(f"[bench] all-gather share rank {a['rank']}: {a['ms_per_step']:.3f} ms/step, {a['tflops']:.1f} TFLOP/s; "
+              f"train {a['train']['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
     print(json.dumps(out))
 
 

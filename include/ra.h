@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define RA_VERSION 3
+#define RA_VERSION 4
 
 enum ra_status {
   RA_OK = 0,
@@ -266,13 +266,62 @@ int ra_ulysses_bwd(const void* const* q_chunks, const void* const* k_chunks,
                    size_t workspace_bytes, void* stream);
 
 /*
+ * ra_allgather_fwd -- one GPU's share of all-gather sequence parallelism,
+ * forward (the page on sequence parallelism for 1M-token training, "How
+ * Sequence Parallelism Works"; set beside Ulysses and Ring Attention in its
+ * "SP Methods: Head-to-Head Comparison" table).  Every rank holds the
+ * contiguous chunk `rank` of a sequence of S = P*C tokens; an all-gather
+ * gives every rank all P key/value chunks, and the rank computes exact
+ * attention of its own query chunk over the gathered sequence in one pass.
+ * On one GPU the all-gather is emulated by 2D device copies of the P chunks
+ * into the workspace (gathered [B,H_kv,S,d], chunk j at tokens
+ * [j*C, (j+1)*C)); there is no ring walk and no merge.
+ *   q: [B,H,C,d] bf16, the rank's queries; k_chunks / v_chunks: HOST arrays
+ *   of P device pointers to [B,H_kv,C,d] bf16 (every chunk is gathered, as
+ *   the collective would; under causal masking the kernels read only chunks
+ *   0..rank).  Causal: local query t sits at global position rank*C + t and
+ *   sees keys <= rank*C + t.  o [B,H,C,d], lse [B,H,C] fp32 are overwritten
+ *   (same meaning as ra_ring_fwd's).  H_kv must divide H (grouped-query
+ *   attention as for the *_gqa calls).  Needs
+ *   ra_allgather_workspace_bytes(P,B,H,H_kv,C,d,0) bytes of 16-byte-aligned
+ *   workspace (RA_ERR_WORKSPACE); NULL chunk pointers give RA_ERR_NULL.
+ *   Other contracts as for ra_ring_fwd.
+ *
+ * ra_allgather_bwd -- the same share's backward (the softmax-attention
+ * gradient with P recomputed from the final lse, as ra_ring_bwd).  o, lse
+ * are ra_allgather_fwd's outputs, dO [B,H,C,d] bf16.  dq [B,H,C,d] fp32 and
+ * dk, dv [B,H_kv,S,d] fp32 are overwritten: dk, dv hold the gradient of the
+ * whole gathered sequence from this rank's queries (zero for keys no local
+ * query sees); summing them over ranks and handing each owner its slice is
+ * the reduce-scatter a multi-GPU run would do.  Workspace:
+ * ra_allgather_workspace_bytes(P,B,H,H_kv,C,d,1) bytes.
+ *
+ * ra_allgather_workspace_bytes: bwd == 0: gathered K and V,
+ * 2 * B*H_kv*P*C*d * 2 bytes; bwd != 0: those and two fp32 values per local
+ * query row, + 2 * B*H*C * 4 bytes.  0 for invalid sizes.
+ */
+size_t ra_allgather_workspace_bytes(int P, int B, int H, int H_kv, int C, int d, int bwd);
+int ra_allgather_fwd(const void* q, const void* const* k_chunks,
+                     const void* const* v_chunks, int P, float* o, float* lse,
+                     int rank, int causal, float scale, int B, int H, int H_kv,
+                     int C, int d, void* workspace, size_t workspace_bytes,
+                     void* stream);
+int ra_allgather_bwd(const void* q, const void* const* k_chunks,
+                     const void* const* v_chunks, int P, const float* o,
+                     const float* lse, const void* dO, float* dq, float* dk,
+                     float* dv, int rank, int causal, float scale, int B,
+                     int H, int H_kv, int C, int d, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * Per-launch tracing, for profiling.  The pages define no such facility; it
  * exists so that a caller can time each kernel of a ring walk with its own
  * events, on the stream the kernel runs on.
  *
  * ra_trace_begin arms tracing on the calling thread.  Every kernel that
  * ra_step_fwd, ra_lse_merge, ra_ring_fwd, ra_ring_bwd (or their *_gqa
- * forms), ra_ulysses_fwd or ra_ulysses_bwd then launch on their
+ * forms), ra_ulysses_fwd, ra_ulysses_bwd, ra_allgather_fwd or
+ * ra_allgather_bwd then launch on their
  * compute stream is bracketed by hipEventRecord(start_events[n], stream)
  * and hipEventRecord(end_events[n], stream), and kinds[n] receives its
  * RA_TRACE_* kind, for the n-th such launch while n < capacity (later
@@ -284,14 +333,14 @@ int ra_ulysses_bwd(const void* const* q_chunks, const void* const* k_chunks,
  * and RA_ERR_SHAPE for capacity < 0.
  */
 enum ra_trace_kind {
-  RA_TRACE_FWD_DIAG = 1,       /* forward step, diagonal (masked) chunk */
+  RA_TRACE_FWD_DIAG = 1,       /* forward, causal-masked (diagonal chunk, or causal offset) */
   RA_TRACE_FWD_FULL = 2,       /* forward step, fully visible chunk */
   RA_TRACE_MERGE = 3,          /* standalone lse merge */
   RA_TRACE_BWD_ROWDOT = 4,     /* backward: D = rowsum(dO * o) */
-  RA_TRACE_BWD_ZERO = 5,       /* backward: dq <- 0 */
-  RA_TRACE_BWD_DQ_DIAG = 6,    /* backward dq kernel, diagonal chunk */
+  RA_TRACE_BWD_ZERO = 5,       /* backward: dq (and dk, dv where overwritten) <- 0 */
+  RA_TRACE_BWD_DQ_DIAG = 6,    /* backward dq kernel, causal-masked */
   RA_TRACE_BWD_DQ_FULL = 7,    /* backward dq kernel, full chunk */
-  RA_TRACE_BWD_DKDV_DIAG = 8,  /* backward dk/dv kernel, diagonal chunk */
+  RA_TRACE_BWD_DKDV_DIAG = 8,  /* backward dk/dv kernel, causal-masked */
   RA_TRACE_BWD_DKDV_FULL = 9   /* backward dk/dv kernel, full chunk */
 };
 int ra_trace_begin(void* const* start_events, void* const* end_events, int* kinds, int capacity);

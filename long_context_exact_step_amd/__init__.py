@@ -17,6 +17,7 @@ __all__ = [
     "RAError", "lib", "version", "step_fwd", "lse_merge", "ring_fwd", "ring_bwd",
     "workspace_bytes", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH", "trace_begin", "trace_end",
     "ulysses_fwd", "ulysses_bwd", "ulysses_workspace_bytes",
+    "allgather_fwd", "allgather_bwd", "allgather_workspace_bytes",
     "TRACE_KINDS",
 ]
 
@@ -80,6 +81,12 @@ def lib():
         L.ra_ulysses_bwd.restype = i
         L.ra_ulysses_bwd.argtypes = [vpp, vpp, vpp, vpp, i, vp, vp, vp, vp, vp, i, i, f, i, i, i, i, vp, sz, vp]
         L.ra_ulysses_fwd.restype = i
+        L.ra_allgather_workspace_bytes.restype = sz
+        L.ra_allgather_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.ra_allgather_fwd.restype = i
+        L.ra_allgather_fwd.argtypes = [vp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, i, vp, sz, vp]
+        L.ra_allgather_bwd.restype = i
+        L.ra_allgather_bwd.argtypes = [vp, vpp, vpp, i, vp, vp, vp, vp, vp, vp, i, i, f, i, i, i, i, i, vp, sz, vp]
         L.ra_ulysses_fwd.argtypes = [vpp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, vp, sz, vp]
         L.ra_trace_begin.restype = i
         L.ra_trace_begin.argtypes = [vpp, vpp, ctypes.POINTER(ctypes.c_int), i]
@@ -111,6 +118,11 @@ def _stream(stream, like):
     if stream is None:
         stream = torch.cuda.current_stream(like.device)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def _need(t, dtype, name):
@@ -275,6 +287,67 @@ def ulysses_bwd(q_chunks, k_chunks, v_chunks, dO_chunks, o, lse, dq, dk, dv, ran
                                 _ptr_array(dO_chunks), P, _ptr(o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                 int(rank), int(bool(causal)), scale, B, H, C, d, _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream, o)))
+    return workspace
+
+
+def allgather_workspace_bytes(P, B, H, C, d, H_kv=None, bwd=False):
+    return int(lib().ra_allgather_workspace_bytes(P, B, H, H if H_kv is None else H_kv, C, d, int(bool(bwd))))
+
+
+def allgather_fwd(q, k_chunks, v_chunks, o, lse, rank, causal, scale=None, workspace=None, stream=None):
+    """ra_allgather_fwd: one rank's share of all-gather sequence parallelism.
+    q [B,H,C,d] bf16 (the rank's chunk); k/v_chunks: P tensors [B,H_kv,C,d]
+    bf16; o [B,H,C,d], lse [B,H,C] fp32 receive attention over the gathered
+    sequence."""
+    import torch
+    _need(q, torch.bfloat16, "q")
+    for n, t in enumerate(list(k_chunks) + list(v_chunks)):
+        _need(t, torch.bfloat16, f"chunk{n}")
+    _need(o, torch.float32, "o")
+    _need(lse, torch.float32, "lse")
+    B, H, C, d = q.shape
+    Hk, P = k_chunks[0].shape[1], len(k_chunks)
+    _shape(o, (B, H, C, d), "o"); _shape(lse, (B, H, C), "lse")
+    for n, t in enumerate(list(k_chunks) + list(v_chunks)):
+        _shape(t, (B, Hk, C, d), f"chunk{n}")
+    need = allgather_workspace_bytes(P, B, H, C, d, H_kv=Hk)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().ra_allgather_fwd(_ptr(q), _ptr_array(k_chunks), _ptr_array(v_chunks), P, _ptr(o), _ptr(lse),
+                                  int(rank), int(bool(causal)), scale, B, H, Hk, C, d, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream, q)))
+    return workspace
+
+
+def allgather_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk, dv, rank, causal, scale=None, workspace=None,
+                  stream=None):
+    """ra_allgather_bwd: the all-gather share's backward.  o, lse from
+    allgather_fwd; dq [B,H,C,d] and dk, dv [B,H_kv,P*C,d] fp32 are
+    overwritten (dk, dv: the gathered sequence's gradient from this rank)."""
+    import torch
+    _need(q, torch.bfloat16, "q"); _need(dO, torch.bfloat16, "dO")
+    for n, t in enumerate(list(k_chunks) + list(v_chunks)):
+        _need(t, torch.bfloat16, f"chunk{n}")
+    for t, n in ((o, "o"), (lse, "lse"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, torch.float32, n)
+    B, H, C, d = q.shape
+    Hk, P = k_chunks[0].shape[1], len(k_chunks)
+    for t, n in ((o, "o"), (dO, "dO"), (dq, "dq")):
+        _shape(t, (B, H, C, d), n)
+    _shape(lse, (B, H, C), "lse")
+    for t, n in ((dk, "dk"), (dv, "dv")):
+        _shape(t, (B, Hk, P * C, d), n)
+    for n, t in enumerate(list(k_chunks) + list(v_chunks)):
+        _shape(t, (B, Hk, C, d), f"chunk{n}")
+    need = allgather_workspace_bytes(P, B, H, C, d, H_kv=Hk, bwd=True)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().ra_allgather_bwd(_ptr(q), _ptr_array(k_chunks), _ptr_array(v_chunks), P, _ptr(o), _ptr(lse),
+                                  _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), int(rank), int(bool(causal)), scale,
+                                  B, H, Hk, C, d, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream, q)))
     return workspace
 
 

@@ -150,6 +150,38 @@ hipError_t ulysses_regroup(const void* const* chunks, uint8_t* dst0, int P, int 
   return hipSuccess;
 }
 
+// The all-gather of one tensor, emulated: chunks[j] ([B, Hk, C, d] bf16) to
+// its place in the gathered [B, Hk, P*C, d] sequence, one 2D copy per chunk.
+hipError_t allgather_copy(const void* const* chunks, uint8_t* dst0, int P, int B, int Hk, int C, int d,
+                          hipStream_t s) {
+  const size_t S = (size_t)P * C, tok = (size_t)d * 2;
+  for (int j = 0; j < P; ++j) {
+    const hipError_t e = hipMemcpy2DAsync(dst0 + (size_t)j * C * tok, S * tok, chunks[j], C * tok, C * tok,
+                                          (size_t)B * Hk, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Validation shared by the two all-gather entry points.
+int allgather_check(const void* const* k_chunks, const void* const* v_chunks, int P, int rank, int B, int H,
+                    int H_kv, int C, int d, const char* what) {
+  if (P < 1) return fail(RA_ERR_SHAPE, "%s: P=%d < 1", what, P);
+  int st = check_dims(B, H, C, d, what);
+  if (st) return st;
+  st = check_groups(H, H_kv, what);
+  if (st) return st;
+  if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "%s: rank=%d outside [0, %d)", what, rank, P);
+  if ((long long)B * H_kv * P * C > 0x7fffffffLL || (long long)P * C + 1024 > 0x3fffffffLL)
+    return fail(RA_ERR_SHAPE, "%s: gathered sequence B*H_kv*P*C too large", what);
+  for (int j = 0; j < P; ++j) {
+    if (!k_chunks[j] || !v_chunks[j]) return fail(RA_ERR_NULL, "%s: chunk %d pointer is NULL", what, j);
+    if (!aligned16(k_chunks[j]) || !aligned16(v_chunks[j]))
+      return fail(RA_ERR_ALIGN, "%s: chunk %d pointer not 16-byte aligned", what, j);
+  }
+  return RA_OK;
+}
+
 // Validation shared by the two head-partitioned entry points.
 int ulysses_check(const void* const* const* chunk_sets, int n_sets, int P, int rank, int B, int H, int C, int d,
                   const char* what) {
@@ -501,6 +533,88 @@ int ra_ulysses_bwd(const void* const* q_chunks, const void* const* k_chunks, con
   if (e == hipSuccess)
     e = traced(causal ? RA_TRACE_BWD_DKDV_DIAG : RA_TRACE_BWD_DKDV_FULL, cs, [&] { return ra::launch_bwd_dkdv(a, cs); });
   if (e != hipSuccess) return hip_fail(e, "ra_ulysses_bwd step");
+  return ok();
+}
+
+size_t ra_allgather_workspace_bytes(int P, int B, int H, int H_kv, int C, int d, int bwd) {
+  if (P < 1 || B < 1 || H < 1 || H_kv < 1 || H % H_kv || C < 1 || (d != 64 && d != 128)) return 0;
+  const size_t kv = 2 * (size_t)B * H_kv * ((size_t)P * C) * d * 2;  // gathered K and V (bf16)
+  if (bwd) return kv + 2 * (size_t)B * H * C * sizeof(float);       // and D, lse2 per local row
+  return kv;
+}
+
+int ra_allgather_fwd(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, float* o,
+                     float* lse, int rank, int causal, float scale, int B, int H, int H_kv, int C, int d,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_chunks || !v_chunks || !o || !lse) return fail(RA_ERR_NULL, "ra_allgather_fwd: NULL pointer");
+  int st = allgather_check(k_chunks, v_chunks, P, rank, B, H, H_kv, C, d, "ra_allgather_fwd");
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(lse))
+    return fail(RA_ERR_ALIGN, "ra_allgather_fwd: device pointers must be 16-byte aligned");
+  const size_t need = ra_allgather_workspace_bytes(P, B, H, H_kv, C, d, 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "ra_allgather_fwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  if (!aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_allgather_fwd: workspace not 16-byte aligned");
+
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  const int S = P * C;
+  const size_t part = (size_t)B * H_kv * S * d * 2;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t e = allgather_copy(k_chunks, ws, P, B, H_kv, C, d, cs);
+  if (e == hipSuccess) e = allgather_copy(v_chunks, ws + part, P, B, H_kv, C, d, cs);
+  if (e != hipSuccess) return hip_fail(e, "ra_allgather_fwd gather");
+  // One pass of the local queries over the gathered sequence; causal: query
+  // t sits at global position rank*C + t.
+  ra::FwdStepArgs a{static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(ws),
+                    reinterpret_cast<const uint16_t*>(ws + part), o, lse, B * H, C, S, d, scale, causal != 0, false,
+                    H / H_kv, causal ? rank * C : 0};
+  e = fwd_step(a, cs);
+  if (e != hipSuccess) return hip_fail(e, "ra_allgather_fwd attention");
+  return ok();
+}
+
+int ra_allgather_bwd(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,
+                     const float* lse, const void* dO, float* dq, float* dk, float* dv, int rank, int causal,
+                     float scale, int B, int H, int H_kv, int C, int d, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!q || !k_chunks || !v_chunks || !o || !lse || !dO || !dq || !dk || !dv)
+    return fail(RA_ERR_NULL, "ra_allgather_bwd: NULL pointer");
+  int st = allgather_check(k_chunks, v_chunks, P, rank, B, H, H_kv, C, d, "ra_allgather_bwd");
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return fail(RA_ERR_ALIGN, "ra_allgather_bwd: device pointers must be 16-byte aligned");
+  const size_t need = ra_allgather_workspace_bytes(P, B, H, H_kv, C, d, 1);
+  if (!workspace || workspace_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "ra_allgather_bwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  if (!aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_allgather_bwd: workspace not 16-byte aligned");
+
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  const int S = P * C, rows = B * H * C;
+  const size_t part = (size_t)B * H_kv * S * d * 2;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* Dbuf = reinterpret_cast<float*>(ws + 2 * part);
+  float* lse2 = Dbuf + rows;
+  hipError_t e = allgather_copy(k_chunks, ws, P, B, H_kv, C, d, cs);
+  if (e == hipSuccess) e = allgather_copy(v_chunks, ws + part, P, B, H_kv, C, d, cs);
+  if (e != hipSuccess) return hip_fail(e, "ra_allgather_bwd gather");
+  e = traced(RA_TRACE_BWD_ROWDOT, cs, [&] {
+    return ra::launch_bwd_rowdot(static_cast<const uint16_t*>(dO), o, lse, Dbuf, lse2, rows, d, cs);
+  });
+  if (e == hipSuccess) e = traced(RA_TRACE_BWD_ZERO, cs, [&] { return ra::launch_zero_f32(dq, (size_t)rows * d, cs); });
+  for (float* g : {dk, dv})
+    if (e == hipSuccess)
+      e = traced(RA_TRACE_BWD_ZERO, cs, [&] { return ra::launch_zero_f32(g, (size_t)B * H_kv * S * d, cs); });
+  if (e != hipSuccess) return hip_fail(e, "ra_allgather_bwd preprocess");
+  const ra::BwdStepArgs a{static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(ws),
+                          reinterpret_cast<const uint16_t*>(ws + part), static_cast<const uint16_t*>(dO), lse2, Dbuf,
+                          dq, dk, dv, B * H, C, S, d, scale, causal != 0, H / H_kv, causal ? rank * C : 0};
+  e = traced(causal ? RA_TRACE_BWD_DQ_DIAG : RA_TRACE_BWD_DQ_FULL, cs, [&] { return ra::launch_bwd_dq(a, cs); });
+  if (e == hipSuccess)
+    e = traced(causal ? RA_TRACE_BWD_DKDV_DIAG : RA_TRACE_BWD_DKDV_FULL, cs, [&] { return ra::launch_bwd_dkdv(a, cs); });
+  if (e != hipSuccess) return hip_fail(e, "ra_allgather_bwd step");
   return ok();
 }
 

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lse2g, const float* __restrict__ Dg,
     float* __restrict__ dqg, int Sq, int Sk, int n_qtiles, int total_tiles, float scale_log2, float scale,
-    int group) {
+    int group, int qoff) {
   constexpr int NW = kDqWaves, NQW = kDqRowsPerWave, BR = NW * NQW, BC = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kDqLookahead;
   constexpr int NQ = 4 * NDB, NS = 2 * NKS * NKB, NOP = NQ + NS;  // dq ops, then S and dP ops
@@ -84,11 +84,12 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
   const uint16_t* __restrict__ kp = kg + (size_t)(bh / group) * Sk * D;
   const uint16_t* __restrict__ vp = vg + (size_t)(bh / group) * Sk * D;
 
+  // Causal: query row q sees keys k <= q + qoff.
   int kend = Sk;
-  if (DIAG) kend = min(kend, q0 + BR);
+  if (DIAG) kend = min(kend, q0 + BR + qoff);
   const int ntiles = (kend + BC - 1) / BC;
-  const int wtiles = DIAG ? min(ntiles, max(0, (min(qw0 + NQW, Sq) - 1) / BC + 1)) : ntiles;
-  const int lim = DIAG ? min(Sk, qq + 1) : Sk;  // keys at or past lim are masked
+  const int wtiles = DIAG ? min(ntiles, max(0, (min(qw0 + NQW, Sq) - 1 + qoff) / BC + 1)) : ntiles;
+  const int lim = DIAG ? min(Sk, qq + 1 + qoff) : Sk;  // keys at or past lim are masked
 
   TileBufDma<D, NW, BC> dma;
   dma.init(wave, lane);
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
     // Masked tiles (the diagonal band, the ragged tail) zero the entries of
     // keys at or past the lane's limit, whatever was computed for them, in a
     // pass of their own that full tiles skip.
-    if ((k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0)) {
+    if ((k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0 + qoff)) {
       const int r = lim - k0 - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lse2g, const float* __restrict__ Dg,
     float* __restrict__ outg, int Sq, int Sk, int n_ktiles, int total_tiles, float scale_log2, float scale,
-    int group) {
+    int group, int qoff) {
   constexpr int NW = kKvWaves, NKW = kKvKeysPerWave, BK = NW * NKW, BQ = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NQB = BQ / 32, TILE = BQ * D * 2, LA = kKvLookahead;
   constexpr int NX = 4 * NDB, NS = (DK ? 2 : 1) * NKS * NQB, NOP = NX + NS;
@@ -337,10 +338,11 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   const float* __restrict__ Dp = Dg;
 
   // Query tiles qs .. ntq-1; this wave's keys see tiles from ws on (causal:
-  // query q sees keys <= q).
-  const int qs = DIAG ? kb0 / BQ : 0;
+  // query q sees keys <= q + qoff).  A block whose keys no query sees
+  // (qs >= ntq) skips the walk and adds zero.
   const int ntq = (Sq + BQ - 1) / BQ;
-  const int ws = DIAG ? min(max(qs, kw0 / BQ), ntq) : qs;
+  const int qs = DIAG ? min(max(0, kb0 - qoff) / BQ, ntq) : 0;
+  const int ws = DIAG ? min(max(qs, max(0, kw0 - qoff) / BQ), ntq) : qs;
 
   TileBufDma<D, NW, BQ> dma;
   dma.init(wave, lane);
@@ -456,7 +458,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   // is query 32*qb + 8*(i/4) + 4g + i%4 of the tile.
   auto vector_phase = [&](int tt) __attribute__((always_inline)) {
     const int q0 = tt * BQ;
-    const bool masked = (q0 + BQ > Sq) || (DIAG && q0 < kw0 + NKW);
+    const bool masked = (q0 + BQ > Sq) || (DIAG && q0 + qoff < kw0 + NKW);
     const uint32_t lo_ = laddr + (uint32_t)((tt & 3) * BQ * 4);
     // The lse (and D) values of accumulator qb's 32 rows, four rows per read,
     // are requested JB row groups at a time and consumed in order with counted
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qi = q0 + qb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (qi >= Sq || (DIAG && kk > qi)) sacc[qb][i] = 0.f;
+          if (qi >= Sq || (DIAG && kk > qi + qoff)) sacc[qb][i] = 0.f;
         }
     }
 #pragma unroll
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   // one after the other into the same accumulators (dk, dv sum over them).
   // The last barrier of a head's walk comes after every wave's last LDS read
   // of it, so the next head's first loads may reuse any buffer.
-  for (int gh = 0; gh < group; ++gh) {
+  for (int gh = 0; gh < group && qs < ntq; ++gh) {
     const int bh = bhk * group + gh;
     qp = qg + (size_t)bh * Sq * D;
     dp = dog + (size_t)bh * Sq * D;
@@ -588,17 +590,18 @@ template <int D>
 hipError_t launch_dq_d(const BwdStepArgs& a, hipStream_t stream) {
   constexpr int BR = kDqWaves * kDqRowsPerWave;
   const int nq = (a.Sq + BR - 1) / BR;
-  if (a.group < 1 || a.BH % a.group) return hipErrorInvalidValue;
+  if (a.group < 1 || a.BH % a.group || a.qoff < 0 || (long long)a.Sq + a.Sk + a.qoff + 1024 > 0x7fffffffLL)
+    return hipErrorInvalidValue;
   const long long total = (long long)nq * a.BH;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   if (total == 0) return hipSuccess;
   const float sl2 = a.scale * kLog2e;
   if (a.diag)
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(64 * kDqWaves), 0, stream, a.q, a.k,
-                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale, a.group);
+                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale, a.group, a.qoff);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(64 * kDqWaves), 0, stream, a.q, a.k,
-                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale, a.group);
+                       a.v, a.dO, a.lse2, a.D, a.dq, a.Sq, a.Sk, nq, (int)total, sl2, a.scale, a.group, a.qoff);
   return hipGetLastError();
 }
 
@@ -606,7 +609,8 @@ template <int D>
 hipError_t launch_dkdv_d(const BwdStepArgs& a, hipStream_t stream) {
   constexpr int BK = kKvWaves * kKvKeysPerWave;
   const int nk = (a.Sk + BK - 1) / BK;
-  if (a.group < 1 || a.BH % a.group) return hipErrorInvalidValue;
+  if (a.group < 1 || a.BH % a.group || a.qoff < 0 || (long long)a.Sq + a.Sk + a.qoff + 1024 > 0x7fffffffLL)
+    return hipErrorInvalidValue;
   const long long total = (long long)nk * (a.BH / a.group);  // blocks per key/value head
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   if (total == 0) return hipSuccess;
@@ -614,7 +618,7 @@ hipError_t launch_dkdv_d(const BwdStepArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)total), block(64 * kKvWaves);
 #define RA_KV_LAUNCH(DIAG, DK, OUT)                                                                               \
   hipLaunchKernelGGL((bwd_kv_kernel<D, DIAG, DK>), grid, block, 0, stream, a.q, a.k, a.v, a.dO, a.lse2, a.D, OUT, \
-                     a.Sq, a.Sk, nk, (int)total, sl2, a.scale, a.group)
+                     a.Sq, a.Sk, nk, (int)total, sl2, a.scale, a.group, a.qoff)
   if (a.diag) {
     RA_KV_LAUNCH(true, false, a.dv);
     RA_KV_LAUNCH(true, true, a.dk);

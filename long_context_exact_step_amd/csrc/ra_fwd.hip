@@ -132,7 +132,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
                                                                   float* __restrict__ og,
                                                                   float* __restrict__ lseg, int Sq, int Sk,
                                                                   int n_qtiles, int total_tiles,
-                                                                  float scale_log2, int group) {
+                                                                  float scale_log2, int group, int qoff) {
   constexpr int NW = kFwdWaves, NQW = kFwdRowsPerWave, BR = NW * NQW, BC = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kFwdLookahead;
   constexpr int NB = kFwdBuffers;
@@ -168,12 +168,13 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   const uint16_t* __restrict__ kp = kg + (size_t)(bh / group) * Sk * D;
   const uint16_t* __restrict__ vp = vg + (size_t)(bh / group) * Sk * D;
 
+  // Causal: query row q sees keys k <= q + qoff.
   int kend = Sk;
-  if (DIAG) kend = min(kend, q0 + BR);
+  if (DIAG) kend = min(kend, q0 + BR + qoff);
   const int ntiles = (kend + BC - 1) / BC;
-  const int wtiles = DIAG ? min(ntiles, max(0, (min(qw0 + NQW, Sq) - 1) / BC + 1)) : ntiles;
+  const int wtiles = DIAG ? min(ntiles, max(0, (min(qw0 + NQW, Sq) - 1 + qoff) / BC + 1)) : ntiles;
   // Keys at or past `lim` are masked for this lane's query.
-  const int lim = DIAG ? min(Sk, qq + 1) : Sk;
+  const int lim = DIAG ? min(Sk, qq + 1 + qoff) : Sk;
 
   // Iteration t reads K(t+1) and V(t-1); step t loads V(t+1) and K(t+3),
   // one 1 KB piece per MFMA slot in DMA_SLOT, V pieces first.  A step ends
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
     }
     if (tt < wtiles) {
       const int k0 = tt * BC;
-      const bool masked = (k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0);
+      const bool masked = (k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0 + qoff);
       const float lt = (l4[0] + l4[1]) + (l4[2] + l4[3]);
       if (masked || __ballot(!(lt <= kLazyBound) || mrow == kNegInf) != 0) softmax_exact(tt, sc);
       else lrow += lt;
@@ -428,7 +429,8 @@ template <int D>
 hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
   constexpr int BR = kFwdWaves * kFwdRowsPerWave;
   const int n_qtiles = (a.Sq + BR - 1) / BR;
-  if (a.group < 1 || a.BH % a.group) return hipErrorInvalidValue;
+  if (a.group < 1 || a.BH % a.group || a.qoff < 0 || (long long)a.Sq + a.qoff + BR > 0x7fffffffLL)
+    return hipErrorInvalidValue;
   const long long total = (long long)n_qtiles * a.BH;
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -436,7 +438,7 @@ hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)total), block(64 * kFwdWaves);
 #define RA_FWD_LAUNCH(DIAG, MERGE)                                                                         \
   hipLaunchKernelGGL((fwd_step_kernel<D, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, a.v, a.o, \
-                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group)
+                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff)
   if (a.diag) {
     if (a.merge) RA_FWD_LAUNCH(true, true);
     else RA_FWD_LAUNCH(true, false);

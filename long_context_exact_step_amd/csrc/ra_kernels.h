@@ -19,9 +19,10 @@ struct FwdStepArgs {
   float* lse;
   int BH, Sq, Sk, d;
   float scale;
-  bool diag;   // diagonal mask: local query t sees local keys <= t (Sq == Sk)
+  bool diag;   // causal mask: query t sees keys <= t + qoff
   bool merge;  // fold into the running (o, lse) instead of overwriting
   int group;   // query heads per key/value head (>= 1, divides BH)
+  int qoff;    // causal offset of the query rows against the keys (>= 0; 0 on the ring's diagonal chunk)
 };
 hipError_t launch_fwd_step(const FwdStepArgs& a, hipStream_t stream);
 
@@ -49,8 +50,9 @@ struct BwdStepArgs {
   float* dv;   // accumulated (+=)
   int BH, Sq, Sk, d;
   float scale;
-  bool diag;
+  bool diag;  // causal mask: query t sees keys <= t + qoff
   int group;  // query heads per key/value head (>= 1, divides BH)
+  int qoff;   // causal offset of the query rows against the keys (>= 0)
 };
 hipError_t launch_bwd_dq(const BwdStepArgs& a, hipStream_t stream);    // dq += ...
 hipError_t launch_bwd_dkdv(const BwdStepArgs& a, hipStream_t stream);  // dk, dv += ...

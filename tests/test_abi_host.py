@@ -39,7 +39,9 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ra_version() == 3  # 2: grouped-query (*_gqa) entry points; 3: ra_ulysses_fwd, ra_ulysses_bwd
+    # 2: grouped-query (*_gqa) entry points; 3: ra_ulysses_fwd, ra_ulysses_bwd;
+    # 4: ra_allgather_fwd, ra_allgather_bwd
+    assert L.ra_version() == 4
     assert L.ra_status_string(RA_OK) == b"RA_OK"
     assert L.ra_status_string(RA_ERR_WORKSPACE) == b"RA_ERR_WORKSPACE"
     assert L.ra_status_string(12345) == b"RA_ERR_UNKNOWN"
@@ -167,6 +169,39 @@ def test_ulysses_workspace_and_validation(L):
     assert bwd(rank=-1) == RA_ERR_RANK
     assert bwd(wsb=need_b - 16) == RA_ERR_WORKSPACE
     assert bwd(dO=(ctypes.c_void_p * P)(FAKE, FAKE, FAKE, 0)) == RA_ERR_NULL
+
+
+def test_allgather_workspace_and_validation(L):
+    kv = 2 * 8 * 131072 * 128 * 2  # gathered K and V, H_kv = 8, S = 4 * 32768
+    assert L.ra_allgather_workspace_bytes(4, 1, 32, 8, 32768, 128, 0) == kv
+    assert L.ra_allgather_workspace_bytes(4, 1, 32, 8, 32768, 128, 1) == kv + 2 * 32 * 32768 * 4
+    assert L.ra_allgather_workspace_bytes(4, 1, 32, 6, 64, 128, 0) == 0  # 32 heads over 6 groups
+    assert L.ra_allgather_workspace_bytes(4, 1, 32, 32, 64, 96, 0) == 0  # unsupported d
+    P, C, d = 4, 64, 128
+    arr = (ctypes.c_void_p * P)(*([FAKE] * P))
+    need = L.ra_allgather_workspace_bytes(P, 1, 8, 2, C, d, 0)
+    call = lambda H=8, Hk=2, rank=1, ws=FAKE, wsb=need, k=arr, q=FAKE, d=d: L.ra_allgather_fwd(
+        vp(q), k, arr, P, vp(FAKE), vp(FAKE), rank, 1, 0.1, 1, H, Hk, C, d, vp(ws), wsb, None)
+    assert call(Hk=3) == RA_ERR_SHAPE
+    assert call(d=96) == RA_ERR_UNSUPPORTED
+    assert call(rank=4) == RA_ERR_RANK
+    assert call(rank=-1) == RA_ERR_RANK
+    assert call(ws=0) == RA_ERR_WORKSPACE
+    assert call(wsb=need - 16) == RA_ERR_WORKSPACE
+    assert call(q=0) == RA_ERR_NULL
+    assert call(q=MIS) == RA_ERR_ALIGN
+    assert call(k=(ctypes.c_void_p * P)(FAKE, FAKE, FAKE, 0)) == RA_ERR_NULL  # every chunk is gathered
+    assert call(k=(ctypes.c_void_p * P)(FAKE, MIS, FAKE, FAKE)) == RA_ERR_ALIGN
+    need_b = L.ra_allgather_workspace_bytes(P, 1, 8, 2, C, d, 1)
+    assert need_b == need + 2 * 8 * C * 4
+    bwd = lambda Hk=2, rank=1, wsb=need_b, dk=FAKE: L.ra_allgather_bwd(
+        vp(FAKE), arr, arr, P, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(dk), vp(FAKE), rank, 1, 0.1, 1, 8, Hk,
+        C, d, vp(FAKE), wsb, None)
+    assert bwd(Hk=5) == RA_ERR_SHAPE
+    assert bwd(rank=4) == RA_ERR_RANK
+    assert bwd(wsb=need_b - 16) == RA_ERR_WORKSPACE
+    assert bwd(dk=0) == RA_ERR_NULL
+    assert bwd(dk=MIS) == RA_ERR_ALIGN
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -333,3 +333,74 @@ def test_ulysses_bwd_every_rank(P, C, H, d, causal):
         assert_close(f64(dq), rq, TOL_GRAD, "dq")
         assert_close(f64(dk), rk, TOL_GRAD, "dk")
         assert_close(f64(dv), rv, TOL_GRAD, "dv")
+
+
+# ---------------------------------------------------------------------------
+# All-gather share: gathered K/V, one pass at a causal offset.
+# ---------------------------------------------------------------------------
+
+# Ragged chunk sizes put the causal offset rank*C off the 64-token tiles;
+# (2, 300) has key blocks that no query of rank 0 sees.
+AG_CASES = [(2, 100, 2, 2, 128, True), (4, 37, 4, 2, 64, True), (3, 129, 2, 2, 128, False),
+            (2, 300, 2, 1, 128, True), (4, 1, 2, 2, 128, True), (3, 70, 4, 4, 64, False)]
+
+
+@pytest.mark.parametrize("P,C,H,Hk,d,causal", AG_CASES)
+def test_allgather_share_every_rank(P, C, H, Hk, d, causal):
+    from oracle.allgather import allgather_share_fwd
+    q, k, v, _ = ring_tensors(113, 1, H, P, C, d, H_kv=Hk)
+    kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
+    scale = 1 / math.sqrt(d)
+    for rank in range(P):
+        print(f"allgather P={P} C={C} H={H} Hk={Hk} d={d} causal={causal} rank={rank}", flush=True)
+        o = torch.full((1, H, C, d), float("nan"), device=dev())
+        lse = torch.full((1, H, C), float("nan"), device=dev())
+        ra.allgather_fwd(q[rank].to(dev()), kd, vd, o, lse, rank, causal, scale)
+        torch.cuda.synchronize()
+        ro, rl = allgather_share_fwd(f64(q[rank]), [f64(t) for t in k], [f64(t) for t in v], rank, causal, scale)
+        assert_close(f64(o), ro, TOL_O, f"o rank {rank}")
+        assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)
+
+
+@pytest.mark.parametrize("P,C,H,Hk,d,causal", AG_CASES)
+def test_allgather_bwd_every_rank(P, C, H, Hk, d, causal):
+    from oracle.allgather import allgather_share_bwd
+    q, k, v, do = ring_tensors(114, 1, H, P, C, d, with_do=True, H_kv=Hk)
+    kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
+    scale = 1 / math.sqrt(d)
+    for rank in range(P):
+        print(f"allgather bwd P={P} C={C} H={H} Hk={Hk} d={d} causal={causal} rank={rank}", flush=True)
+        qd, dd = q[rank].to(dev()), do[rank].to(dev())
+        o = torch.empty(1, H, C, d, device=dev())
+        lse = torch.empty(1, H, C, device=dev())
+        ra.allgather_fwd(qd, kd, vd, o, lse, rank, causal, scale)
+        dq = torch.full((1, H, C, d), float("nan"), device=dev())
+        dk, dv = (torch.full((1, Hk, P * C, d), float("nan"), device=dev()) for _ in range(2))
+        ra.allgather_bwd(qd, kd, vd, o, lse, dd, dq, dk, dv, rank, causal, scale)
+        torch.cuda.synchronize()
+        rq, rk, rv = allgather_share_bwd(f64(q[rank]), [f64(t) for t in k], [f64(t) for t in v], f64(do[rank]),
+                                         rank, causal, scale)
+        assert_close(f64(dq), rq, TOL_GRAD, "dq")
+        assert_close(f64(dk), rk, TOL_GRAD, "dk")
+        assert_close(f64(dv), rv, TOL_GRAD, "dv")
+        if causal:
+            assert not dk[:, :, (rank + 1) * C:].any() and not dv[:, :, (rank + 1) * C:].any(), \
+                "keys past the rank's chunk got a gradient"
+
+
+def test_allgather_equals_ring_walk():
+    """The two methods reach the same exact attention: the all-gather share
+    and the ring walk of the same rank agree to rounding."""
+    P, C, H, d = 4, 200, 2, 128
+    q, k, v, _ = ring_tensors(115, 1, H, P, C, d)
+    kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
+    for rank in range(P):
+        print(f"allgather vs ring rank={rank}", flush=True)
+        qd = q[rank].to(dev())
+        o1, o2 = (torch.empty(1, H, C, d, device=dev()) for _ in range(2))
+        l1, l2 = (torch.empty(1, H, C, device=dev()) for _ in range(2))
+        ra.allgather_fwd(qd, kd, vd, o1, l1, rank, True)
+        ra.ring_fwd(qd, kd, vd, o2, l2, rank, True, ring_mode="resident")
+        torch.cuda.synchronize()
+        assert_close(f64(o1), f64(o2), 1e-2, "o all-gather vs ring")
+        assert_close(f64(l1), f64(l2), 1e-3, "lse all-gather vs ring", rel=None)

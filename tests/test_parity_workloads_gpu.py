@@ -490,3 +490,112 @@ def test_ulysses_bwd_128k_sampled_rows_and_sums():
     r_v = ((dv_c.sum(dim=2) - sum_do).abs().max() / sum_do.abs().max()).item()
     say(f"  max|ddQ|={e_q:.2e} rel={rel:.2e}  max|sum dK|/sum|dK|={r_k:.2e}  sum dV vs sum dO={r_v:.2e}")
     assert e_q <= TOL_GRAD and rel <= TOL_REL and r_k <= 1e-3 and r_v <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# All-gather share: the rank's queries over the gathered sequence in one pass.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.timeout(600)
+def test_allgather_share_128k_sampled_rows():
+    """Rank 3's share of the 128K/CP=4 sequence (MHA, then key/value chunks
+    of H/4 heads) against the oracle on 256 sampled rows per head."""
+    w = WORKLOADS[2]
+    r = w.ranks[0]
+    for Hk in (w.H, w.H // GQA_GROUP):
+        say(f"{w.name}, H_kv={Hk}: all-gather inputs")
+        q, k, v, _ = gen_workload(w, H_kv=Hk)
+        kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
+        o = torch.full((w.B, w.H, w.C, w.d), float("nan"), device=dev())
+        lse = torch.full((w.B, w.H, w.C), float("nan"), device=dev())
+        say(f"{w.name}, H_kv={Hk}: all-gather share of rank {r}")
+        ra.allgather_fwd(q[r].to(dev()), kd, vd, o, lse, r, w.causal, w.scale)
+        torch.cuda.synchronize()
+        del kd, vd
+        torch.cuda.empty_cache()
+        check_rows(w, r, q[r], k, v, o, lse, lambda h: inputs.query_row_sample(w.id, h, w.C),
+                   f"{w.name} all-gather H_kv={Hk} sampled rows", grp=w.H // Hk)
+
+
+@pytest.fixture(scope="module")
+def train_run_allgather():
+    w = WORKLOADS[5]
+    r = w.ranks[0]
+    say(f"{w.name}: all-gather training inputs")
+    q, k, v, do = gen_workload(w, with_do=True)
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    qd, dd = q[r].to(dev()), do[r].to(dev())
+    o = torch.full((w.B, w.H, w.C, w.d), float("nan"), device=dev())
+    lse = torch.full((w.B, w.H, w.C), float("nan"), device=dev())
+    ra.allgather_fwd(qd, kd, vd, o, lse, r, w.causal, w.scale)
+    dq = torch.full_like(o, float("nan"))
+    dk, dv = (torch.full((w.B, w.H, w.P * w.C, w.d), float("nan"), device=dev()) for _ in range(2))
+    say(f"{w.name}: all-gather backward of rank {r}")
+    ra.allgather_bwd(qd, kd, vd, o, lse, dd, dq, dk, dv, r, w.causal, w.scale)
+    torch.cuda.synchronize()
+    out = dict(w=w, r=r, q=q[r], k=k, v=v, do=do[r], o=o.cpu(), lse=lse.cpu(), dq=dq.cpu(), dk=dk.cpu(),
+               dv=dv.cpu())
+    del kd, vd, qd, dd, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return out
+
+
+@pytest.mark.timeout(600)
+def test_allgather_train_forward_and_dq_sampled_rows(train_run_allgather):
+    t = train_run_allgather
+    w, r = t["w"], t["r"]
+    check_rows(w, r, t["q"], t["k"], t["v"], t["o"], t["lse"], lambda h: inputs.query_row_sample(w.id, h, w.C),
+               f"{w.name} all-gather forward sampled rows")
+
+    def one(h):
+        rows = inputs.query_row_sample(w.id, h, w.C)
+        kh, vh = head_full(t["k"], h), head_full(t["v"], h)
+        qh, doh = f64(t["q"][:, h:h + 1, rows]), f64(t["do"][:, h:h + 1, rows])
+        rq, _, _ = oracle.attention_bwd(qh, kh, vh, doh, w.scale, True, q_pos=r * w.C + rows)
+        gq = f64(t["dq"][:, h:h + 1, rows])
+        return np.abs(gq - rq).max(), np.linalg.norm(gq - rq) ** 2, np.linalg.norm(rq) ** 2
+
+    say(f"{w.name}: all-gather oracle dQ on 256 rows x {w.H} heads")
+    res = fan_out(one, range(w.H))
+    e_q = max(x[0] for x in res)
+    rel = math.sqrt(sum(x[1] for x in res) / sum(x[2] for x in res))
+    say(f"  max|ddQ|={e_q:.2e} rel={rel:.2e}")
+    assert e_q <= TOL_GRAD and rel <= TOL_REL
+
+
+@pytest.mark.timeout(900)
+def test_allgather_train_dk_dv_sampled_key_rows(train_run_allgather):
+    t = train_run_allgather
+    w, r = t["w"], t["r"]
+    heads = [0, w.H - 1]
+    pos = r * w.C + np.arange(w.C)
+
+    def one(h):
+        kh, vh = head_full(t["k"], h), head_full(t["v"], h)
+        qh, doh = f64(t["q"][:, h:h + 1]), f64(t["do"][:, h:h + 1])
+        rows = np.concatenate([j * w.C + inputs.key_row_sample(w.id, h, j, w.C) for j in range(w.P)])
+        rk, rv = oracle.attention_bwd_key_rows(qh, kh, vh, doh, w.scale, True, rows, q_pos=pos)
+        gk, gv = f64(t["dk"][:, h:h + 1, rows]), f64(t["dv"][:, h:h + 1, rows])
+        return (np.abs(gk - rk).max(), np.abs(gv - rv).max(),
+                np.linalg.norm(gk - rk) ** 2 + np.linalg.norm(gv - rv) ** 2,
+                np.linalg.norm(rk) ** 2 + np.linalg.norm(rv) ** 2)
+
+    say(f"{w.name}: all-gather oracle dK/dV on 256 key rows x {w.P} chunks x heads {heads}")
+    res = fan_out(one, heads)
+    e_k, e_v = max(x[0] for x in res), max(x[1] for x in res)
+    rel = math.sqrt(sum(x[2] for x in res) / sum(x[3] for x in res))
+    say(f"  max|ddK|={e_k:.2e} max|ddV|={e_v:.2e} rel={rel:.2e}")
+    assert e_k <= TOL_GRAD and e_v <= TOL_GRAD and rel <= TOL_REL
+
+
+def test_allgather_train_gradient_sums_every_key(train_run_allgather):
+    """Over the whole gathered sequence: sum_k dK_k = 0 and sum_k dV_k = sum_q dO_q."""
+    t = train_run_allgather
+    w = t["w"]
+    dk, dv = t["dk"].double(), t["dv"].double()
+    r_k = (dk.sum(dim=2).abs() / dk.abs().sum(dim=2).clamp_min(1e-30)).max().item()
+    sum_do = t["do"].double().sum(dim=2)
+    r_v = ((dv.sum(dim=2) - sum_do).abs().max() / sum_do.abs().max()).item()
+    say(f"{w.name}: all-gather max|sum dK|/sum|dK|={r_k:.2e}  max|sum dV - sum dO|/max|sum dO|={r_v:.2e}")
+    assert r_k <= 1e-3 and r_v <= 1e-3
