@@ -539,7 +539,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   // one after the other into the same accumulators (dk, dv sum over them).
   // The last barrier of a head's walk comes after every wave's last LDS read
   // of it, so the next head's first loads may reuse any buffer.
-  for (int gh = 0; gh < group && qs < ntq; ++gh) {
+  for (int gh = 0; gh < group && (!DIAG || qs < ntq); ++gh) {
     const int bh = bhk * group + gh;
     qp = qg + (size_t)bh * Sq * D;
     dp = dog + (size_t)bh * Sq * D;

@@ -341,20 +341,22 @@ def test_ulysses_bwd_every_rank(P, C, H, d, causal):
 
 # Ragged chunk sizes put the causal offset rank*C off the 64-token tiles;
 # (2, 300) has key blocks that no query of rank 0 sees.
-AG_CASES = [(2, 100, 2, 2, 128, True), (4, 37, 4, 2, 64, True), (3, 129, 2, 2, 128, False),
-            (2, 300, 2, 1, 128, True), (4, 1, 2, 2, 128, True), (3, 70, 4, 4, 64, False)]
+# The last two run two sequences (B = 2) through one gather.
+AG_CASES = [(2, 100, 2, 2, 128, True, 1), (4, 37, 4, 2, 64, True, 1), (3, 129, 2, 2, 128, False, 1),
+            (2, 300, 2, 1, 128, True, 1), (4, 1, 2, 2, 128, True, 1), (3, 70, 4, 4, 64, False, 1),
+            (3, 90, 4, 2, 128, True, 2), (2, 65, 2, 1, 64, False, 2)]
 
 
-@pytest.mark.parametrize("P,C,H,Hk,d,causal", AG_CASES)
-def test_allgather_share_every_rank(P, C, H, Hk, d, causal):
+@pytest.mark.parametrize("P,C,H,Hk,d,causal,B", AG_CASES)
+def test_allgather_share_every_rank(P, C, H, Hk, d, causal, B):
     from oracle.allgather import allgather_share_fwd
-    q, k, v, _ = ring_tensors(113, 1, H, P, C, d, H_kv=Hk)
+    q, k, v, _ = ring_tensors(113, B, H, P, C, d, H_kv=Hk)
     kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
     scale = 1 / math.sqrt(d)
     for rank in range(P):
-        print(f"allgather P={P} C={C} H={H} Hk={Hk} d={d} causal={causal} rank={rank}", flush=True)
-        o = torch.full((1, H, C, d), float("nan"), device=dev())
-        lse = torch.full((1, H, C), float("nan"), device=dev())
+        print(f"allgather P={P} C={C} B={B} H={H} Hk={Hk} d={d} causal={causal} rank={rank}", flush=True)
+        o = torch.full((B, H, C, d), float("nan"), device=dev())
+        lse = torch.full((B, H, C), float("nan"), device=dev())
         ra.allgather_fwd(q[rank].to(dev()), kd, vd, o, lse, rank, causal, scale)
         torch.cuda.synchronize()
         ro, rl = allgather_share_fwd(f64(q[rank]), [f64(t) for t in k], [f64(t) for t in v], rank, causal, scale)
@@ -362,20 +364,20 @@ def test_allgather_share_every_rank(P, C, H, Hk, d, causal):
         assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)
 
 
-@pytest.mark.parametrize("P,C,H,Hk,d,causal", AG_CASES)
-def test_allgather_bwd_every_rank(P, C, H, Hk, d, causal):
+@pytest.mark.parametrize("P,C,H,Hk,d,causal,B", AG_CASES)
+def test_allgather_bwd_every_rank(P, C, H, Hk, d, causal, B):
     from oracle.allgather import allgather_share_bwd
-    q, k, v, do = ring_tensors(114, 1, H, P, C, d, with_do=True, H_kv=Hk)
+    q, k, v, do = ring_tensors(114, B, H, P, C, d, with_do=True, H_kv=Hk)
     kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
     scale = 1 / math.sqrt(d)
     for rank in range(P):
-        print(f"allgather bwd P={P} C={C} H={H} Hk={Hk} d={d} causal={causal} rank={rank}", flush=True)
+        print(f"allgather bwd P={P} C={C} B={B} H={H} Hk={Hk} d={d} causal={causal} rank={rank}", flush=True)
         qd, dd = q[rank].to(dev()), do[rank].to(dev())
-        o = torch.empty(1, H, C, d, device=dev())
-        lse = torch.empty(1, H, C, device=dev())
+        o = torch.empty(B, H, C, d, device=dev())
+        lse = torch.empty(B, H, C, device=dev())
         ra.allgather_fwd(qd, kd, vd, o, lse, rank, causal, scale)
-        dq = torch.full((1, H, C, d), float("nan"), device=dev())
-        dk, dv = (torch.full((1, Hk, P * C, d), float("nan"), device=dev()) for _ in range(2))
+        dq = torch.full((B, H, C, d), float("nan"), device=dev())
+        dk, dv = (torch.full((B, Hk, P * C, d), float("nan"), device=dev()) for _ in range(2))
         ra.allgather_bwd(qd, kd, vd, o, lse, dd, dq, dk, dv, rank, causal, scale)
         torch.cuda.synchronize()
         rq, rk, rv = allgather_share_bwd(f64(q[rank]), [f64(t) for t in k], [f64(t) for t in v], f64(do[rank]),
