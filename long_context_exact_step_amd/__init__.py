@@ -125,6 +125,23 @@ def _shape(t, shape, name):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _bhsd(t, name):
+    """(B, H, S, d) of a 4-d tensor."""
+    if t.dim() != 4:
+        raise ValueError(f"{name}: expected a [B, H, S, d] tensor, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _chunks(ts, shape, name):
+    """Every chunk of a list has `shape`; returns the count."""
+    if len(ts) < 1:
+        raise ValueError(f"{name}: no chunks")
+    for n, t in enumerate(ts):
+        if t is not None:
+            _shape(t, shape, f"{name}[{n}]")
+    return len(ts)
+
+
 def _need(t, dtype, name):
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
@@ -144,10 +161,12 @@ def step_fwd(q, k, v, o_partial, lse_partial, step, causal, scale=None, stream=N
     """ra_step_fwd: one ring step's normalised partial and its lse.  k and v
     may carry fewer heads than q (grouped-query attention, ra_step_fwd_gqa)."""
     import torch
+    B, H, Sq, d = _bhsd(q, "q")
+    _, Hk, Sk, _ = _bhsd(k, "k")
+    _shape(k, (B, Hk, Sk, d), "k"); _shape(v, (B, Hk, Sk, d), "v")
+    _shape(o_partial, (B, H, Sq, d), "o_partial"); _shape(lse_partial, (B, H, Sq), "lse_partial")
     _need(q, torch.bfloat16, "q"); _need(k, torch.bfloat16, "k"); _need(v, torch.bfloat16, "v")
     _need(o_partial, torch.float32, "o_partial"); _need(lse_partial, torch.float32, "lse_partial")
-    B, H, Sq, d = q.shape
-    Hk, Sk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     args = (int(step), int(bool(causal)), _stream(stream, q))
     ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(o_partial), _ptr(lse_partial))
@@ -160,11 +179,13 @@ def step_fwd(q, k, v, o_partial, lse_partial, step, causal, scale=None, stream=N
 def lse_merge(o, lse, o_partial, lse_partial, stream=None):
     """ra_lse_merge: fold (o_partial, lse_partial) into (o, lse) in place."""
     import torch
+    B, H, S, d = _bhsd(o, "o")
+    _shape(o_partial, (B, H, S, d), "o_partial")
+    _shape(lse, (B, H, S), "lse"); _shape(lse_partial, (B, H, S), "lse_partial")
     for t, n in ((o, "o"), (o_partial, "o_partial")):
         _need(t, torch.float32, n)
     for t, n in ((lse, "lse"), (lse_partial, "lse_partial")):
         _need(t, torch.float32, n)
-    B, H, S, d = o.shape
     _check(lib().ra_lse_merge(_ptr(o), _ptr(lse), _ptr(o_partial), _ptr(lse_partial),
                               B, H, S, d, _stream(stream, o)))
 
@@ -185,14 +206,17 @@ def ring_fwd(q, k_chunks, v_chunks, o, lse, rank, causal, scale=None, ring_mode=
     for ring_mode "double_buffer"); allocated here if not given.
     """
     import torch
+    B, H, C, d = _bhsd(q, "q")
+    Hk = _bhsd(k_chunks[0], "k_chunks[0]")[1]
+    P = _chunks(k_chunks, (B, Hk, C, d), "k_chunks")
+    if _chunks(v_chunks, (B, Hk, C, d), "v_chunks") != P:
+        raise ValueError(f"v_chunks: {len(v_chunks)} chunks, expected {P} like k_chunks")
+    _shape(o, (B, H, C, d), "o"); _shape(lse, (B, H, C), "lse")
     _need(q, torch.bfloat16, "q")
     _need(o, torch.float32, "o")
     _need(lse, torch.float32, "lse")
     for n, t in enumerate(list(k_chunks) + list(v_chunks)):
         _need(t, torch.bfloat16, f"chunk{n}")
-    B, H, C, d = q.shape
-    Hk = k_chunks[0].shape[1]
-    P = len(k_chunks)
     mode = _MODES[ring_mode]
     need = workspace_bytes(P, B, H, C, d, mode, False, H_kv=Hk)
     if need and workspace is None:
@@ -216,6 +240,15 @@ def ring_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, 
     The chunks and their gradients may carry fewer heads than q (grouped-query
     attention, ra_ring_bwd_gqa)."""
     import torch
+    B, H, C, d = _bhsd(q, "q")
+    Hk = _bhsd(k_chunks[0], "k_chunks[0]")[1]
+    P = _chunks(k_chunks, (B, Hk, C, d), "k_chunks")
+    for ts, n in ((v_chunks, "v_chunks"), (dk_chunks, "dk_chunks"), (dv_chunks, "dv_chunks")):
+        if _chunks(ts, (B, Hk, C, d), n) != P:
+            raise ValueError(f"{n}: {len(ts)} chunks, expected {P}")
+    for t, n in ((o, "o"), (dO, "dO"), (dq, "dq")):
+        _shape(t, (B, H, C, d), n)
+    _shape(lse, (B, H, C), "lse")
     _need(q, torch.bfloat16, "q"); _need(dO, torch.bfloat16, "dO")
     _need(o, torch.float32, "o"); _need(lse, torch.float32, "lse"); _need(dq, torch.float32, "dq")
     for n, t in enumerate(list(k_chunks) + list(v_chunks)):
@@ -223,9 +256,6 @@ def ring_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, 
     for n, t in enumerate(list(dk_chunks) + list(dv_chunks)):
         if t is not None:
             _need(t, torch.float32, f"grad_chunk{n}")
-    B, H, C, d = q.shape
-    Hk = k_chunks[0].shape[1]
-    P = len(k_chunks)
     need = workspace_bytes(P, B, H, C, d, "resident", True, H_kv=Hk)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -250,12 +280,18 @@ def ulysses_fwd(q_chunks, k_chunks, v_chunks, o, lse, rank, causal, scale=None, 
     chunks); o [B,H/P,P*C,d], lse [B,H/P,P*C] fp32 receive attention of the
     rank's heads over the whole sequence."""
     import torch
+    B, H, C, d = _bhsd(q_chunks[0], "q_chunks[0]")
+    P = _chunks(q_chunks, (B, H, C, d), "q_chunks")
+    for ts, n in ((k_chunks, "k_chunks"), (v_chunks, "v_chunks")):
+        if _chunks(ts, (B, H, C, d), n) != P:
+            raise ValueError(f"{n}: {len(ts)} chunks, expected {P}")
+    if H % P:
+        raise ValueError(f"H={H} heads do not split over P={P} ranks")
+    _shape(o, (B, H // P, P * C, d), "o"); _shape(lse, (B, H // P, P * C), "lse")
     for n, t in enumerate(list(q_chunks) + list(k_chunks) + list(v_chunks)):
         _need(t, torch.bfloat16, f"chunk{n}")
     _need(o, torch.float32, "o")
     _need(lse, torch.float32, "lse")
-    B, H, C, d = q_chunks[0].shape
-    P = len(q_chunks)
     need = ulysses_workspace_bytes(P, B, H, C, d)
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.uint8, device=o.device)
@@ -272,13 +308,21 @@ def ulysses_bwd(q_chunks, k_chunks, v_chunks, dO_chunks, o, lse, dq, dk, dv, ran
     sequence like q_chunks; o, lse from ulysses_fwd; dq, dk, dv [B,H/P,P*C,d]
     fp32 are overwritten."""
     import torch
+    B, H, C, d = _bhsd(q_chunks[0], "q_chunks[0]")
+    P = _chunks(q_chunks, (B, H, C, d), "q_chunks")
+    for ts, n in ((k_chunks, "k_chunks"), (v_chunks, "v_chunks"), (dO_chunks, "dO_chunks")):
+        if _chunks(ts, (B, H, C, d), n) != P:
+            raise ValueError(f"{n}: {len(ts)} chunks, expected {P}")
+    if H % P:
+        raise ValueError(f"H={H} heads do not split over P={P} ranks")
+    for t, n in ((o, "o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _shape(t, (B, H // P, P * C, d), n)
+    _shape(lse, (B, H // P, P * C), "lse")
     for n, t in enumerate(list(q_chunks) + list(k_chunks) + list(v_chunks) + list(dO_chunks)):
         _need(t, torch.bfloat16, f"chunk{n}")
     for t, n in ((o, "o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
         _need(t, torch.float32, n)
     _need(lse, torch.float32, "lse")
-    B, H, C, d = q_chunks[0].shape
-    P = len(q_chunks)
     need = ulysses_workspace_bytes(P, B, H, C, d, bwd=True)
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.uint8, device=o.device)
@@ -300,16 +344,17 @@ def allgather_fwd(q, k_chunks, v_chunks, o, lse, rank, causal, scale=None, works
     bf16; o [B,H,C,d], lse [B,H,C] fp32 receive attention over the gathered
     sequence."""
     import torch
+    B, H, C, d = _bhsd(q, "q")
+    Hk = _bhsd(k_chunks[0], "k_chunks[0]")[1]
+    P = _chunks(k_chunks, (B, Hk, C, d), "k_chunks")
+    if _chunks(v_chunks, (B, Hk, C, d), "v_chunks") != P:
+        raise ValueError(f"v_chunks: {len(v_chunks)} chunks, expected {P} like k_chunks")
+    _shape(o, (B, H, C, d), "o"); _shape(lse, (B, H, C), "lse")
     _need(q, torch.bfloat16, "q")
     for n, t in enumerate(list(k_chunks) + list(v_chunks)):
         _need(t, torch.bfloat16, f"chunk{n}")
     _need(o, torch.float32, "o")
     _need(lse, torch.float32, "lse")
-    B, H, C, d = q.shape
-    Hk, P = k_chunks[0].shape[1], len(k_chunks)
-    _shape(o, (B, H, C, d), "o"); _shape(lse, (B, H, C), "lse")
-    for n, t in enumerate(list(k_chunks) + list(v_chunks)):
-        _shape(t, (B, Hk, C, d), f"chunk{n}")
     need = allgather_workspace_bytes(P, B, H, C, d, H_kv=Hk)
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
@@ -326,20 +371,21 @@ def allgather_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk, dv, rank, causal, s
     allgather_fwd; dq [B,H,C,d] and dk, dv [B,H_kv,P*C,d] fp32 are
     overwritten (dk, dv: the gathered sequence's gradient from this rank)."""
     import torch
-    _need(q, torch.bfloat16, "q"); _need(dO, torch.bfloat16, "dO")
-    for n, t in enumerate(list(k_chunks) + list(v_chunks)):
-        _need(t, torch.bfloat16, f"chunk{n}")
-    for t, n in ((o, "o"), (lse, "lse"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _need(t, torch.float32, n)
-    B, H, C, d = q.shape
-    Hk, P = k_chunks[0].shape[1], len(k_chunks)
+    B, H, C, d = _bhsd(q, "q")
+    Hk = _bhsd(k_chunks[0], "k_chunks[0]")[1]
+    P = _chunks(k_chunks, (B, Hk, C, d), "k_chunks")
+    if _chunks(v_chunks, (B, Hk, C, d), "v_chunks") != P:
+        raise ValueError(f"v_chunks: {len(v_chunks)} chunks, expected {P} like k_chunks")
     for t, n in ((o, "o"), (dO, "dO"), (dq, "dq")):
         _shape(t, (B, H, C, d), n)
     _shape(lse, (B, H, C), "lse")
     for t, n in ((dk, "dk"), (dv, "dv")):
         _shape(t, (B, Hk, P * C, d), n)
+    _need(q, torch.bfloat16, "q"); _need(dO, torch.bfloat16, "dO")
     for n, t in enumerate(list(k_chunks) + list(v_chunks)):
-        _shape(t, (B, Hk, C, d), f"chunk{n}")
+        _need(t, torch.bfloat16, f"chunk{n}")
+    for t, n in ((o, "o"), (lse, "lse"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, torch.float32, n)
     need = allgather_workspace_bytes(P, B, H, C, d, H_kv=Hk, bwd=True)
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)

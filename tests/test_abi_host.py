@@ -211,3 +211,33 @@ def test_python_binding_rejects_cpu_tensors():
     lse = torch.zeros(1, 1, 8)
     with pytest.raises(ValueError):
         ra.step_fwd(q, q, q, o, lse, 1, False)
+
+
+def test_python_binding_rejects_mis_shaped_tensors():
+    """Shapes are checked from tensor metadata before anything reaches the
+    library, so a mis-sized output cannot be written past its end."""
+    import torch
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    f32 = lambda *s: torch.zeros(*s)
+    B, H, C, d, P = 1, 2, 8, 64, 3
+    q, kc = bf(B, H, C, d), [bf(B, H, C, d) for _ in range(P)]
+    o, lse = f32(B, H, C, d), f32(B, H, C)
+    cases = [
+        lambda: ra.step_fwd(q, q, q, f32(B, H, C + 1, d), lse, 1, False),
+        lambda: ra.step_fwd(q, bf(B, H, C, d), bf(B, H, C + 1, d), o, lse, 1, False),
+        lambda: ra.lse_merge(o, f32(B, H, C - 1), o, lse),
+        lambda: ra.ring_fwd(q, kc, kc[:2], o, lse, 1, True),
+        lambda: ra.ring_fwd(q, kc, kc, o, f32(B, H, 2 * C), 1, True),
+        lambda: ra.ring_fwd(q, kc + [bf(B, H, C + 1, d)], kc + [bf(B, H, C, d)], o, lse, 1, True),
+        lambda: ra.ring_bwd(q, kc, kc, o, lse, q, o, [f32(B, H, C, d)] * P, [f32(B, H, C, 2 * d)] * P, 1, True),
+        # Ulysses over 2 ranks: outputs hold H/2 = 1 head of the 2*C tokens.
+        lambda: ra.ulysses_fwd(kc[:2], kc[:2], kc[:2], f32(B, H, 2 * C, d), f32(B, H, 2 * C), 0, True),
+        lambda: ra.ulysses_bwd(kc[:2], kc[:2], kc[:2], kc[:2], f32(B, 1, 2 * C, d), f32(B, 1, 2 * C),
+                               *([f32(B, 1, C, d)] * 3), 0, True),
+        lambda: ra.allgather_fwd(q, kc, kc, f32(B, H, C, d + 1), lse, 1, True),
+        lambda: ra.allgather_bwd(q, kc, kc, o, lse, q, o, f32(B, H, C, d), f32(B, H, P * C, d), 1, True),
+        lambda: ra.allgather_fwd(bf(H, C, d), kc, kc, o, lse, 1, True),
+    ]
+    for n, call in enumerate(cases):
+        with pytest.raises(ValueError, match="expected"):
+            call()
