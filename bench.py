@@ -16,7 +16,9 @@ H/4 heads (4 query heads per key/value head), under "gqa".  And (unless
 parallelism on the same sequence, under "ulysses".  And (unless
 --no-allgather): the same rank's share of all-gather sequence parallelism
 (gathered key/value chunks, one pass at a causal offset), forward and
-training step, under "allgather".
+training step, under "allgather".  And (unless --no-ceiling): the bf16 peak
+derived from the device's CU count and clock, and what a dense MFMA probe
+sustains on random and on zero operands, under "mfma_ceiling".
 
 Prints ONE JSON line: throughput in algorithmic TFLOP/s (4*d flops per
 visible (query, key) pair forward, 10*d backward), tokens/s, the roofline of
@@ -344,6 +346,42 @@ def run_allgather(w, steps, warmup, wt):
     return out
 
 
+def mfma_ceiling(iters=200000):
+    """What the bf16 matrix cores deliver on this device: the peak derived from
+    the CU count and maximum engine clock (4096 flop per CU per clock), and the
+    throughput of a probe kernel (two waves per SIMD issuing back-to-back
+    independent 32x32x16 bf16 MFMAs) on random N(0,1) operands and on zeros.
+    The chip is power-limited and MFMA power depends on the data, so the
+    random-operand figure is the ceiling that attention on N(0,1) inputs
+    meets."""
+    import torch
+    import long_context_exact_step_amd as ra
+
+    dev = torch.device("cuda", 0)
+    cus, clk_khz = ra.device_info()
+    out = {"cus": cus, "max_clock_mhz": clk_khz / 1e3,
+           "derived_peak_tflops": round(cus * 4096 * clk_khz * 1e3 / 1e12, 1)}
+    gen = torch.Generator().manual_seed(20261202)
+    operands = {"random": torch.randn(8192, generator=gen).to(torch.bfloat16).to(dev),
+                "zero": torch.zeros(8192, dtype=torch.bfloat16, device=dev)}
+    sink = torch.empty(cus * 512, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    flops = cus * 8 * iters * 16 * 32768
+    for name, ops in operands.items():
+        ra.mfma_probe(ops, sink, clocks, cus, max(1, iters // 10))  # warm-up
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        ra.mfma_probe(ops, sink, clocks, cus, iters)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        cyc, ref = clocks.tolist()
+        out[name] = {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 3),
+                     "clock_ghz": round(cyc / (ref / 100e6) / 1e9, 3) if ref > 0 else None}
+    return out
+
+
 def cpu_baseline(w, tensors, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample: 256 seeded query
     rows per head of the measured rank, heads taken in order until the time
@@ -407,6 +445,7 @@ def main():
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query (H_kv = H/4) measurements")
     ap.add_argument("--no-ulysses", action="store_true", help="skip the head-partitioned (Ulysses) share")
     ap.add_argument("--no-allgather", action="store_true", help="skip the all-gather sequence-parallel share")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA throughput probe")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -458,6 +497,13 @@ def main():
         "kernels": fwd["kernels"],
         "roofline": roofline,
     }
+    if not args.no_ceiling:
+        ce = mfma_ceiling()
+        ce["kernel_frac_of_random_ceiling"] = round(achieved / ce["random"]["tflops"], 4)
+        out["mfma_ceiling"] = ce
+        print(f"[bench] MFMA probe: random {ce['random']['tflops']} TFLOP/s at {ce['random']['clock_ghz']} GHz, "
+              f"zero {ce['zero']['tflops']} TFLOP/s at {ce['zero']['clock_ghz']} GHz; derived peak "
+              f"{ce['derived_peak_tflops']}", file=sys.stderr, flush=True)
     if not args.no_cpu:
         cb, par = cpu_baseline(w, tensors, args.cpu_seconds)
         out["cpu_baseline"] = cb

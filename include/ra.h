@@ -346,6 +346,34 @@ enum ra_trace_kind {
 int ra_trace_begin(void* const* start_events, void* const* end_events, int* kinds, int capacity);
 int ra_trace_end(void);
 
+/*
+ * Measurement helpers (no page defines them): what the bf16 matrix cores of
+ * the current device can deliver, to set the attention kernels' throughput
+ * against.
+ *
+ * ra_device_info writes the current device's compute-unit count and its
+ * maximum engine clock in kHz (hipDeviceGetAttribute).  A CU's four SIMDs
+ * each finish one 32x32x16 bf16 MFMA (32768 flop) every 32 cycles, so the
+ * dense bf16 peak is cu_count * 4096 flop * clock.  RA_ERR_NULL for NULL
+ * outputs, RA_ERR_HIP if the runtime fails.
+ *
+ * ra_mfma_probe launches `blocks` workgroups of 8 waves, one per CU (each
+ * reserves 96 KB of LDS), two waves per SIMD as in the attention kernels.
+ * Every wave loads 16 operand registers from `operands` (device, at least
+ * 16 * 64 * 16 = 16384 bytes of bf16 data, which sets what the matrix cores
+ * multiply: random values draw more power than zeros) and issues
+ * iters * 16 back-to-back 32x32x16 bf16 MFMAs into four independent
+ * accumulators: 524288 * iters flop per wave.  `sink` (device, blocks * 512
+ * floats) receives per-lane sums; `clocks` (device, 2 values) receives the
+ * shader-clock cycles (s_memtime) and 100 MHz reference ticks
+ * (s_memrealtime) that wave 0 of block 0 spent in its loop, whose ratio is
+ * the clock the cores ran at.  Asynchronous on `stream`; RA_ERR_NULL,
+ * RA_ERR_SHAPE (blocks or iters < 1), RA_ERR_HIP.
+ */
+int ra_device_info(int* cu_count, int* max_clock_khz);
+int ra_mfma_probe(const void* operands, float* sink, unsigned long long* clocks, int blocks, int iters,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

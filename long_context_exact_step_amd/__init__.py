@@ -18,7 +18,7 @@ __all__ = [
     "workspace_bytes", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH", "trace_begin", "trace_end",
     "ulysses_fwd", "ulysses_bwd", "ulysses_workspace_bytes",
     "allgather_fwd", "allgather_bwd", "allgather_workspace_bytes",
-    "TRACE_KINDS",
+    "TRACE_KINDS", "device_info", "mfma_probe",
 ]
 
 # ra_trace_kind values (include/ra.h).
@@ -92,6 +92,10 @@ def lib():
         L.ra_trace_begin.argtypes = [vpp, vpp, ctypes.POINTER(ctypes.c_int), i]
         L.ra_trace_end.restype = i
         L.ra_trace_end.argtypes = []
+        L.ra_device_info.restype = i
+        L.ra_device_info.argtypes = [ctypes.POINTER(i), ctypes.POINTER(i)]
+        L.ra_mfma_probe.restype = i
+        L.ra_mfma_probe.argtypes = [vp, vp, vp, i, i, vp]
         _lib = L
     return _lib
 
@@ -411,3 +415,30 @@ def trace_begin(start_events, end_events, kinds):
 def trace_end():
     """ra_trace_end: number of launches made while tracing was armed."""
     return int(lib().ra_trace_end())
+
+
+def device_info():
+    """ra_device_info: (compute units, maximum engine clock in kHz) of the
+    current device."""
+    cu, clk = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().ra_device_info(ctypes.byref(cu), ctypes.byref(clk)))
+    return cu.value, clk.value
+
+
+def mfma_probe(operands, sink, clocks, blocks, iters, stream=None):
+    """ra_mfma_probe: dense bf16 MFMA throughput probe.  operands: >= 16384
+    bytes of bf16 data; sink: float32, >= blocks * 512 values; clocks: int64,
+    >= 2 values (shader cycles, 100 MHz reference ticks of wave 0's loop)."""
+    import torch
+    if operands.dtype != torch.bfloat16 or operands.numel() * 2 < 16384:
+        raise ValueError("operands: expected >= 8192 bf16 values")
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 512:
+        raise ValueError(f"sink: expected >= {blocks * 512} float32 values")
+    if clocks.dtype != torch.int64 or clocks.numel() < 2:
+        raise ValueError("clocks: expected >= 2 int64 values")
+    for t, n in ((operands, "operands"), (sink, "sink"), (clocks, "clocks")):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{n}: must be a contiguous GPU tensor")
+    _check(lib().ra_mfma_probe(_ptr(operands), _ptr(sink), _ptr(clocks), int(blocks), int(iters),
+                               _stream(stream, sink)))
+

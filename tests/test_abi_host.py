@@ -241,3 +241,12 @@ def test_python_binding_rejects_mis_shaped_tensors():
     for n, call in enumerate(cases):
         with pytest.raises(ValueError, match="expected"):
             call()
+
+
+def test_probe_helpers_validation(L):
+    """The MFMA probe rejects NULL buffers and empty launches on the host."""
+    assert L.ra_device_info(None, None) == RA_ERR_NULL
+    assert L.ra_mfma_probe(vp(0), vp(FAKE), vp(FAKE), 1, 1, None) == RA_ERR_NULL
+    assert L.ra_mfma_probe(vp(FAKE), vp(FAKE), vp(FAKE), 0, 1, None) == RA_ERR_SHAPE
+    assert L.ra_mfma_probe(vp(FAKE), vp(FAKE), vp(FAKE), 4, 0, None) == RA_ERR_SHAPE
+

@@ -406,3 +406,28 @@ def test_allgather_equals_ring_walk():
         torch.cuda.synchronize()
         assert_close(f64(o1), f64(o2), 1e-2, "o all-gather vs ring")
         assert_close(f64(l1), f64(l2), 1e-3, "lse all-gather vs ring", rel=None)
+
+
+def test_mfma_probe_runs_within_the_derived_peak():
+    """The throughput probe: zero operands give zero sums, random ones finite
+    sums, and the measured rate stays under the peak derived from the CU count
+    and clock."""
+    cus, clk_khz = ra.device_info()
+    print(f"mfma probe: {cus} CUs, {clk_khz / 1e3:.0f} MHz", flush=True)
+    assert cus > 0 and clk_khz > 0
+    peak = cus * 4096 * clk_khz * 1e3
+    sink = torch.full((cus * 512,), float("nan"), device=dev())
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev())
+    ra.mfma_probe(torch.zeros(8192, dtype=torch.bfloat16, device=dev()), sink, clocks, cus, 100)
+    torch.cuda.synchronize()
+    assert not sink.any() and clocks[0].item() > 0 and clocks[1].item() > 0
+    ops = torch.randn(8192, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(dev())
+    iters = 20000
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    ra.mfma_probe(ops, sink, clocks, cus, iters)
+    t1.record()
+    torch.cuda.synchronize()
+    rate = cus * 8 * iters * 16 * 32768 / (t0.elapsed_time(t1) * 1e-3)
+    print(f"  random operands: {rate / 1e12:.0f} TFLOP/s of a derived {peak / 1e12:.0f}", flush=True)
+    assert torch.isfinite(sink).all() and 0 < rate <= 1.02 * peak
