@@ -6,21 +6,22 @@
 //   P = exp(scale q k^T - lse), dP = dO v^T, dS = P (dP - D), D = rowsum(dO o),
 //   dq += scale dS k,  dk += scale dS^T q,  dv += P^T dO.
 //
-// Three launches per step, none with atomics (results are deterministic):
+// Two launches per step, none with atomics (results are deterministic):
 //  * dq kernel -- a block owns 256 query rows (32 per wave, Q^T and dO^T in
 //    registers as MFMA B operands, like the forward) and streams 64-key tiles
 //    of K and V (row-major LDS tiles, A operands; K^T is read from the same
 //    tile through the transposing LDS read).  Scores are computed transposed
 //    (S^T = K Q^T, dP^T = V dO^T), so lse and D are per-lane scalars and dS^T
 //    feeds dq^T += K^T dS^T directly.
-//  * dv pass, then dk pass of the key kernel -- a block owns 256 keys of the
-//    chunk (32 per wave, K and V in registers as B operands) and streams
-//    64-query tiles of Q and dO (row-major; Q^T and dO^T through the
-//    transposing read).  Here S = Q K^T has a lane per key, so P and dS feed
-//    dv^T += dO^T P and dk^T += Q^T dS directly; lse and D of the tile's
-//    queries are staged in LDS.
-// The price of avoiding atomics is recomputing S in all three launches and dP
-// in two.
+//  * key kernel -- a block owns 128 keys of the chunk; the two waves of a
+//    SIMD share 32 of them, one holding K (S, P, dv) and the other V (dP, dS,
+//    dk), and stream 64-query tiles of Q and dO (row-major; Q^T and dO^T
+//    through the transposing read).  Here S = Q K^T has a lane per key, so P
+//    and dS feed dv^T += dO^T P and dk^T += Q^T dS directly; lse and D of the
+//    tile's queries are staged in LDS, and P passes from one wave to the
+//    other through LDS.
+// The price of avoiding atomics is recomputing S and dP in both launches:
+// 14 d flop per (query, key) pair executed for the 10 d of the gradient.
 #include "ra_device.h"
 #include "ra_kernels.h"
 
@@ -29,6 +30,15 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
+
+// One ds_write_b128 of v at LDS byte address addr + OFF, as inline assembly
+// beside the inline-assembly reads; its completion is waited for explicitly
+// (s_waitcnt lgkmcnt(0)) before the barrier after which another wave reads it.
+template <int OFF>
+__device__ __forceinline__ void ds_write_b128_off(uint32_t addr, const u32x4& v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
+}
 
 // ---------------------------------------------------------------------------
 // dq kernel.
@@ -284,52 +294,55 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dk/dv kernel, in two passes.
+// dk/dv kernel, one pass: the two waves of a SIMD share 32 keys.
 // ---------------------------------------------------------------------------
-constexpr int kKvWaves = 8;  // waves per block; waves w and w + 4 share a SIMD
-constexpr int kKvKeysPerWave = 32;
-constexpr int kKvLookahead = 2;  // MFMAs whose LDS operands are read ahead
+constexpr int kKvfWaves = 8;  // waves w and w + 4 share a SIMD and the same 32 keys
+constexpr int kKvfKeysPerWave = 32;
+constexpr int kKvfLookahead = 2;  // MFMAs whose LDS operands are read ahead
 
-// dv^T += dO^T P (DK = false) or dk^T += scale Q^T dS (DK = true) for one
-// ring step.  A block holds 256 keys of the chunk, 32 per wave (K and, for
-// dk, V in registers as MFMA B operands), and walks the query rows in
-// 64-row tiles.  Scores are computed with a lane per key, S = Q K^T (and
-// dP = dO V^T), so P and dS pack straight into the B operands of the
-// transposed products; lse and D of a tile's rows are staged in LDS.  Per
-// tile a wave runs two phases, as in the dq kernel:
-//   MFMA phase of tile t:  acc += X^T(t-1) Y(t-1) (X = dO, Y = P; or X = Q,
-//                          Y = dS), S(t) [and dP(t)];
-//   vector phase of tile t: P = exp2(S scale - lse) (masked), [dS = P (dP - D)],
-//                          packed to bf16.
-// Waves 4..7 run the same code one phase behind waves 0..3.  Splitting dk
-// and dv into two passes keeps each under the 256 registers two waves per
-// SIMD allow (both accumulators plus K, V, S and dP would not fit); the
-// price is computing S twice.
-template <int D, bool DIAG, bool DK>
-__global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
+// dv^T += dO^T P and dk^T += scale Q^T dS for one ring step in one launch.
+// A block holds 128 keys.  Waves w and w + 4 (one SIMD) hold the same 32
+// keys and split the work:
+//   wave w (S, P, dv): MFMA phase of tile t: dv^T += dO^T(t-1) P(t-1),
+//     S(t) = Q(t) K^T; vector phase: P = exp2(S scale - lse) (masked), packed
+//     to bf16, kept as its own B operand and written to LDS for its partner;
+//   wave w + 4 (dP, dS, dk), one phase behind: MFMA phase of tile t:
+//     dk^T += Q^T(t-1) dS(t-1), dP(t) = dO(t) V^T; vector phase: reads P(t)
+//     (written in the phase before), dS = P (dP - D), packed to bf16.
+// S is computed once per (query, key) pair in this kernel, and each wave
+// holds one accumulator and one register operand (K or V), which keeps two
+// waves per SIMD within the register file.  Both roles run the same MFMA phase code on runtime buffer offsets;
+// only the vector phases differ.  dS is formed from the bf16 P that also
+// feeds dv.  Tiles of Q and dO stream through four LDS buffers each, two
+// tiles ahead; the lse and D rows of a tile sit beside them.
+template <int D, bool DIAG>
+__global__ __launch_bounds__(64 * kKvfWaves) void bwd_kvf_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lse2g, const float* __restrict__ Dg,
-    float* __restrict__ outg, int Sq, int Sk, int n_ktiles, int total_tiles, float scale_log2, float scale,
-    int group, int qoff) {
-  constexpr int NW = kKvWaves, NKW = kKvKeysPerWave, BK = NW * NKW, BQ = kTileTokens;
-  constexpr int NKS = D / 16, NDB = D / 32, NQB = BQ / 32, TILE = BQ * D * 2, LA = kKvLookahead;
-  constexpr int NX = 4 * NDB, NS = (DK ? 2 : 1) * NKS * NQB, NOP = NX + NS;
-  // LDS: Q tiles in buffers 0..3, dO tiles in buffers 0..3 at DOFF, then the
-  // rows' lse and D (64 floats per tile each); tile j uses buffer j % 4.
-  constexpr int DOFF = 4 * TILE, LOFF = 8 * TILE, DLOFF = LOFF + 4 * BQ * 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[8 * TILE + 8 * BQ * 4];
+    float* __restrict__ dkg, float* __restrict__ dvg, int Sq, int Sk, int n_ktiles, int total_tiles,
+    float scale_log2, float scale, int group, int qoff) {
+  constexpr int NW = kKvfWaves, NKW = kKvfKeysPerWave, BK = (NW / 2) * NKW, BQ = kTileTokens;
+  constexpr int NKS = D / 16, NDB = D / 32, NQB = BQ / 32, TILE = BQ * D * 2, LA = kKvfLookahead;
+  constexpr int NX = 4 * NDB, NS = NKS * NQB, NOP = NX + NS;
+  // LDS: Q tiles in buffers 0..3, dO tiles in buffers 0..3 at DOFF, the rows'
+  // lse and D (64 floats per tile each), then one P tile per wave pair (bf16,
+  // word k of lane l at k * 1024 + 16 l); tile j uses buffer j % 4.
+  constexpr int DOFF = 4 * TILE, LOFF = 8 * TILE, DLOFF = LOFF + 4 * BQ * 4, POFF = DLOFF + 4 * BQ * 4;
+  constexpr int PSLOT = 2 * NQB * 64 * 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[POFF + (NW / 2) * PSLOT];
   auto qbuf = [&](int b) __attribute__((always_inline)) { return smem + b * TILE; };
   auto dbuf = [&](int b) __attribute__((always_inline)) { return smem + DOFF + b * TILE; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const bool lead = wave < NW / 2;  // waves 4..7 run one phase behind
+  const bool lead = wave < NW / 2;  // S, P, dv; waves 4..7 (dP, dS, dk) run one phase behind
+  const int pw = wave & (NW / 2 - 1);  // key group of the wave pair
   const int t = xcd_remap(blockIdx.x, total_tiles);
   const int bhk = t / n_ktiles;  // key/value head row; its query heads are bhk * group + [0, group)
   const int kt = t - bhk * n_ktiles;  // low key tiles see the most queries: they go first
   const int kb0 = kt * BK;
-  const int kw0 = kb0 + wave * NKW;
+  const int kw0 = kb0 + pw * NKW;
   const int kk = kw0 + l32;
   // Query-side rows of the query head being walked (set per head below).
   const uint16_t* __restrict__ qp = qg;
@@ -337,9 +350,9 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   const float* __restrict__ lp = lse2g;
   const float* __restrict__ Dp = Dg;
 
-  // Query tiles qs .. ntq-1; this wave's keys see tiles from ws on (causal:
-  // query q sees keys <= q + qoff).  A block whose keys no query sees
-  // (qs >= ntq) skips the walk and adds zero.
+  // Query tiles qs .. ntq-1; this pair's keys see tiles from ws on (causal:
+  // query q sees keys <= q + qoff).  A block whose keys no query sees skips
+  // the walk and adds zero.
   const int ntq = (Sq + BQ - 1) / BQ;
   const int qs = DIAG ? min(max(0, kb0 - qoff) / BQ, ntq) : 0;
   const int ws = DIAG ? min(max(qs, max(0, kw0 - qoff) / BQ), ntq) : qs;
@@ -352,8 +365,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
 #if defined(__HIP_DEVICE_COMPILE__)
     const int row = min(j * BQ + lane, Sq - 1);
     if (wave == 0) __builtin_amdgcn_global_load_lds(lp + row, (lds_void*)(smem + LOFF + (j & 3) * BQ * 4), 4, 0, 0);
-    if (DK && wave == 1)
-      __builtin_amdgcn_global_load_lds(Dp + row, (lds_void*)(smem + DLOFF + (j & 3) * BQ * 4), 4, 0, 0);
+    if (wave == 1) __builtin_amdgcn_global_load_lds(Dp + row, (lds_void*)(smem + DLOFF + (j & 3) * BQ * 4), 4, 0, 0);
 #endif
   };
   auto load_tile = [&](int j) __attribute__((always_inline)) {
@@ -370,29 +382,29 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     else load_rows(j);
   };
 
-  u32x4 kf[NKS], vf[DK ? NKS : 1];
+  // The register operand: K rows (S = Q K^T) or V rows (dP = dO V^T) of key kk.
+  u32x4 kvf[NKS];
   {
-    const uint16_t* krow = kg + ((size_t)bhk * Sk + kk) * D;
-    const uint16_t* vrow = vg + ((size_t)bhk * Sk + kk) * D;
+    const uint16_t* row = (lead ? kg : vg) + ((size_t)bhk * Sk + kk) * D;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      kf[s] = (kk < Sk) ? ld16(krow + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
-      if constexpr (DK) vf[s] = (kk < Sk) ? ld16(vrow + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int s = 0; s < NKS; ++s) kvf[s] = (kk < Sk) ? ld16(row + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
   }
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-  f32x16 sacc[NQB], pacc[DK ? NQB : 1];
+  f32x16 sacc[NQB];  // S (waves 0..3) or dP (waves 4..7) of the current tile
   u32x4 yb[NQB][2];  // P or dS of the last vector phase, bf16 (B operand of the product)
 
   const uint32_t base = lds_addr(smem);
-  uint32_t raddr[NKS];  // row-major operand (Q or dO) of row l32, chunk pair s
+  // Row-major operand of the scores (Q or dO) and transposed operand of the
+  // product (dO^T or Q^T), as buffer-0 addresses.
+  const uint32_t roff = lead ? 0u : (uint32_t)DOFF, xoff = lead ? (uint32_t)DOFF : 0u;
+  uint32_t raddr[NKS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) raddr[s] = base + (uint32_t)tile_off<D>(l32, 2 * s + g);
-  uint32_t taddr[NDB][2];  // transposed operand (dO^T or Q^T)
+  for (int s = 0; s < NKS; ++s) raddr[s] = base + roff + (uint32_t)tile_off<D>(l32, 2 * s + g);
+  uint32_t taddr[NDB][2];
   {
     const int m = (lane & 15) >> 2, a4 = lane & 3, half16 = (lane >> 4) & 1;
 #pragma unroll
@@ -400,13 +412,14 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
       const int d = db * 32 + 16 * half16 + 4 * a4;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        taddr[db][tt] = base + (DK ? 0u : (uint32_t)DOFF) + tile_off<D>(4 * g + m + 8 * tt, d >> 3) + ((d & 4) ? 8 : 0);
+        taddr[db][tt] = base + xoff + tile_off<D>(4 * g + m + 8 * tt, d >> 3) + ((d & 4) ? 8 : 0);
     }
   }
   const uint32_t laddr = base + LOFF + (uint32_t)(4 * g) * 4;  // this lane's rows 4g .. 4g+3 of a tile's lse
+  const uint32_t paddr = base + POFF + (uint32_t)(pw * PSLOT + lane * 16);
 
-  // MFMA phase: acc from the X buffer at xo (previous tile) and yb, then S
-  // from the Q buffer at bo [and dP from the dO buffer at bo].
+  // MFMA phase: acc from the X buffer at xo (previous tile) and yb, then the
+  // scores from the buffer at bo.
   auto mfma_phase = [&](uint32_t xo, uint32_t bo, auto&& hook) __attribute__((always_inline)) {
     u32x2 lo[LA + 1], hi[LA + 1];
     u32x4 rq[LA + 1];
@@ -423,9 +436,8 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
         lo[b] = ds_read_tr16_off<OFF>(taddr[db][0] + xo);
         hi[b] = ds_read_tr16_off<OFF>(taddr[db][1] + xo);
       } else if constexpr (m < NOP) {
-        constexpr int j = m - NX, s = j / (NS / NKS), r = j % (NS / NKS), qb = r % NQB;
-        if constexpr (r < NQB) rq[b] = ds_read_b128_off<qb * 32 * D * 2>(raddr[s] + bo);
-        else rq[b] = ds_read_b128_off<qb * 32 * D * 2>(raddr[s] + bo + (uint32_t)DOFF);
+        constexpr int j = m - NX, s = j / NQB, qb = j % NQB;
+        rq[b] = ds_read_b128_off<qb * 32 * D * 2>(raddr[s] + bo);
       }
     };
     auto run = [&](auto mc) __attribute__((always_inline)) {
@@ -438,15 +450,10 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
         const u32x4 a = {lo[b][0], lo[b][1], hi[b][0], hi[b][1]};
         acc[db] = mfma32(a, yb[gi >> 1][gi & 1], acc[db]);
       } else {
-        constexpr int j = m - NX, s = j / (NS / NKS), r = j % (NS / NKS), qb = r % NQB;
+        constexpr int j = m - NX, s = j / NQB, qb = j % NQB;
         lgkm_wait<N>(rq[b]);
-        if constexpr (r < NQB) {
-          if constexpr (s == 0) sacc[qb] = mfma32(rq[b], kf[0], f32x16{});
-          else sacc[qb] = mfma32(rq[b], kf[s], sacc[qb]);
-        } else {
-          if constexpr (s == 0) pacc[qb] = mfma32(rq[b], vf[0], f32x16{});
-          else pacc[qb] = mfma32(rq[b], vf[s], pacc[qb]);
-        }
+        if constexpr (s == 0) sacc[qb] = mfma32(rq[b], kvf[0], f32x16{});
+        else sacc[qb] = mfma32(rq[b], kvf[s], sacc[qb]);
       }
       hook(mc);
     };
@@ -454,49 +461,34 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     static_for<NOP>(run);
   };
 
-  // Vector phase of tile tt: Y = P or dS into yb.  Row i of accumulator qb
-  // is query 32*qb + 8*(i/4) + 4g + i%4 of the tile.
-  auto vector_phase = [&](int tt) __attribute__((always_inline)) {
+  // Vector phase of tile tt, waves 0..3: P into yb and the pair's LDS slot.
+  // Row i of accumulator qb is query 32*qb + 8*(i/4) + 4g + i%4 of the tile.
+  auto vector_p = [&](int tt) __attribute__((always_inline)) {
     const int q0 = tt * BQ;
     const bool masked = (q0 + BQ > Sq) || (DIAG && q0 + qoff < kw0 + NKW);
     const uint32_t lo_ = laddr + (uint32_t)((tt & 3) * BQ * 4);
-    // The lse (and D) values of accumulator qb's 32 rows, four rows per read,
-    // are requested JB row groups at a time and consumed in order with counted
-    // waits, so their LDS latency is paid once per batch, not once per read.
-    constexpr int R = DK ? 2 : 1;   // reads per row group
-    constexpr int JB = DK ? 2 : 4;  // row groups per batch (dk: fewer registers)
+    // The lse values of accumulator qb's 32 rows, four rows per read, are
+    // requested together and consumed in order with counted waits.
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-      static_for<4 / JB>([&](auto bc) __attribute__((always_inline)) {
-      u32x4 lrs[JB], drs[JB];
+    for (int qb = 0; qb < NQB; ++qb) {
+      u32x4 lrs[4];
 #pragma unroll
-      for (int jj = 0; jj < JB; ++jj) {
-        const int j = decltype(bc)::value * JB + jj;
-        lrs[jj] = ds_read_b128_off<0>(lo_ + (qb * 32 + 8 * j) * 4);
-        if constexpr (DK) drs[jj] = ds_read_b128_off<DLOFF - LOFF>(lo_ + (qb * 32 + 8 * j) * 4);
-      }
-      static_for<JB>([&](auto jc) __attribute__((always_inline)) {
-        constexpr int jj = decltype(jc)::value, j = decltype(bc)::value * JB + jj;
-        lgkm_wait<(JB - 1 - jj) * R>(lrs[jj]);
-        u32x4 lr = lrs[jj];
-        u32x4 dr = {0, 0, 0, 0};
-        if constexpr (DK) {
-          lgkm_wait<(JB - 1 - jj) * R>(drs[jj]);
-          dr = drs[jj];
-        }
+      for (int j = 0; j < 4; ++j) lrs[j] = ds_read_b128_off<0>(lo_ + (qb * 32 + 8 * j) * 4);
+      static_for<4>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        lgkm_wait<3 - j>(lrs[j]);
+        const u32x4 lr = lrs[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * j + e;
           // lse2 is +inf for a row that saw no key: P = 0.
-          const float p = fast_exp2(fmaf(sacc[qb][i], scale_log2, -as_float(lr[e])));
-          if constexpr (DK) sacc[qb][i] = p * (pacc[qb][i] - as_float(dr[e]));
-          else sacc[qb][i] = p;
+          sacc[qb][i] = fast_exp2(fmaf(sacc[qb][i], scale_log2, -as_float(lr[e])));
         }
       });
-      });
+    }
     // Masked tiles (the diagonal band, the ragged tail) zero the entries of
-    // rows past the chunk or of keys after the query, whatever was computed
-    // for them, in a pass of their own that full tiles skip.
+    // rows past the chunk or of keys after the query, in a pass of their own
+    // that full tiles skip.  dS of those entries is then zero too.
     if (masked) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
@@ -511,14 +503,59 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
       yb[qb][0] = pack8(sacc[qb], 0);
       yb[qb][1] = pack8(sacc[qb], 8);
     }
+    // Hand P to the partner wave; the writes complete before the barrier
+    // after which it reads them.
+    static_for<2 * NQB>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      ds_write_b128_off<k * 1024>(paddr, yb[k >> 1][k & 1]);
+    });
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  // Vector phase of tile tt, waves 4..7: dS = P (dP - D) into yb, with P(tt)
+  // from the partner's slot.
+  auto vector_ds = [&](int tt) __attribute__((always_inline)) {
+    const uint32_t lo_ = laddr + (uint32_t)((tt & 3) * BQ * 4);
+    u32x4 pk[NQB][2];
+    static_for<2 * NQB>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      pk[k >> 1][k & 1] = ds_read_b128_off<k * 1024>(paddr);
+    });
+    static_for<2 * NQB>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      lgkm_wait<0>(pk[k >> 1][k & 1]);
+    });
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      u32x4 drs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) drs[j] = ds_read_b128_off<DLOFF - LOFF>(lo_ + (qb * 32 + 8 * j) * 4);
+      static_for<4>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        lgkm_wait<3 - j>(drs[j]);
+        const u32x4 dr = drs[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * j + e;
+          const uint32_t w = pk[qb][i >> 3][(i & 7) >> 1];
+          const float p = as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+          sacc[qb][i] = p * (sacc[qb][i] - as_float(dr[e]));
+        }
+      });
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      yb[qb][0] = pack8(sacc[qb], 0);
+      yb[qb][1] = pack8(sacc[qb], 8);
+    }
   };
 
   // Tile tt's MFMA phase runs for ws <= tt <= ntq: at tt = ws Y is still zero
   // (the X buffer it multiplies holds finite data), and at tt = ntq only its
-  // product with the previous tile is used.
-  // The phase of tile tt also issues tile tt + 2's loads, one piece every
-  // EVERY MFMAs; a wave without that phase issues them all at once.  Tiles
-  // past the last one load zeros (or clamped rows) that nothing reads.
+  // product with the previous tile is used.  The phase of tile tt also issues
+  // tile tt + 2's loads, one piece every EVERY MFMAs; a wave without that
+  // phase issues them all at once.  Tiles past the last one load zeros (or
+  // clamped rows) that nothing reads.
   auto mfma_tile = [&](int tt) __attribute__((always_inline)) {
     constexpr int EVERY = NOP / NPC;
     if (tt >= ws && tt <= ntq) {
@@ -533,7 +570,10 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     }
   };
   auto vector_tile = [&](int tt) __attribute__((always_inline)) {
-    if (tt >= ws && tt < ntq) vector_phase(tt);
+    if (tt >= ws && tt < ntq) {
+      if (lead) vector_p(tt);
+      else vector_ds(tt);
+    }
   };
   // Grouped-query attention: the block's keys serve `group` query heads, walked
   // one after the other into the same accumulators (dk, dv sum over them).
@@ -545,19 +585,19 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
     dp = dog + (size_t)bh * Sq * D;
     lp = lse2g + (size_t)bh * Sq;
     Dp = Dg + (size_t)bh * Sq;
-    if (qs < ntq) {
-      load_tile(qs);
-      if (qs + 1 < ntq) load_tile(qs + 1);
-      // Finite data for the Y = 0 product of the first tile.
-      dma.load(DK ? qbuf((qs + 3) & 3) : dbuf((qs + 3) & 3), DK ? qp : dp, qs * BQ, Sq);
-    }
+    load_tile(qs);
+    if (qs + 1 < ntq) load_tile(qs + 1);
+    // Finite data in both X buffers of the Y = 0 product of the first tile.
+    dma.load(qbuf((qs + 3) & 3), qp, qs * BQ, Sq);
+    dma.load(dbuf((qs + 3) & 3), dp, qs * BQ, Sq);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) yb[qb][0] = yb[qb][1] = u32x4{0, 0, 0, 0};
-    // Iteration u: MFMA phase of tile u (reads Q(u), dO(u) and X(u-1)),
-    // vector phase of tile u.  The MFMA phase loads tile u + 2 into buffers
-    // whose last readers (tiles u - 2 and u - 1's products) finished two
-    // phases back for either wave group; the iteration ends waiting for that
-    // load.
+    // Iteration u: MFMA phase of tile u, vector phase of tile u.  Waves 4..7
+    // run one phase behind, so their vector phase of tile u follows the
+    // barrier after waves 0..3 wrote P(u).  The MFMA phase loads tile u + 2
+    // into buffers whose last readers (tiles u - 2 and u - 1's products)
+    // finished two phases back for either wave group; the iteration ends
+    // waiting for that load.
     wait_vmem();
     phase_barrier();
     if (!lead) phase_barrier();
@@ -572,8 +612,8 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_kv_kernel(
   }
 
   if (kk < Sk) {
-    float* row = outg + ((size_t)bhk * Sk + kk) * D;
-    const float f = DK ? scale : 1.f;
+    float* row = (lead ? dvg : dkg) + ((size_t)bhk * Sk + kk) * D;
+    const float f = lead ? 1.f : scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -607,7 +647,7 @@ hipError_t launch_dq_d(const BwdStepArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_dkdv_d(const BwdStepArgs& a, hipStream_t stream) {
-  constexpr int BK = kKvWaves * kKvKeysPerWave;
+  constexpr int BK = (kKvfWaves / 2) * kKvfKeysPerWave;
   const int nk = (a.Sk + BK - 1) / BK;
   if (a.group < 1 || a.BH % a.group || a.qoff < 0 || (long long)a.Sq + a.Sk + a.qoff + 1024 > 0x7fffffffLL)
     return hipErrorInvalidValue;
@@ -615,18 +655,13 @@ hipError_t launch_dkdv_d(const BwdStepArgs& a, hipStream_t stream) {
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   if (total == 0) return hipSuccess;
   const float sl2 = a.scale * kLog2e;
-  const dim3 grid((unsigned)total), block(64 * kKvWaves);
-#define RA_KV_LAUNCH(DIAG, DK, OUT)                                                                               \
-  hipLaunchKernelGGL((bwd_kv_kernel<D, DIAG, DK>), grid, block, 0, stream, a.q, a.k, a.v, a.dO, a.lse2, a.D, OUT, \
-                     a.Sq, a.Sk, nk, (int)total, sl2, a.scale, a.group, a.qoff)
-  if (a.diag) {
-    RA_KV_LAUNCH(true, false, a.dv);
-    RA_KV_LAUNCH(true, true, a.dk);
-  } else {
-    RA_KV_LAUNCH(false, false, a.dv);
-    RA_KV_LAUNCH(false, true, a.dk);
-  }
-#undef RA_KV_LAUNCH
+  const dim3 grid((unsigned)total), block(64 * kKvfWaves);
+  if (a.diag)
+    hipLaunchKernelGGL((bwd_kvf_kernel<D, true>), grid, block, 0, stream, a.q, a.k, a.v, a.dO, a.lse2, a.D, a.dk,
+                       a.dv, a.Sq, a.Sk, nk, (int)total, sl2, a.scale, a.group, a.qoff);
+  else
+    hipLaunchKernelGGL((bwd_kvf_kernel<D, false>), grid, block, 0, stream, a.q, a.k, a.v, a.dO, a.lse2, a.D, a.dk,
+                       a.dv, a.Sq, a.Sk, nk, (int)total, sl2, a.scale, a.group, a.qoff);
   return hipGetLastError();
 }
 
