@@ -83,10 +83,16 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const bool lead = wave < NW / 2;  // waves 4..7 run one phase behind
-  const int t = xcd_remap(blockIdx.x, total_tiles);
-  const int bh = t / n_qtiles;
-  int qt = t - bh * n_qtiles;
-  if (DIAG) qt = n_qtiles - 1 - qt;  // longest rows of the triangle first
+  int bh, qt;
+  if constexpr (DIAG) {
+    // Causal: the last query tiles see the most keys; they go first.
+    longest_first(blockIdx.x, total_tiles / n_qtiles, bh, qt);
+    qt = n_qtiles - 1 - qt;
+  } else {
+    const int t = xcd_remap(blockIdx.x, total_tiles);
+    bh = t / n_qtiles;
+    qt = t - bh * n_qtiles;
+  }
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * NQW;
   const int qq = qw0 + l32;
@@ -338,9 +344,16 @@ __global__ __launch_bounds__(64 * kKvfWaves) void bwd_kvf_kernel(
   const int l32 = lane & 31, g = lane >> 5;
   const bool lead = wave < NW / 2;  // S, P, dv; waves 4..7 (dP, dS, dk) run one phase behind
   const int pw = wave & (NW / 2 - 1);  // key group of the wave pair
-  const int t = xcd_remap(blockIdx.x, total_tiles);
-  const int bhk = t / n_ktiles;  // key/value head row; its query heads are bhk * group + [0, group)
-  const int kt = t - bhk * n_ktiles;  // low key tiles see the most queries: they go first
+  // Key/value head row bhk (its query heads are bhk * group + [0, group)) and
+  // key tile kt.  Causal: low key tiles see the most queries; they go first.
+  int bhk, kt;
+  if constexpr (DIAG) {
+    longest_first(blockIdx.x, total_tiles / n_ktiles, bhk, kt);
+  } else {
+    const int t = xcd_remap(blockIdx.x, total_tiles);
+    bhk = t / n_ktiles;
+    kt = t - bhk * n_ktiles;
+  }
   const int kb0 = kt * BK;
   const int kw0 = kb0 + pw * NKW;
   const int kk = kw0 + l32;

@@ -65,6 +65,18 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// Block b's (head row, level) in a causal launch whose blocks shrink with the
+// level: level 0 (the longest block of every head) for all n_bh head rows
+// first, then level 1, and so on.  Consecutive blocks go round-robin over the
+// XCDs, so every XCD receives its blocks longest first; when n_bh is a
+// multiple of the XCD count, an XCD holds the same head rows at every level
+// (their K/V lines stay in its L2).  Ordering the levels within each head
+// only would start some heads' longest blocks near the end of the launch.
+__device__ __forceinline__ void longest_first(int b, int n_bh, int& bh, int& level) {
+  level = b / n_bh;
+  bh = b - level * n_bh;
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 

@@ -38,7 +38,7 @@
 //    2^8.
 //  * Blocks are mapped so each XCD works on one contiguous range of
 //    (head, query tile) pairs (K/V lines shared in that XCD's L2); on the
-//    diagonal chunk the longest query tiles go first.
+//    diagonal chunk the longest query tiles of every head go first.
 #include <type_traits>
 
 #include "ra_device.h"
@@ -156,10 +156,16 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
   const int l32 = lane & 31, g = lane >> 5;
-  const int t = xcd_remap(blockIdx.x, total_tiles);
-  const int bh = t / n_qtiles;
-  int qt = t - bh * n_qtiles;
-  if (DIAG) qt = n_qtiles - 1 - qt;  // longest rows of the triangle first
+  int bh, qt;
+  if constexpr (DIAG) {
+    // Causal: the last query tiles see the most keys; they go first.
+    longest_first(blockIdx.x, total_tiles / n_qtiles, bh, qt);
+    qt = n_qtiles - 1 - qt;
+  } else {
+    const int t = xcd_remap(blockIdx.x, total_tiles);
+    bh = t / n_qtiles;
+    qt = t - bh * n_qtiles;
+  }
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * NQW;
   const int qq = qw0 + l32;
