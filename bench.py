@@ -55,6 +55,67 @@ def fwd_kernel_sha():
     return h.hexdigest()[:16]
 
 
+COUNTER_KERNEL = "fwd_step_kernel<128, false, true>"  # the full-chunk step with the fused merge
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def ingest_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
+    """Turn two rocprofv3 counter passes over the default forward walk (one
+    with FETCH_SIZE, one with WRITE_SIZE, in KiB per dispatch) into the HBM
+    bytes per full-chunk launch that `roofline.traffic` reports.  Each counter
+    is scaled by what it reads for the 256 MiB key/value staging copies of the
+    same run (a plain copy of known size), then stamped with the forward
+    kernel's source hash so that a later change to the kernel voids it."""
+    import csv
+    import glob
+    from long_context_exact_step_amd.workloads import WORKLOADS
+
+    def values(d, counter):
+        out = {"kernel": [], "copy": []}
+        paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not paths:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for path in paths:
+            with open(path, newline="") as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") != counter:
+                        continue
+                    name = r.get("Kernel_Name", "")
+                    if COUNTER_KERNEL in name:
+                        out["kernel"].append(float(r["Counter_Value"]))
+                    elif COPY_KERNEL in name:
+                        out["copy"].append(float(r["Counter_Value"]))
+        if not out["kernel"] or not out["copy"]:
+            raise SystemExit(f"{d}: no {counter} rows for {COUNTER_KERNEL} and the staging copies")
+        return out
+
+    w = WORKLOADS[2]
+    chunk_kib = w.B * w.H * w.C * w.d * 2 / 1024  # one K or V chunk, bf16
+    mean = lambda v: sum(v) / len(v)
+    # The largest copies of the run are the chunk staging copies.
+    big = lambda v: [x for x in v if x >= 0.95 * max(v)]
+    fe, wr = values(fetch_dir, "FETCH_SIZE"), values(write_dir, "WRITE_SIZE")
+    ff, wf = chunk_kib / mean(big(fe["copy"])), chunk_kib / mean(big(wr["copy"]))
+    fetch_b = mean(fe["kernel"]) * ff * 1024
+    write_b = mean(wr["kernel"]) * wf * 1024
+    rec = {
+        "kernel": COUNTER_KERNEL, "workload_id": w.id,
+        "workload": w.name + " (full-chunk merge step)", "source_sha": fwd_kernel_sha(),
+        "dispatches": {"fetch": len(fe["kernel"]), "write": len(wr["kernel"])},
+        "fetch_kib_per_dispatch_raw": mean(fe["kernel"]), "write_kib_per_dispatch_raw": mean(wr["kernel"]),
+        "copy_calibration": {"kernel": COPY_KERNEL + " (256 MiB chunk staging copy, same runs)",
+                             "fetch_kib_raw": mean(big(fe["copy"])), "write_kib_raw": mean(big(wr["copy"])),
+                             "fetch_factor": ff, "write_factor": wf},
+        "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "command_fetch": cmd_fetch, "command_write": cmd_write,
+    }
+    with open(PROFILE_COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 class HipEvents:
     """Timing-enabled hipEvent_t handles made through the HIP runtime."""
 
@@ -447,7 +508,12 @@ def main():
     ap.add_argument("--no-allgather", action="store_true", help="skip the all-gather sequence-parallel share")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA throughput probe")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CMD_FETCH", "CMD_WRITE"),
+                    help="write the forward kernel's HBM traffic from two rocprofv3 counter passes (no GPU used)")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the ring on a single MI355X; multi-GPU runs "
               "(--gpus > 1) are not supported.", file=sys.stderr)
