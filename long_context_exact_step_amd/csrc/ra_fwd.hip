@@ -204,6 +204,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float mrow = kNegInf, lrow = 0.f;
+  float mref = 0.f;  // exponent reference: mrow, or 0 while the row has seen no key
   // S^T of tiles t (being softmaxed) and t + 1 (being computed): sacc[t % 2].
   f32x16 sacc[2][NKB];
   // P^T in bf16: P^T(t-1) while iteration t multiplies it, overwritten in
@@ -330,6 +331,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
       for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     lrow = lrow * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
     mrow = mnew;
+    mref = mb;
   };
 
   // Piece k of step tt's loads: V(tt+1) replaces V(tt-3) and K(tt+3)
@@ -348,8 +350,8 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   auto iteration = [&](int tt, auto ic) __attribute__((always_inline)) {
     constexpr int I = decltype(ic)::value;
     f32x16(&sc)[NKB] = sacc[I % 2];
-    const float mb = (mrow == kNegInf) ? 0.f : mrow;
-    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+    const float mb = mref;
+    float l4[4];
     // Each element runs as three stages in three consecutive slots (scale,
     // exp2, sum and pack), so no instruction waits on one issued in its own
     // slot.  xs / ps hold the elements between stages, by element index.
@@ -360,8 +362,12 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
     auto exp_stage = [&](int e) __attribute__((always_inline)) { ps[e] = fast_exp2(xs[e]); };
     auto sum_stage = [&](int e) __attribute__((always_inline)) {
       const int kb = e >> 4, i = e & 15;
-      l4[i & 3] += ps[e];
-      asm volatile("" : "+v"(l4[i & 3]));  // keeps the sum in this slot
+      if (e < 4) {
+        l4[i & 3] = ps[e];  // elements 0..3 start the four partial sums
+      } else {
+        l4[i & 3] += ps[e];
+        asm volatile("" : "+v"(l4[i & 3]));  // keeps the sum in this slot
+      }
       if (i & 1) pb[kb][i >> 3][(i & 7) >> 1] = pack_bf16(ps[e - 1], ps[e]);
     };
     // Slots SH .. NOP-1 take the elements in order, spread evenly: slot m
