@@ -129,10 +129,11 @@ constexpr int kBufWord3 = 0x00020000;
 // issues its share of the tile's 1 KB pieces; piece p fills LDS bytes
 // [1024p, 1024p+1024) of the tile in lane order, so lane l loads the global
 // chunk that belongs at physical slot l of the piece.  The tile's first row
-// is the buffer resource's base and the rows left in the matrix set its size,
-// so the per-lane offset is the same for every tile (no vector arithmetic per
-// piece), and rows past the end fail the buffer range check, which writes
-// zeros to LDS instead of reading out of bounds.
+// is the buffer resource's base and the tile's rows that exist in the matrix
+// (at most TOK) set its size, so the per-lane offset is the same for every
+// tile (no vector arithmetic per piece), and rows past the end fail the
+// buffer range check, which writes zeros to LDS instead of reading out of
+// bounds.
 template <int D, int NW, int TOK = kTileTokens>
 struct TileBufDma {
   static constexpr int kPieces = TOK * D * 2 / 1024;
@@ -158,7 +159,9 @@ struct TileBufDma {
   // the arguments other than the piece index are wave-uniform.
   __device__ __forceinline__ void load_piece(int i, uint8_t* tile, const uint16_t* mat, int t0, int n) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int rows = n > t0 ? n - t0 : 0;
+    // The resource covers this tile only: its byte size stays far below the
+    // 32-bit record count however long the matrix is.
+    const int rows = n > t0 ? min(n - t0, TOK) : 0;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(mat) + (size_t)t0 * D, 0, rows * (D * 2), kBufWord3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + (piece0 + i) * 1024), 16, off[i], 0, 0, 0);

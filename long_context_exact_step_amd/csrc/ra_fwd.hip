@@ -203,7 +203,10 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float mrow = kNegInf, lrow = 0.f;
+  // Running row sum, compensated: lrow - lcomp is the sum.  Over a long chunk
+  // each tile adds far less than the sum holds, and plain fp32 accumulation
+  // would drift by up to (tiles x 2^-25) of it.
+  float mrow = kNegInf, lrow = 0.f, lcomp = 0.f;
   float mref = 0.f;  // exponent reference: mrow, or 0 while the row has seen no key
   // S^T of tiles t (being softmaxed) and t + 1 (being computed): sacc[t % 2].
   f32x16 sacc[2][NKB];
@@ -329,7 +332,8 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    lrow = lrow * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
+    lrow = (lrow - lcomp) * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
+    lcomp = 0.f;
     mrow = mnew;
     mref = mb;
   };
@@ -398,7 +402,11 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
       const bool masked = (k0 + BC > Sk) || (DIAG && k0 + BC - 1 > qw0 + qoff);
       const float lt = (l4[0] + l4[1]) + (l4[2] + l4[3]);
       if (masked || __ballot(!(lt <= kLazyBound) || mrow == kNegInf) != 0) softmax_exact(tt, sc);
-      else lrow += lt;
+      else {
+        const float y = lt - lcomp, sum = lrow + y;
+        lcomp = (sum - lrow) - y;
+        lrow = sum;
+      }
     }
   };
   auto step = [&](int tt, auto ic) __attribute__((always_inline)) {
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   // Reads issued for an iteration that never ran.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-  fwd_epilogue<D, MERGE>(oacc, mrow, lrow, og, lseg, bh, Sq, qq, g);
+  fwd_epilogue<D, MERGE>(oacc, mrow, lrow - lcomp, og, lseg, bh, Sq, qq, g);
 }
 
 template <int D>

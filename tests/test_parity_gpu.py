@@ -98,6 +98,40 @@ def test_ring_fwd_every_rank(P, C, d, causal, mode):
         assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_maximum_chunk_length(d):
+    """A key chunk longer than 2^32 bytes (2^24 + 100 tokens at d = 128,
+    2^25 + 100 at d = 64; the host accepts any B*H*S < 2^31).  Every key is
+    zero except keys 100..127, which carry k = 2 and v = 1 against q = 1: their
+    score s = 2 sqrt(d) dominates, and with 28 such keys among N
+        O = 28 e^s / (28 e^s + N - 28),  lse = ln(28 e^s + N - 28).
+    Those keys sit in the second 64-key tile, whose rows counted from the
+    tile to the end of the chunk are just past 2^32 bytes: a tile resource
+    sized by the rows left in the matrix would wrap there and read them as
+    zeros (O = 0, lse = ln N)."""
+    n = (1 << (32 - (d * 2).bit_length() + 1)) + 100
+    print(f"maximum chunk length d={d} keys={n}", flush=True)
+    assert n * d * 2 > 1 << 32
+    q = torch.ones(1, 1, 256, d, dtype=torch.bfloat16, device=dev())
+    k = torch.zeros(1, 1, n, d, dtype=torch.bfloat16, device=dev())
+    v = torch.zeros(1, 1, n, d, dtype=torch.bfloat16, device=dev())
+    k[:, :, 100:128] = 2
+    v[:, :, 100:128] = 1
+    scale = 1 / math.sqrt(d)
+    o = torch.full((1, 1, 256, d), float("nan"), device=dev())
+    lse = torch.full((1, 1, 256), float("nan"), device=dev())
+    ra.step_fwd(q, k, v, o, lse, 1, False, scale)
+    torch.cuda.synchronize()
+    del k, v
+    torch.cuda.empty_cache()
+    s = 2 * d * scale
+    big = 28 * math.exp(s)
+    o_ref = big / (big + n - 28)
+    lse_ref = math.log(big + n - 28)
+    assert_close(f64(o), np.full((1, 1, 256, d), o_ref), TOL_O, "o")
+    assert_close(f64(lse), np.full((1, 1, 256), lse_ref), TOL_LSE, "lse", rel=None)
+
+
 def test_steps_plus_merge_equal_fused_ring():
     """The unfused path (ra_step_fwd per chunk + ra_lse_merge) and the fused
     ring walk agree, and merge order does not matter."""
