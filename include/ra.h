@@ -25,7 +25,9 @@
  *     a row has seen; o is normalised (the softmax-weighted mean of v).  A
  *     row that has seen no key has o = 0 and lse = -inf.
  *   d must be 64 or 128; B, H and every sequence length must be >= 1 (any
- *     length: ragged tails are masked in the kernels).
+ *     length: ragged tails are masked in the kernels).  B * H * S must stay
+ *     below 2^31 for every tensor (RA_ERR_SHAPE otherwise); a single chunk
+ *     may exceed 4 GiB.
  *   Every device pointer must be 16-byte aligned.
  *   Causality is over global positions with the diagonal included: query at
  *     global position p sees key positions <= p.  Chunk j holds global
