@@ -222,6 +222,41 @@ def test_ring_bwd_matches_oracle(P, C, d, causal):
             assert_close(f64(dv[j]), rv[:, :, sl], TOL_GRAD, f"dv chunk {j}")
 
 
+@pytest.mark.parametrize("scale", [0.03, 0.5])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ring_walk_other_scales(scale, d):
+    """The softmax scale is an argument: forward and backward at scales far
+    from 1/sqrt(d) (flat and peaked softmax).  At the peaked scale the
+    gradients reach ~18 and P and dS are rounded to bf16 for the MFMAs, so
+    the gradients' max-abs bound is 3e-2 of the largest reference gradient
+    when that exceeds 1 (the relative Frobenius bound of 1e-2 applies as
+    everywhere)."""
+    B, H, P, C, rank = 1, 2, 3, 150, 2
+    print(f"ring fwd/bwd scale={scale} d={d}", flush=True)
+    q, k, v, do = ring_tensors(112, B, H, P, C, d, with_do=True, ranks=[rank])
+    qd, dod = q[rank].to(dev()), do[rank].to(dev())
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    o = torch.empty(B, H, C, d, device=dev())
+    lse = torch.empty(B, H, C, device=dev())
+    ra.ring_fwd(qd, kd, vd, o, lse, rank, True, scale, ring_mode="resident")
+    dq = torch.empty(B, H, C, d, device=dev())
+    dk = [torch.zeros(B, H, C, d, device=dev()) for _ in range(P)]
+    dv = [torch.zeros(B, H, C, d, device=dev()) for _ in range(P)]
+    ra.ring_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, rank, True, scale)
+    torch.cuda.synchronize()
+    kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
+    pos = rank * C + np.arange(C)
+    ro, rl = oracle.attention_fwd(f64(q[rank]), kf, vf, scale, True, q_pos=pos)
+    rq, rk, rv = oracle.attention_bwd(f64(q[rank]), kf, vf, f64(do[rank]), scale, True, q_pos=pos)
+    assert_close(f64(o), ro, TOL_O, "o")
+    assert_close(f64(lse), rl, TOL_LSE, "lse", rel=None)
+    bound = lambda ref: TOL_GRAD * max(1.0, float(np.abs(ref).max()))
+    assert_close(f64(dq), rq, bound(rq), "dq")
+    assert_close(f64(torch.cat(dk, dim=2)), rk, bound(rk), "dk")
+    assert_close(f64(torch.cat(dv, dim=2)), rv, bound(rv), "dv")
+
+
 def test_ring_bwd_accumulates_over_ranks():
     """Walking every rank's share into the same dK_j/dV_j accumulators gives
     the full-sequence gradient."""
