@@ -20,9 +20,10 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(float* __restrict__ o, f
                                                         const float* __restrict__ op,
                                                         const float* __restrict__ lp, int rows) {
   constexpr int LPR = D / 4;
-  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  const int row = gid / LPR, c = gid % LPR;
-  if (row >= rows) return;
+  // 64-bit thread index: rows * LPR passes 2^31 from 2^31 / LPR rows on.
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)rows * LPR) return;
+  const int row = (int)(gid / LPR), c = (int)(gid % LPR);
   const float la = lse[row], lb = lp[row];
   const float M = fmaxf(la, lb);
   float wa = 0.f, wb = 0.f, lnew = kNegInf;
@@ -57,9 +58,10 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
                                                      float* __restrict__ out, float* __restrict__ lse2,
                                                      int rows) {
   constexpr int VPL = D / 32;
-  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  const int row = gid >> 5, c = gid & 31;
-  const bool ok = row < rows;
+  // 64-bit thread index: rows * 32 passes 2^31 from 2^26 rows on.
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool ok = gid < (long long)rows * 32;
+  const int row = (int)(gid >> 5), c = (int)(gid & 31);
   float acc = 0.f;
   if (ok) {
     const size_t off = (size_t)row * D + c * VPL;

@@ -73,6 +73,32 @@ def test_lse_merge_matches_oracle():
     assert_close(f64(go), ro, 1e-5, "merged o")
 
 
+def test_lse_merge_past_2_26_rows():
+    """ra_lse_merge over 2^26 + 2000 rows at d = 128: the merge kernel's
+    thread count, rows x 32, passes 2^31 there (the host accepts any
+    B*H*S < 2^31).  Constant operands give closed forms for every row:
+    o <- (e^la a + e^lb b) / (e^la + e^lb), lse <- ln(e^la + e^lb)."""
+    B, H, S, d = 1, 2, (1 << 25) + 1000, 128
+    print(f"lse_merge rows={B * H * S}", flush=True)
+    a, b, la, lb = 1.0, 3.0, 0.5, -0.25
+    o = torch.full((B, H, S, d), a, device=dev())
+    op = torch.full((B, H, S, d), b, device=dev())
+    lse = torch.full((B, H, S), la, device=dev())
+    lp = torch.full((B, H, S), lb, device=dev())
+    ra.lse_merge(o, lse, op, lp)
+    torch.cuda.synchronize()
+    del op, lp
+    tot = math.exp(la) + math.exp(lb)
+    o_ref = (math.exp(la) * a + math.exp(lb) * b) / tot
+    lse_ref = math.log(tot)
+    omin, omax = (x.item() for x in torch.aminmax(o))
+    lmin, lmax = (x.item() for x in torch.aminmax(lse))
+    del o, lse
+    torch.cuda.empty_cache()
+    assert abs(omin - o_ref) < 1e-5 and abs(omax - o_ref) < 1e-5, (omin, omax, o_ref)
+    assert abs(lmin - lse_ref) < 1e-5 and abs(lmax - lse_ref) < 1e-5, (lmin, lmax, lse_ref)
+
+
 @pytest.mark.parametrize("P,C,d,causal", [
     (1, 100, 128, True), (2, 3, 64, True), (4, 100, 128, True), (3, 129, 64, False),
     (4, 64, 128, False), (2, 200, 128, True),
