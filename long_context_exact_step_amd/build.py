@@ -3,7 +3,8 @@
     python -m long_context_exact_step_amd.build
 
 Each HIP source is compiled to an object under <repo>/_build/ in parallel and
-linked into long_context_exact_step_amd/libra.so.  Always rebuilds.
+linked into long_context_exact_step_amd/libra.so; the plain-C client
+(csrc/ra_client.c) is then built beside it as ra_client.  Always rebuilds.
 """
 
 import os
@@ -17,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libra.so")
+CLIENT = os.path.join(PKG, "ra_client")
 SOURCES = ["ra_api.hip", "ra_fwd.hip", "ra_merge.hip", "ra_bwd.hip", "ra_ceiling.hip"]
 ARCH = "gfx950"
 
@@ -62,7 +64,25 @@ def build(verbose=False, extra_flags=(), out=LIB):
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}", file=sys.stderr)
+    if out == LIB:
+        client = build_client()
+        if verbose:
+            print(f"built {client}", file=sys.stderr)
     return out
+
+
+def build_client():
+    """ra_client: a plain-C program that drives the library through
+    include/ra.h alone (C11, host code, linked against libra.so and the HIP
+    runtime)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = CLIENT + ".tmp"
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          "-I" + INCLUDE, "-I" + os.path.join(rocm, "include"), os.path.join(CSRC, "ra_client.c"),
+          "-L" + PKG, "-lra", "-L" + os.path.join(rocm, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp])
+    os.replace(tmp, CLIENT)
+    return CLIENT
 
 
 if __name__ == "__main__":

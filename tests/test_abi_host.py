@@ -250,3 +250,16 @@ def test_probe_helpers_validation(L):
     assert L.ra_mfma_probe(vp(FAKE), vp(FAKE), vp(FAKE), 0, 1, None) == RA_ERR_SHAPE
     assert L.ra_mfma_probe(vp(FAKE), vp(FAKE), vp(FAKE), 4, 0, None) == RA_ERR_SHAPE
 
+
+
+def test_c_client_links_and_reports_usage():
+    """ra_client (csrc/ra_client.c) is plain C11 against include/ra.h: it
+    links against libra.so and the HIP runtime, and without arguments prints
+    its usage and exits with status 2 before touching the GPU."""
+    import subprocess
+    client = os.path.join(ROOT, "long_context_exact_step_amd", "ra_client")
+    if not os.path.exists(client):
+        pytest.skip("ra_client is not built (__graft_entry__.build() builds it)")
+    r = subprocess.run([client], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "usage: ra_client IN OUT" in r.stderr
