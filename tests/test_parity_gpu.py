@@ -103,8 +103,10 @@ def test_lse_merge_past_2_26_rows():
     (1, 100, 128, True), (2, 3, 64, True), (4, 100, 128, True), (3, 129, 64, False),
     (4, 64, 128, False), (2, 200, 128, True),
 ])
-@pytest.mark.parametrize("mode", ["resident", "double_buffer"])
+@pytest.mark.parametrize("mode", ["resident", "double_buffer", "double_buffer_one_stream"])
 def test_ring_fwd_every_rank(P, C, d, causal, mode):
+    """double_buffer_one_stream: staging copies serialized on the compute
+    stream (no copy stream given)."""
     B, H = 1, 2
     q, k, v, _ = ring_tensors(102, B, H, P, C, d)
     kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
@@ -112,11 +114,12 @@ def test_ring_fwd_every_rank(P, C, d, causal, mode):
     vd = [t.to(dev()) for t in v]
     scale = 1 / math.sqrt(d)
     copy_stream = torch.cuda.Stream() if mode == "double_buffer" else None
+    ring_mode = "resident" if mode == "resident" else "double_buffer"
     for rank in range(P):
         print(f"ring_fwd P={P} C={C} d={d} causal={causal} mode={mode} rank={rank}", flush=True)
         o = torch.full((B, H, C, d), float("nan"), device=dev())
         lse = torch.full((B, H, C), float("nan"), device=dev())
-        ra.ring_fwd(q[rank].to(dev()), kd, vd, o, lse, rank, causal, scale, ring_mode=mode,
+        ra.ring_fwd(q[rank].to(dev()), kd, vd, o, lse, rank, causal, scale, ring_mode=ring_mode,
                     copy_stream=copy_stream)
         torch.cuda.synchronize()
         ro, rl = oracle.attention_fwd(f64(q[rank]), kf, vf, scale, causal, q_pos=rank * C + np.arange(C))
