@@ -17,8 +17,9 @@ parallelism on the same sequence, under "ulysses".  And (unless
 --no-allgather): the same rank's share of all-gather sequence parallelism
 (gathered key/value chunks, one pass at a causal offset), forward and
 training step, under "allgather".  And (unless --no-ceiling): the bf16 peak
-derived from the device's CU count and clock, and what a dense MFMA probe
-sustains on random and on zero operands, under "mfma_ceiling".
+derived from the device's CU count and clock, what a dense MFMA probe
+sustains on random and on zero operands, and one full-chunk step kernel on
+the workload's random inputs and on zeros, under "mfma_ceiling".
 
 Prints ONE JSON line: throughput in algorithmic TFLOP/s (4*d flops per
 visible (query, key) pair forward, 10*d backward), tokens/s, the roofline of
@@ -443,6 +444,40 @@ def mfma_ceiling(iters=200000):
     return out
 
 
+def step_on_zeros(w, launches=5):
+    """One full-chunk forward step (ra_step_fwd, no mask) at the workload's
+    chunk shape on its seeded N(0,1) inputs and on all-zero inputs.  The
+    instructions are the same; only the data, and so the matrix cores' power
+    and the clock the chip holds, differ.  The zero-input rate shows what the
+    kernel's schedule reaches at the unthrottled clock."""
+    import torch
+    import long_context_exact_step_amd as ra
+    from long_context_exact_step_amd import inputs
+
+    dev = torch.device("cuda", 0)
+    B, H, C, d = w.B, w.H, w.C, w.d
+    flops = 4 * d * B * H * C * C
+    q = inputs.chunk(w.id, inputs.Q, w.ranks[-1], B, H, C, d).to(dev)
+    k = inputs.chunk(w.id, inputs.K, 0, B, H, C, d).to(dev)
+    v = inputs.chunk(w.id, inputs.V, 0, B, H, C, d).to(dev)
+    o = torch.empty(B, H, C, d, device=dev)
+    lse = torch.empty(B, H, C, device=dev)
+    out = {"kernel": "fwd_step_kernel, full chunk, no merge", "C": C, "H": H}
+    for name, (qq, kk, vv) in {"random": (q, k, v), "zero": tuple(torch.zeros_like(t) for t in (q, k, v))}.items():
+        ra.step_fwd(qq, kk, vv, o, lse, 1, False, w.scale)  # warm-up
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(launches):
+            ra.step_fwd(qq, kk, vv, o, lse, 1, False, w.scale)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / launches
+        out[name] = {"ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def cpu_baseline(w, tensors, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample: 256 seeded query
     rows per head of the measured rank, heads taken in order until the time
@@ -566,10 +601,14 @@ def main():
     if not args.no_ceiling:
         ce = mfma_ceiling()
         ce["kernel_frac_of_random_ceiling"] = round(achieved / ce["random"]["tflops"], 4)
+        ce["step_kernel_by_input_data"] = step_on_zeros(w)
         out["mfma_ceiling"] = ce
         print(f"[bench] MFMA probe: random {ce['random']['tflops']} TFLOP/s at {ce['random']['clock_ghz']} GHz, "
               f"zero {ce['zero']['tflops']} TFLOP/s at {ce['zero']['clock_ghz']} GHz; derived peak "
               f"{ce['derived_peak_tflops']}", file=sys.stderr, flush=True)
+        sz = ce["step_kernel_by_input_data"]
+        print(f"[bench] full-chunk step kernel: random inputs {sz['random']['tflops']} TFLOP/s, zero inputs "
+              f"{sz['zero']['tflops']} TFLOP/s", file=sys.stderr, flush=True)
     if not args.no_cpu:
         cb, par = cpu_baseline(w, tensors, args.cpu_seconds)
         out["cpu_baseline"] = cb
