@@ -1,8 +1,9 @@
-"""The ring walk captured in a HIP graph.  The library launches kernels and
-device-to-device copies on the caller's streams and orders the staging slots
-with events; it enqueues no memset, allocation or synchronisation, so a
+"""The library's calls captured in a HIP graph.  The library launches kernels
+and device-to-device copies on the caller's streams and orders the staging
+slots with events; it enqueues no memset, allocation or synchronisation, so a
 caller may capture a whole training step (forward walk in double-buffer mode
-with its copy stream, backward walk) and replay it.  Every replay must give
+with its copy stream, backward walk; or the Ulysses or all-gather share's
+forward and backward) and replay it.  Every replay must give
 the eager result bit for bit, with the program's own eager work and
 synchronisations between replays, and a replay after the inputs change in
 place must match an eager run on the new inputs."""
@@ -97,3 +98,64 @@ def test_captured_training_step_replays_bit_identical(B, H, H_kv, P, C, d, rank,
     torch.cuda.synchronize()
     _same(got, s.outputs(), "replay on new inputs")
     assert not torch.equal(got[0], want[0]), "the replay did not read the new inputs"
+
+
+def _replays_match(run, outputs, reps=3):
+    """Eager run, capture, then replays with eager work between them: every
+    replay must reproduce the eager outputs bit for bit."""
+    run()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        for t in outputs:
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        _same([t.clone() for t in outputs], want, f"replay {rep}")
+        run()  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_captured_ulysses_and_allgather_shares():
+    """The other two parallel shares (2D regroup / gather copies, the row
+    pre-pass and the step kernels) captured and replayed likewise."""
+    B, H, Hk, P, C, d, rank = 1, 4, 2, 2, 130, 128, 1
+    print(f"graph ulysses/allgather B={B} H={H} H_kv={Hk} P={P} C={C} d={d} rank={rank}", flush=True)
+    scale = 1 / math.sqrt(d)
+    q, k, v, do = ring_tensors(114, B, H, P, C, d, with_do=True)
+    qc = [q[r].to(dev()) for r in range(P)]
+    dc = [do[r].to(dev()) for r in range(P)]
+    kc = [t.to(dev()) for t in k]
+    vc = [t.to(dev()) for t in v]
+    S, Hs = P * C, H // P
+    uo = torch.empty(B, Hs, S, d, device=dev())
+    ul = torch.empty(B, Hs, S, device=dev())
+    udq, udk, udv = (torch.empty(B, Hs, S, d, device=dev()) for _ in range(3))
+    uws_f = torch.empty(ra.ulysses_workspace_bytes(P, B, H, C, d), dtype=torch.uint8, device=dev())
+    uws_b = torch.empty(ra.ulysses_workspace_bytes(P, B, H, C, d, bwd=True), dtype=torch.uint8, device=dev())
+
+    def ulysses():
+        ra.ulysses_fwd(qc, kc, vc, uo, ul, rank, True, scale, workspace=uws_f)
+        ra.ulysses_bwd(qc, kc, vc, dc, uo, ul, udq, udk, udv, rank, True, scale, workspace=uws_b)
+
+    _replays_match(ulysses, [uo, ul, udq, udk, udv])
+
+    kg = [gen(114, inputs.K, j, B, Hk, C, d).to(dev()) for j in range(P)]
+    vg = [gen(114, inputs.V, j, B, Hk, C, d).to(dev()) for j in range(P)]
+    ao = torch.empty(B, H, C, d, device=dev())
+    al = torch.empty(B, H, C, device=dev())
+    adq = torch.empty(B, H, C, d, device=dev())
+    adk, adv = (torch.empty(B, Hk, S, d, device=dev()) for _ in range(2))
+    aws_f = torch.empty(ra.allgather_workspace_bytes(P, B, H, C, d, H_kv=Hk), dtype=torch.uint8, device=dev())
+    aws_b = torch.empty(ra.allgather_workspace_bytes(P, B, H, C, d, H_kv=Hk, bwd=True), dtype=torch.uint8,
+                        device=dev())
+
+    def allgather():
+        ra.allgather_fwd(qc[rank], kg, vg, ao, al, rank, True, scale, workspace=aws_f)
+        ra.allgather_bwd(qc[rank], kg, vg, ao, al, dc[rank], adq, adk, adv, rank, True, scale, workspace=aws_b)
+
+    _replays_match(allgather, [ao, al, adq, adk, adv])
