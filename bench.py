@@ -535,7 +535,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--ring-mode", default="double_buffer", choices=["double_buffer", "resident"])
+    ap.add_argument("--ring-mode", default="double_buffer", choices=["double_buffer", "resident", "fused"])
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query (H_kv = H/4) measurements")

@@ -69,10 +69,18 @@ enum ra_status {
 };
 
 enum ra_ring_mode {
-  RA_RING_RESIDENT = 0,     /* walk the resident chunks in ring order, no copies */
-  RA_RING_DOUBLE_BUFFER = 1 /* stage each chunk into a 2-slot buffer first (the
-                               emulated receive), overlapped with the previous
-                               step's compute when copy_stream is given */
+  RA_RING_RESIDENT = 0,      /* walk the resident chunks in ring order, no copies */
+  RA_RING_DOUBLE_BUFFER = 1, /* stage each chunk into a 2-slot buffer first (the
+                                emulated receive), overlapped with the previous
+                                step's compute when copy_stream is given */
+  RA_RING_FUSED = 2          /* resident chunks walked by one launch: the
+                                online-softmax state runs on from chunk to
+                                chunk in registers and no partial crosses HBM.
+                                Needs C % 64 == 0, at most 16 visible
+                                chunks and (visible chunks) * C < 2^30;
+                                otherwise the call runs as RA_RING_RESIDENT.  Chunks are visited in index
+                                order, so results differ from the ring order's
+                                by rounding only. */
 };
 
 /* Library version (RA_VERSION). */

@@ -28,8 +28,9 @@ TRACE_KINDS = {1: "fwd_diag", 2: "fwd_full", 3: "merge", 4: "bwd_rowdot", 5: "bw
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
 RING_RESIDENT = 0
 RING_DOUBLE_BUFFER = 1
-_MODES = {"resident": RING_RESIDENT, "double_buffer": RING_DOUBLE_BUFFER,
-          RING_RESIDENT: RING_RESIDENT, RING_DOUBLE_BUFFER: RING_DOUBLE_BUFFER}
+RING_FUSED = 2
+_MODES = {"resident": RING_RESIDENT, "double_buffer": RING_DOUBLE_BUFFER, "fused": RING_FUSED,
+          RING_RESIDENT: RING_RESIDENT, RING_DOUBLE_BUFFER: RING_DOUBLE_BUFFER, RING_FUSED: RING_FUSED}
 
 _lib = None
 

@@ -303,7 +303,7 @@ int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks, const void* cons
   st = check_groups(H, H_kv, "ra_ring_fwd");
   if (st) return st;
   if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "ra_ring_fwd: rank=%d outside [0, %d)", rank, P);
-  if (ring_mode != RA_RING_RESIDENT && ring_mode != RA_RING_DOUBLE_BUFFER)
+  if (ring_mode != RA_RING_RESIDENT && ring_mode != RA_RING_DOUBLE_BUFFER && ring_mode != RA_RING_FUSED)
     return fail(RA_ERR_UNSUPPORTED, "ra_ring_fwd: ring_mode=%d", ring_mode);
   for (int j = 0; j < P; ++j) {
     if (!k_chunks[j] || !v_chunks[j]) return fail(RA_ERR_NULL, "ra_ring_fwd: chunk %d pointer is NULL", j);
@@ -328,7 +328,28 @@ int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks, const void* cons
                            C, C, d, scale, diag, merge, H / H_kv};
   };
 
-  if (ring_mode == RA_RING_RESIDENT) {
+  if (ring_mode == RA_RING_FUSED && C % 64 == 0 && (int)steps.size() <= ra::kMaxWalkChunks &&
+      (long long)steps.size() * C <= 0x3fffffffLL) {
+    // One pass over the visible chunks in index order; under causal masking
+    // the diagonal chunk comes last and the local queries sit at rank * C.
+    ra::ChunkTable t{};
+    t.n = 0;
+    t.C = C;
+    for (int j = 0; j < P; ++j)
+      if (!causal || j <= rank) {
+        t.k[t.n] = static_cast<const uint16_t*>(k_chunks[j]);
+        t.v[t.n] = static_cast<const uint16_t*>(v_chunks[j]);
+        ++t.n;
+      }
+    ra::FwdStepArgs a = step_args(nullptr, nullptr, causal != 0, false);
+    a.Sk = t.n * C;
+    a.qoff = causal ? rank * C : 0;
+    a.walk = &t;
+    const hipError_t e = fwd_step(a, cs);
+    if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd fused walk");
+    return ok();
+  }
+  if (ring_mode != RA_RING_DOUBLE_BUFFER) {
     for (size_t i = 0; i < steps.size(); ++i) {
       const Step& sp = steps[i];
       const hipError_t e = fwd_step(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, i > 0), cs);

@@ -125,14 +125,17 @@ constexpr int kFwdBuffers = 4;    // LDS buffers per operand (K, V)
 // tiles ahead of use, so the operands of an iteration's first MFMAs are read
 // before the barrier that ends the previous one and the operand stream runs
 // on across it.  One workgroup barrier per tile.
-template <int D, bool DIAG, bool MERGE>
-__global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t* __restrict__ qg,
-                                                                  const uint16_t* __restrict__ kg,
-                                                                  const uint16_t* __restrict__ vg,
-                                                                  float* __restrict__ og,
-                                                                  float* __restrict__ lseg, int Sq, int Sk,
-                                                                  int n_qtiles, int total_tiles,
-                                                                  float scale_log2, int group, int qoff) {
+//
+// WALK: the keys are tbl.n resident chunks walked in one pass (Sk = n * C),
+// so the online-softmax state runs on from chunk to chunk in registers and
+// no partial crosses HBM.  Key tile T is tile T % (C/64) of chunk
+// T / (C/64); the chunk bases sit one per lane and are read out with
+// readlane as the tile loads cross into a new chunk.
+template <int D, bool DIAG, bool MERGE, bool WALK>
+__device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
+                                         const uint16_t* __restrict__ vg, float* __restrict__ og,
+                                         float* __restrict__ lseg, int Sq, int Sk, int n_qtiles, int total_tiles,
+                                         float scale_log2, int group, int qoff, const ChunkTable& tbl) {
   constexpr int NW = kFwdWaves, NQW = kFwdRowsPerWave, BR = NW * NQW, BC = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kFwdLookahead;
   constexpr int NB = kFwdBuffers;
@@ -171,8 +174,46 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   const int qq = qw0 + l32;
   const uint16_t* __restrict__ qp = qg + (size_t)bh * Sq * D;
   // Grouped-query attention: query head row bh reads key/value head bh / group.
-  const uint16_t* __restrict__ kp = kg + (size_t)(bh / group) * Sk * D;
-  const uint16_t* __restrict__ vp = vg + (size_t)(bh / group) * Sk * D;
+  const uint16_t* __restrict__ kp = WALK ? kg : kg + (size_t)(bh / group) * Sk * D;
+  const uint16_t* __restrict__ vp = WALK ? vg : vg + (size_t)(bh / group) * Sk * D;
+  // Walk: chunk bases (lane c holds chunk c's), the head's offset in a
+  // chunk, and the source (base, first token, tokens) of key tile T.
+  [[maybe_unused]] uint64_t kchunk = 0, vchunk = 0;
+  [[maybe_unused]] int tpc = 1;
+  [[maybe_unused]] size_t hoff = 0;
+  if constexpr (WALK) {
+    tpc = tbl.C / kTileTokens;
+    hoff = (size_t)(bh / group) * tbl.C * D;
+#pragma unroll
+    for (int i = 0; i < kMaxWalkChunks; ++i)
+      if (lane == i) {
+        kchunk = (uint64_t)(uintptr_t)tbl.k[i];
+        vchunk = (uint64_t)(uintptr_t)tbl.v[i];
+      }
+  }
+  auto chunk_base = [&](uint64_t table, int c) __attribute__((always_inline)) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)table, c);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(table >> 32), c);
+    return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo) + hoff;
+  };
+  // A walk position: tile l of chunk c, its chunk's base, and the tokens
+  // there (0 past the last chunk: such tiles read as zeros).
+  struct WalkPos {
+    int c, l, n;
+    const uint16_t* base;
+  };
+  auto walk_pos = [&](uint64_t table, int T) __attribute__((always_inline)) {
+    const int c = T / tpc;
+    return WalkPos{c, T - c * tpc, c < tbl.n ? tbl.C : 0, chunk_base(table, c < tbl.n ? c : 0)};
+  };
+  auto walk_next = [&](uint64_t table, WalkPos& p) __attribute__((always_inline)) {
+    if (++p.l == tpc) {
+      p.l = 0;
+      ++p.c;
+      p.n = p.c < tbl.n ? tbl.C : 0;
+      p.base = chunk_base(table, p.c < tbl.n ? p.c : 0);
+    }
+  };
 
   // Causal: query row q sees keys k <= q + qoff.
   int kend = Sk;
@@ -189,11 +230,26 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   constexpr int NPIECE = Dma::kPerWave;  // pieces per tile per wave
   Dma dma;
   dma.init(wave, lane);
+  [[maybe_unused]] WalkPos vpos{}, kpos{};  // walk: tiles tt + 1 (V) and tt + 3 (K) of step tt
+  if constexpr (WALK) {
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (j < ntiles) dma.load(kbuf(j), kp, j * BC, Sk);
-  dma.load(vbuf(0), vp, 0, Sk);
-  dma.load(vbuf(NB - 1), vp, 0, Sk);  // finite data for the P = 0 product of iteration 0
+    for (int j = 0; j < 3; ++j)
+      if (j < ntiles) {
+        const WalkPos p = walk_pos(kchunk, j);
+        dma.load(kbuf(j), p.base, p.l * BC, p.n);
+      }
+    const WalkPos v0 = walk_pos(vchunk, 0);
+    dma.load(vbuf(0), v0.base, 0, v0.n);
+    dma.load(vbuf(NB - 1), v0.base, 0, v0.n);  // finite data for the P = 0 product of iteration 0
+    vpos = walk_pos(vchunk, 1);
+    kpos = walk_pos(kchunk, 3);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < ntiles) dma.load(kbuf(j), kp, j * BC, Sk);
+    dma.load(vbuf(0), vp, 0, Sk);
+    dma.load(vbuf(NB - 1), vp, 0, Sk);  // finite data for the P = 0 product of iteration 0
+  }
 
   u32x4 qf[NKS];
 #pragma unroll
@@ -343,8 +399,13 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   // past the last tile read zeros and are never used.
   auto dma_piece = [&](int tt, auto ic, int k) __attribute__((always_inline)) {
     constexpr int I = decltype(ic)::value;
-    if (k < NPIECE) dma.load_piece(k, vbuf((I + 1) % NB), vp, (tt + 1) * BC, Sk);
-    else dma.load_piece(k - NPIECE, kbuf((I + 3) % NB), kp, (tt + 3) * BC, Sk);
+    if constexpr (WALK) {
+      if (k < NPIECE) dma.load_piece(k, vbuf((I + 1) % NB), vpos.base, vpos.l * BC, vpos.n);
+      else dma.load_piece(k - NPIECE, kbuf((I + 3) % NB), kpos.base, kpos.l * BC, kpos.n);
+    } else {
+      if (k < NPIECE) dma.load_piece(k, vbuf((I + 1) % NB), vp, (tt + 1) * BC, Sk);
+      else dma.load_piece(k - NPIECE, kbuf((I + 3) % NB), kp, (tt + 3) * BC, Sk);
+    }
   };
   // Iteration tt (tt % NB == I): PV(tt-1), S^T(tt+1) and the softmax of tile
   // tt.  The same code runs for tt = wtiles, where only PV(tt-1) matters: the
@@ -416,6 +477,10 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
 #pragma unroll
       for (int k = 0; k < 2 * NPIECE; ++k) dma_piece(tt, ic, k);
     }
+    if constexpr (WALK) {
+      walk_next(vchunk, vpos);
+      walk_next(kchunk, kpos);
+    }
     wait_vmem_but<NPIECE>();
     phase_barrier();
   };
@@ -445,6 +510,31 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
   fwd_epilogue<D, MERGE>(oacc, mrow, lrow - lcomp, og, lseg, bh, Sq, qq, g);
 }
 
+template <int D, bool DIAG, bool MERGE>
+__global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t* __restrict__ qg,
+                                                                  const uint16_t* __restrict__ kg,
+                                                                  const uint16_t* __restrict__ vg,
+                                                                  float* __restrict__ og,
+                                                                  float* __restrict__ lseg, int Sq, int Sk,
+                                                                  int n_qtiles, int total_tiles,
+                                                                  float scale_log2, int group, int qoff) {
+  const ChunkTable none{};
+  fwd_body<D, DIAG, MERGE, false>(qg, kg, vg, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group, qoff,
+                                  none);
+}
+
+// One pass over resident chunks (no merge: the pass sees every key).
+template <int D, bool DIAG>
+__global__ __launch_bounds__(64 * kFwdWaves) void fwd_walk_kernel(const uint16_t* __restrict__ qg,
+                                                                  float* __restrict__ og,
+                                                                  float* __restrict__ lseg, int Sq, int Sk,
+                                                                  int n_qtiles, int total_tiles,
+                                                                  float scale_log2, int group, int qoff,
+                                                                  ChunkTable tbl) {
+  fwd_body<D, DIAG, false, true>(qg, nullptr, nullptr, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group,
+                                 qoff, tbl);
+}
+
 template <int D>
 hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
   constexpr int BR = kFwdWaves * kFwdRowsPerWave;
@@ -456,6 +546,19 @@ hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   const float sl2 = a.scale * kLog2e;
   dim3 grid((unsigned)total), block(64 * kFwdWaves);
+  if (a.walk) {
+    const ChunkTable& t = *a.walk;
+    if (a.merge || t.n < 1 || t.n > kMaxWalkChunks || t.C < 1 || t.C % kTileTokens ||
+        (long long)t.n * t.C != a.Sk)
+      return hipErrorInvalidValue;
+    if (a.diag)
+      hipLaunchKernelGGL((fwd_walk_kernel<D, true>), grid, block, 0, stream, a.q, a.o, a.lse, a.Sq, a.Sk, n_qtiles,
+                         (int)total, sl2, a.group, a.qoff, t);
+    else
+      hipLaunchKernelGGL((fwd_walk_kernel<D, false>), grid, block, 0, stream, a.q, a.o, a.lse, a.Sq, a.Sk, n_qtiles,
+                         (int)total, sl2, a.group, a.qoff, t);
+    return hipGetLastError();
+  }
 #define RA_FWD_LAUNCH(DIAG, MERGE)                                                                         \
   hipLaunchKernelGGL((fwd_step_kernel<D, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, a.v, a.o, \
                      a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff)

@@ -11,6 +11,16 @@ namespace ra {
 // merge == false, folded into the running values when merge == true.  Query
 // head row bh reads key/value head bh / group (grouped-query attention with
 // `group` query heads per key/value head; 1 = multi-head).
+// Resident key/value chunks walked by one launch, in order: chunk c holds
+// keys [c*C, (c+1)*C) of the walked sequence; C is a multiple of 64.
+constexpr int kMaxWalkChunks = 16;
+struct ChunkTable {
+  const uint16_t* k[kMaxWalkChunks];
+  const uint16_t* v[kMaxWalkChunks];
+  int n;  // chunks walked (1 .. kMaxWalkChunks)
+  int C;  // tokens per chunk
+};
+
 struct FwdStepArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -23,6 +33,9 @@ struct FwdStepArgs {
   bool merge;  // fold into the running (o, lse) instead of overwriting
   int group;   // query heads per key/value head (>= 1, divides BH)
   int qoff;    // causal offset of the query rows against the keys (>= 0; 0 on the ring's diagonal chunk)
+  // Non-null: the keys are walk->n resident chunks (k, v unused; Sk =
+  // n * C; merge must be false).
+  const ChunkTable* walk = nullptr;
 };
 hipError_t launch_fwd_step(const FwdStepArgs& a, hipStream_t stream);
 

@@ -127,6 +127,55 @@ def test_ring_fwd_every_rank(P, C, d, causal, mode):
         assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)
 
 
+@pytest.mark.parametrize("P,C,d,causal,H_kv", [
+    (4, 128, 128, True, None), (3, 192, 64, True, None), (3, 192, 64, False, None), (2, 256, 128, True, 1),
+    (16, 64, 128, True, None),
+])
+def test_ring_fwd_fused_every_rank(P, C, d, causal, H_kv):
+    """RA_RING_FUSED: the visible chunks walked by one launch.  Every rank
+    against the oracle, and against the per-step resident walk (the same
+    exact result, summed in another order)."""
+    B, H = 1, 2
+    q, k, v, _ = ring_tensors(115, B, H, P, C, d, H_kv=H_kv)
+    kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    scale = 1 / math.sqrt(d)
+    for rank in range(P):
+        print(f"ring_fwd fused P={P} C={C} d={d} causal={causal} H_kv={H_kv} rank={rank}", flush=True)
+        outs = {}
+        for mode in ("fused", "resident"):
+            o = torch.full((B, H, C, d), float("nan"), device=dev())
+            lse = torch.full((B, H, C), float("nan"), device=dev())
+            ra.ring_fwd(q[rank].to(dev()), kd, vd, o, lse, rank, causal, scale, ring_mode=mode)
+            torch.cuda.synchronize()
+            outs[mode] = (f64(o), f64(lse))
+        ro, rl = oracle.attention_fwd(f64(q[rank]), kf, vf, scale, causal, q_pos=rank * C + np.arange(C))
+        assert_close(outs["fused"][0], ro, TOL_O, f"o rank {rank}")
+        assert_close(outs["fused"][1], rl, TOL_LSE, f"lse rank {rank}", rel=None)
+        assert_close(outs["fused"][0], outs["resident"][0], 2e-3, "fused vs resident o", rel=None)
+        assert_close(outs["fused"][1], outs["resident"][1], 1e-4, "fused vs resident lse", rel=None)
+
+
+@pytest.mark.parametrize("P,C", [(3, 100), (17, 64)])
+def test_ring_fwd_fused_falls_back(P, C):
+    """Chunk lengths that are not a multiple of 64, or more than 16 visible
+    chunks, run the per-step resident walk: bit-identical to it."""
+    B, H, d, rank = 1, 2, 128, P - 1
+    print(f"ring_fwd fused fallback P={P} C={C}", flush=True)
+    q, k, v, _ = ring_tensors(116, B, H, P, C, d, ranks=[rank])
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    outs = []
+    for mode in ("fused", "resident"):
+        o = torch.empty(B, H, C, d, device=dev())
+        lse = torch.empty(B, H, C, device=dev())
+        ra.ring_fwd(q[rank].to(dev()), kd, vd, o, lse, rank, True, ring_mode=mode)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_maximum_chunk_length(d):
     """A key chunk longer than 2^32 bytes (2^24 + 100 tokens at d = 128,
