@@ -194,6 +194,14 @@ def kernel_stats(rec, w, kind_flops):
     return out
 
 
+def walk_stats(rec, flops, steps):
+    """Fused walk: one launch per rank walks every visible chunk; its work is
+    the walk's whole forward."""
+    ms = sum(m for _, m in rec) / steps
+    return {"fwd_walk": {"launches": len(rec), "ms_per_step": round(ms, 4),
+                         "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}}
+
+
 def run_fwd(w, steps, warmup, ring_mode, H_kv=None):
     """The forward walk of workload w; H_kv < H runs it with grouped-query
     key/value chunks of H_kv heads."""
@@ -213,7 +221,9 @@ def run_fwd(w, steps, warmup, ring_mode, H_kv=None):
     ws = torch.empty(max(1, ra.workspace_bytes(P, B, H, C, d, ring_mode, H_kv=Hk)), dtype=torch.uint8,
                      device=dev)
     copy_stream = torch.cuda.Stream(dev) if ring_mode == "double_buffer" else None
-    n_launch = sum(sum(k != "skip" for *_, k in step_kinds(r, P, w.causal)) for r in w.ranks)
+    fused = ring_mode == "fused" and C % 64 == 0
+    n_launch = len(w.ranks) if fused else sum(sum(k != "skip" for *_, k in step_kinds(r, P, w.causal))
+                                              for r in w.ranks)
 
     def step():
         for r in w.ranks:
@@ -226,7 +236,7 @@ def run_fwd(w, steps, warmup, ring_mode, H_kv=None):
         "secs": secs, "ms_per_step": secs / steps * 1e3,
         "tflops": flops * steps / secs / 1e12,
         "tokens_per_s": B * C * len(w.ranks) * steps / secs,
-        "kernels": kernel_stats(rec, w, lambda k: 4 * d),
+        "kernels": (walk_stats(rec, flops, steps) if fused else kernel_stats(rec, w, lambda k: 4 * d)),
         "kv_bytes_per_ring_step": 2 * B * Hk * C * d * 2,
         "rec": rec,
     }
@@ -555,7 +565,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from long_context_exact_step_amd.workloads import WORKLOADS
+    from long_context_exact_step_amd.workloads import WORKLOADS, fwd_flops
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -565,15 +575,22 @@ def main():
     print(f"[bench] fwd {w.name}: {fwd['ms_per_step']:.3f} ms/step, {fwd['tflops']:.1f} TFLOP/s", file=sys.stderr,
           flush=True)
 
-    dom = "fwd_full" if "fwd_full" in fwd["kernels"] else "fwd_diag"
-    dk = fwd["kernels"][dom]
-    dom_flops = 4 * w.d * pairs_of_kind(dom, w)
+    if "fwd_walk" in fwd["kernels"]:  # fused walk: the launches are the whole forward
+        dom = "fwd_walk"
+        dk = fwd["kernels"][dom]
+        dk = {"launches": dk["launches"], "avg_ms": dk["ms_per_step"]}
+        dom_flops = fwd_flops(w)
+    else:
+        dom = "fwd_full" if "fwd_full" in fwd["kernels"] else "fwd_diag"
+        dk = fwd["kernels"][dom]
+        dom_flops = 4 * w.d * pairs_of_kind(dom, w)
     achieved = dom_flops / (dk["avg_ms"] * 1e-3) / 1e12
     traffic = None
     try:
         with open(PROFILE_COUNTERS) as f:
             prof = json.load(f)
-        if prof.get("source_sha") == fwd_kernel_sha() and prof.get("workload_id") == w.id:
+        # The counters cover the full-chunk step kernel, not the fused walk.
+        if prof.get("source_sha") == fwd_kernel_sha() and prof.get("workload_id") == w.id and dom != "fwd_walk":
             traffic = prof.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
@@ -582,8 +599,9 @@ def main():
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
         # HBM bytes per launch (counters) over the live launch time: achieved HBM bandwidth.
         "traffic_gbps": None if traffic is None else round(traffic / (dk["avg_ms"] * 1e-3) / 1e9, 1),
-        "kernel": f"fwd_step_kernel ({dom}), {dk['launches']} launches, avg {dk['avg_ms']} ms",
-        "flops_per_launch": dom_flops,
+        "kernel": (f"fwd_walk_kernel (fused walk), {dk['launches']} launches, {dk['avg_ms']} ms per step"
+                   if dom == "fwd_walk" else f"fwd_step_kernel ({dom}), {dk['launches']} launches, avg {dk['avg_ms']} ms"),
+        "flops_per_launch": dom_flops,  # fused walk: per step (all its launches)
     }
 
     out = {
