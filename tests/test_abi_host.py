@@ -90,6 +90,8 @@ def test_ring_fwd_validation(L):
     assert ring_fwd(L, rank=4) == RA_ERR_RANK
     assert ring_fwd(L, rank=-1) == RA_ERR_RANK
     assert ring_fwd(L, mode=7) == RA_ERR_UNSUPPORTED
+    assert ring_fwd(L, mode=2, rank=4) == RA_ERR_RANK  # the fused walk validates like the others
+    assert ring_fwd(L, mode=2, chunks=[FAKE, MIS, FAKE, FAKE]) == RA_ERR_ALIGN
     assert ring_fwd(L, chunks=[FAKE, 0, FAKE, FAKE]) == RA_ERR_NULL
     assert ring_fwd(L, chunks=[FAKE, MIS, FAKE, FAKE]) == RA_ERR_ALIGN
     assert ring_fwd(L, ws=0) == RA_ERR_WORKSPACE
@@ -117,6 +119,7 @@ def test_workspace_sizes(L):
     # Double buffer: 2 slots x (K + V) x B*H*C*d bf16.
     assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 1, 0) == 2 * 2 * 32 * 32768 * 128 * 2
     assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 0, 0) == 0
+    assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 2, 0) == 0  # fused walk: no staging
     assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 128, 0, 1) == 2 * 32 * 16384 * 4
     assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 96, 0, 1) == 0
 
