@@ -127,22 +127,21 @@ def test_ring_fwd_every_rank(P, C, d, causal, mode):
         assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)
 
 
-@pytest.mark.parametrize("P,C,d,causal,H_kv", [
-    (4, 128, 128, True, None), (3, 192, 64, True, None), (3, 192, 64, False, None), (2, 256, 128, True, 1),
-    (16, 64, 128, True, None),
+@pytest.mark.parametrize("P,C,d,causal,H_kv,B,H", [
+    (4, 128, 128, True, None, 1, 2), (3, 192, 64, True, None, 1, 2), (3, 192, 64, False, None, 1, 2),
+    (2, 256, 128, True, 1, 1, 2), (16, 64, 128, True, None, 1, 2), (3, 128, 128, True, 2, 2, 4),
 ])
-def test_ring_fwd_fused_every_rank(P, C, d, causal, H_kv):
+def test_ring_fwd_fused_every_rank(P, C, d, causal, H_kv, B, H):
     """RA_RING_FUSED: the visible chunks walked by one launch.  Every rank
     against the oracle, and against the per-step resident walk (the same
     exact result, summed in another order)."""
-    B, H = 1, 2
     q, k, v, _ = ring_tensors(115, B, H, P, C, d, H_kv=H_kv)
     kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
     kd = [t.to(dev()) for t in k]
     vd = [t.to(dev()) for t in v]
     scale = 1 / math.sqrt(d)
     for rank in range(P):
-        print(f"ring_fwd fused P={P} C={C} d={d} causal={causal} H_kv={H_kv} rank={rank}", flush=True)
+        print(f"ring_fwd fused P={P} C={C} d={d} causal={causal} H_kv={H_kv} B={B} H={H} rank={rank}", flush=True)
         outs = {}
         for mode in ("fused", "resident"):
             o = torch.full((B, H, C, d), float("nan"), device=dev())
