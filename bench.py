@@ -60,7 +60,7 @@ COUNTER_KERNEL = "fwd_step_kernel<128, false, true>"  # the full-chunk step with
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def ingest_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
+def ingest_counters(fetch_dir, write_dir, cmd_fetch, cmd_write, out_path=PROFILE_COUNTERS):
     """Turn two rocprofv3 counter passes over the default forward walk (one
     with FETCH_SIZE, one with WRITE_SIZE, in KiB per dispatch) into the HBM
     bytes per full-chunk launch that `roofline.traffic` reports.  Each counter
@@ -111,10 +111,11 @@ def ingest_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
         "hbm_bytes_per_launch": fetch_b + write_b,
         "command_fetch": cmd_fetch, "command_write": cmd_write,
     }
-    with open(PROFILE_COUNTERS, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec, indent=1))
+    return rec
 
 
 class HipEvents:

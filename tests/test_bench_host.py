@@ -1,0 +1,53 @@
+"""bench.py's host logic on the CPU: the multi-GPU refusal and the counter
+ingestion that turns two rocprofv3 counter passes into the forward kernel's
+HBM bytes per launch (copy-calibrated)."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+KERNEL = "void ra::(anonymous namespace)::fwd_step_kernel<128, false, true>(unsigned short const*, float*)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "single MI355X" in r.stderr
+
+
+def _write_pass(d, counter, kernel_values, copy_values):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "x_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        n = 0
+        for name, vals in ((KERNEL, kernel_values), (COPY, copy_values)):
+            for v in vals:
+                n += 1
+                w.writerow({"Dispatch_Id": n, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_counter_ingestion(tmp_path):
+    """The staging copies move one 256 MiB chunk (262144 KiB); a copy that
+    reads FETCH_SIZE 131072 KiB gives a factor of 2.  Small copies (not the
+    chunk staging) are ignored for the calibration."""
+    _write_pass(tmp_path / "f", "FETCH_SIZE", [1000.0, 1200.0], [131072.0, 131072.0, 64.0])
+    _write_pass(tmp_path / "w", "WRITE_SIZE", [500.0, 700.0], [262144.0, 262144.0, 8.0])
+    out = tmp_path / "counters.json"
+    rec = bench.ingest_counters(str(tmp_path / "f"), str(tmp_path / "w"), "cmd f", "cmd w", out_path=str(out))
+    assert rec["copy_calibration"]["fetch_factor"] == 2.0
+    assert rec["copy_calibration"]["write_factor"] == 1.0
+    assert rec["hbm_fetch_bytes_per_launch"] == 1100.0 * 2 * 1024
+    assert rec["hbm_write_bytes_per_launch"] == 600.0 * 1024
+    assert rec["hbm_bytes_per_launch"] == (2200.0 + 600.0) * 1024
+    assert rec["source_sha"] == bench.fwd_kernel_sha()
+    assert json.loads(out.read_text()) == rec
