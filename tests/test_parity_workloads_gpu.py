@@ -75,29 +75,35 @@ def fan_out(fn, items):
         return list(ex.map(fn, items))
 
 
-def check_rows(w, rank, q, k, v, o, lse, rows_of_head, label, grp=1):
-    """Oracle on rows_of_head(h) of every head vs the GPU (o, lse).  grp > 1:
+def check_rows(w, rank, q, k, v, o, lse, rows_of_head, label, grp=1, more=()):
+    """Oracle on rows_of_head(h) of every head vs the GPU (o, lse), and vs each
+    further (o, lse, label) in `more` (one oracle evaluation for all).  grp > 1:
     grouped-query key/value chunks, query head h reads key/value head h // grp."""
-    o_c, l_c = o.cpu(), lse.cpu()
+    outs = [(o.cpu(), lse.cpu(), label)] + [(a.cpu(), b.cpu(), n) for a, b, n in more]
 
     def one(h):
         rows = rows_of_head(h)
         kh, vh = head_full(k, h // grp), head_full(v, h // grp)
         qh = f64(q[:, h:h + 1, rows])
         ro, rl = oracle.attention_fwd(qh, kh, vh, w.scale, w.causal, q_pos=rank * w.C + rows)
-        go, gl = f64(o_c[:, h:h + 1, rows]), f64(l_c[:, h:h + 1, rows])
-        return (np.abs(go - ro).max(), np.abs(gl - rl).max(),
-                np.linalg.norm(go - ro) ** 2, np.linalg.norm(ro) ** 2, np.isfinite(go).all())
+        res = []
+        for o_c, l_c, _ in outs:
+            go, gl = f64(o_c[:, h:h + 1, rows]), f64(l_c[:, h:h + 1, rows])
+            res.append((np.abs(go - ro).max(), np.abs(gl - rl).max(),
+                        np.linalg.norm(go - ro) ** 2, np.linalg.norm(ro) ** 2, np.isfinite(go).all()))
+        return res
 
-    res = fan_out(one, range(w.H))
-    err_o = max(r[0] for r in res)
-    err_l = max(r[1] for r in res)
-    rel = math.sqrt(sum(r[2] for r in res) / sum(r[3] for r in res))
-    say(f"{label}: max|dO|={err_o:.2e} max|dlse|={err_l:.2e} rel={rel:.2e}")
-    assert all(r[4] for r in res), f"{label}: non-finite output"
-    assert err_o <= TOL_O, f"{label}: O max abs err {err_o}"
-    assert err_l <= TOL_LSE, f"{label}: lse max abs err {err_l}"
-    assert rel <= TOL_REL, f"{label}: O relative err {rel}"
+    per_head = fan_out(one, range(w.H))
+    for n, (_, _, name) in enumerate(outs):
+        res = [r[n] for r in per_head]
+        err_o = max(r[0] for r in res)
+        err_l = max(r[1] for r in res)
+        rel = math.sqrt(sum(r[2] for r in res) / sum(r[3] for r in res))
+        say(f"{name}: max|dO|={err_o:.2e} max|dlse|={err_l:.2e} rel={rel:.2e}")
+        assert all(r[4] for r in res), f"{name}: non-finite output"
+        assert err_o <= TOL_O, f"{name}: O max abs err {err_o}"
+        assert err_l <= TOL_LSE, f"{name}: lse max abs err {err_l}"
+        assert rel <= TOL_REL, f"{name}: O relative err {rel}"
 
 
 # ---------------------------------------------------------------------------
@@ -127,9 +133,11 @@ def test_full_ring_all_rows():
     kd = [t.to(dev()) for t in k]
     vd = [t.to(dev()) for t in v]
     for r in w.ranks:
-        say(f"full ring rank {r}: GPU walk, then oracle on all {w.C} rows x {w.H} heads")
+        say(f"full ring rank {r}: GPU walk (double buffer, and fused), then oracle on all {w.C} rows x {w.H} heads")
         o, lse = gpu_ring_fwd(w, r, q[r], kd, vd)
-        check_rows(w, r, q[r], k, v, o, lse, lambda h: np.arange(w.C), f"full ring rank {r}")
+        fo, fl = gpu_ring_fwd(w, r, q[r], kd, vd, "fused")
+        check_rows(w, r, q[r], k, v, o, lse, lambda h: np.arange(w.C), f"full ring rank {r}",
+                   more=[(fo, fl, f"full ring rank {r} fused")])
 
 
 # ---------------------------------------------------------------------------
