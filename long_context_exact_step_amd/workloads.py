@@ -60,6 +60,18 @@ def step_kinds(rank, P, causal):
     return out
 
 
+MAX_WALK_CHUNKS = 16  # chunks one fused-walk launch can hold (ra_kernels.h kMaxWalkChunks)
+
+
+def fused_walk_applies(w, rank):
+    """Whether ra_ring_fwd in RA_RING_FUSED mode walks this rank's visible
+    chunks in one launch (the library's rule: C a multiple of 64, at most 16
+    visible chunks, visible chunks * C < 2^30); otherwise it runs the
+    per-step resident walk."""
+    nvis = sum(kind != "skip" for *_, kind in step_kinds(rank, w.P, w.causal))
+    return w.C % 64 == 0 and nvis <= MAX_WALK_CHUNKS and nvis * w.C < 2 ** 30
+
+
 def visible_pairs_per_head(w, rank):
     """(query, key) pairs a rank's walk evaluates per (batch, head)."""
     n = 0

@@ -9,8 +9,8 @@ stream).
   visible score 0, so lse_p = ln(p + 1) and O_p is the mean of V over the
   visible prefix; V = 1 makes O = 1.
 * Training share (C=16K, P=4, rank 3): O/lse and dQ on 256 sampled query
-  rows per head, dK/dV on 256 sampled key rows per chunk for 4 heads, and on
-  every key the sums that hold exactly: sum_k dK_k = 0 and
+  rows per head, dK/dV on 256 sampled key rows per (head, chunk) for every
+  head, and on every key the sums that hold exactly: sum_k dK_k = 0 and
   sum_k dV_k = sum_q dO_q.
 * Head-partitioned (Ulysses) share of the 128K/CP=4 sequence: ranks 0 and 3,
   H/4 = 8 heads over all 131072 tokens, 256 sampled rows per head; its
@@ -18,8 +18,12 @@ stream).
   key.
 * Grouped-query attention (key/value chunks of H/4 heads): the 128K/CP=4
   share on sampled rows, and the training share's dQ on sampled rows, dK/dV
-  (summed over each group's query heads) on sampled key rows of two
-  key/value heads, and the gradient sums on every key.
+  (summed over each group's query heads) on sampled key rows of every
+  key/value head, and the gradient sums on every key.
+* All-gather share: the 128K/CP=4 forward on sampled rows (MHA and grouped
+  heads); the training share's forward and dQ on sampled rows, dK/dV on
+  sampled key rows of every head over the gathered sequence, and the
+  gradient sums.
 
 The oracle runs on the host, fanned out over heads with one BLAS thread per
 task.
@@ -260,7 +264,7 @@ def test_train_forward_and_dq_sampled_rows(train_run):
 def test_train_dk_dv_sampled_key_rows(train_run):
     t = train_run
     w, r = t["w"], t["r"]
-    heads = [0, 11, 22, 31]
+    heads = range(w.H)
     pos = r * w.C + np.arange(w.C)
 
     def one(h):
@@ -280,7 +284,7 @@ def test_train_dk_dv_sampled_key_rows(train_run):
                          np.linalg.norm(rk[:, :, sl]) ** 2 + np.linalg.norm(rv[:, :, sl]) ** 2))
         return errs
 
-    say(f"{w.name}: oracle dK/dV on 256 key rows x {w.P} chunks x heads {heads}")
+    say(f"{w.name}: oracle dK/dV on 256 key rows x {w.P} chunks x all {w.H} heads")
     res = [e for per_head in fan_out(one, heads) for e in per_head]
     e_k, e_v = max(x[0] for x in res), max(x[1] for x in res)
     rel = math.sqrt(sum(x[2] for x in res) / sum(x[3] for x in res))
@@ -372,32 +376,38 @@ def test_gqa_train_dq_sampled_rows(train_run_gqa):
 
 @pytest.mark.timeout(900)
 def test_gqa_train_dk_dv_sampled_key_rows(train_run_gqa):
-    """dK/dV of a key/value head sum over the 4 query heads of its group."""
+    """dK/dV of every key/value head, which sum over the 4 query heads of its
+    group: the oracle runs once per query head (its contribution to its
+    key/value head at that head's sampled key rows) and the contributions of
+    a group are added."""
     t = train_run_gqa
     w, r = t["w"], t["r"]
-    kv_heads = [0, t["Hk"] - 1]
+    Hk = t["Hk"]
     pos = r * w.C + np.arange(w.C)
+    key_rows = {hk: [inputs.key_row_sample(w.id, hk, j, w.C) for j in range(w.P)] for hk in range(Hk)}
 
-    def one(hk):
+    def one(h):
+        hk = h // GQA_GROUP
         kh, vh = head_full(t["k"], hk), head_full(t["v"], hk)
-        grp = slice(hk * GQA_GROUP, (hk + 1) * GQA_GROUP)
-        qg, dog = f64(t["q"][:, grp]), f64(t["do"][:, grp])
-        per_chunk = [inputs.key_row_sample(w.id, hk, j, w.C) for j in range(w.P)]
-        all_rows = np.concatenate([j * w.C + rows for j, rows in enumerate(per_chunk)])
-        rk, rv = oracle.attention_bwd_key_rows(qg, kh, vh, dog, w.scale, True, all_rows, q_pos=pos)
-        errs = []
+        qh, doh = f64(t["q"][:, h:h + 1]), f64(t["do"][:, h:h + 1])
+        all_rows = np.concatenate([j * w.C + rows for j, rows in enumerate(key_rows[hk])])
+        return oracle.attention_bwd_key_rows(qh, kh, vh, doh, w.scale, True, all_rows, q_pos=pos)
+
+    say(f"{w.name}, H_kv={Hk}: oracle dK/dV on 256 key rows x {w.P} chunks x all {Hk} key/value heads "
+        f"({w.H} query heads)")
+    per_q = fan_out(one, range(w.H))
+    res = []
+    for hk in range(Hk):
+        rk = sum(per_q[h][0] for h in range(hk * GQA_GROUP, (hk + 1) * GQA_GROUP))
+        rv = sum(per_q[h][1] for h in range(hk * GQA_GROUP, (hk + 1) * GQA_GROUP))
         n0 = 0
-        for j, rows in enumerate(per_chunk):
+        for j, rows in enumerate(key_rows[hk]):
             sl = slice(n0, n0 + len(rows))
             n0 += len(rows)
             gk, gv = f64(t["dk"][j][:, hk:hk + 1, rows]), f64(t["dv"][j][:, hk:hk + 1, rows])
-            errs.append((np.abs(gk - rk[:, :, sl]).max(), np.abs(gv - rv[:, :, sl]).max(),
-                         np.linalg.norm(gk - rk[:, :, sl]) ** 2 + np.linalg.norm(gv - rv[:, :, sl]) ** 2,
-                         np.linalg.norm(rk[:, :, sl]) ** 2 + np.linalg.norm(rv[:, :, sl]) ** 2))
-        return errs
-
-    say(f"{w.name}, H_kv={t['Hk']}: oracle dK/dV on 256 key rows x {w.P} chunks x key/value heads {kv_heads}")
-    res = [e for per_head in fan_out(one, kv_heads) for e in per_head]
+            res.append((np.abs(gk - rk[:, :, sl]).max(), np.abs(gv - rv[:, :, sl]).max(),
+                        np.linalg.norm(gk - rk[:, :, sl]) ** 2 + np.linalg.norm(gv - rv[:, :, sl]) ** 2,
+                        np.linalg.norm(rk[:, :, sl]) ** 2 + np.linalg.norm(rv[:, :, sl]) ** 2))
     e_k, e_v = max(x[0] for x in res), max(x[1] for x in res)
     rel = math.sqrt(sum(x[2] for x in res) / sum(x[3] for x in res))
     say(f"  max|ddK|={e_k:.2e} max|ddV|={e_v:.2e} rel={rel:.2e}")
@@ -576,7 +586,7 @@ def test_allgather_train_forward_and_dq_sampled_rows(train_run_allgather):
 def test_allgather_train_dk_dv_sampled_key_rows(train_run_allgather):
     t = train_run_allgather
     w, r = t["w"], t["r"]
-    heads = [0, w.H - 1]
+    heads = range(w.H)
     pos = r * w.C + np.arange(w.C)
 
     def one(h):
@@ -589,7 +599,7 @@ def test_allgather_train_dk_dv_sampled_key_rows(train_run_allgather):
                 np.linalg.norm(gk - rk) ** 2 + np.linalg.norm(gv - rv) ** 2,
                 np.linalg.norm(rk) ** 2 + np.linalg.norm(rv) ** 2)
 
-    say(f"{w.name}: all-gather oracle dK/dV on 256 key rows x {w.P} chunks x heads {heads}")
+    say(f"{w.name}: all-gather oracle dK/dV on 256 key rows x {w.P} chunks x all {w.H} heads")
     res = fan_out(one, heads)
     e_k, e_v = max(x[0] for x in res), max(x[1] for x in res)
     rel = math.sqrt(sum(x[2] for x in res) / sum(x[3] for x in res))
