@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define RA_VERSION 4
+#define RA_VERSION 5
 
 enum ra_status {
   RA_OK = 0,
@@ -229,6 +229,34 @@ int ra_ring_bwd_gqa(const void* q, const void* const* k_chunks,
                     int causal, float scale, int B, int H, int H_kv, int C,
                     int d, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * ra_ring_bwd_noalloc -- ra_ring_bwd_gqa for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, or
+ * harnesses that forbid hipMalloc.  Same arguments, results and contracts as
+ * ra_ring_bwd_gqa (H_kv == H for multi-head attention), minus the workspace:
+ * the row terms the backward needs (rowsum(dO * o) and lse in base 2, two
+ * floats per query row) live in a static device array of the library,
+ * sized for RA_NOALLOC_MAX_ROWS query rows (16 MiB), of which each device
+ * keeps its own copy until the process ends.  The call allocates and frees
+ * nothing.
+ *   - B*H*C above RA_NOALLOC_MAX_ROWS is RA_ERR_WORKSPACE, before anything
+ *     is enqueued.
+ *   - The first call on a device looks up the array's address there
+ *     (RA_ERR_HIP if that fails).
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's contents (each call writes every row it reads before
+ *     reading it, so nothing needs clearing).  Calls that overlap on one
+ *     device -- on different streams, or from different threads -- race on
+ *     it and must be ordered by the caller.
+ */
+#define RA_NOALLOC_MAX_ROWS (1 << 21)
+int ra_ring_bwd_noalloc(const void* q, const void* const* k_chunks,
+                        const void* const* v_chunks, int P, const float* o,
+                        const float* lse, const void* dO, float* dq,
+                        float* const* dk_chunks, float* const* dv_chunks,
+                        int rank, int causal, float scale, int B, int H,
+                        int H_kv, int C, int d, void* stream);
 
 /*
  * ra_ulysses_fwd -- one GPU's share of head-partitioned (Ulysses) sequence

@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "RAError", "lib", "version", "step_fwd", "lse_merge", "ring_fwd", "ring_bwd",
-    "workspace_bytes", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH", "trace_begin", "trace_end",
+    "workspace_bytes", "ring_bwd_noalloc", "NOALLOC_MAX_ROWS", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH", "trace_begin", "trace_end",
     "ulysses_fwd", "ulysses_bwd", "ulysses_workspace_bytes",
     "allgather_fwd", "allgather_bwd", "allgather_workspace_bytes",
     "TRACE_KINDS", "device_info", "mfma_probe",
@@ -27,6 +27,7 @@ TRACE_KINDS = {1: "fwd_diag", 2: "fwd_full", 3: "merge", 4: "bwd_rowdot", 5: "bw
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
 RING_RESIDENT = 0
+NOALLOC_MAX_ROWS = 1 << 21  # RA_NOALLOC_MAX_ROWS (include/ra.h)
 RING_DOUBLE_BUFFER = 1
 RING_FUSED = 2
 _MODES = {"resident": RING_RESIDENT, "double_buffer": RING_DOUBLE_BUFFER, "fused": RING_FUSED,
@@ -77,6 +78,8 @@ def lib():
         L.ra_ring_fwd_gqa.argtypes = [vp, vpp, vpp, i, vp, vp, i, i, f, i, i, i, i, i, i, vp, sz, vp, vp]
         L.ra_ring_bwd_gqa.restype = i
         L.ra_ring_bwd_gqa.argtypes = [vp, vpp, vpp, i, vp, vp, vp, vp, vpp, vpp, i, i, f, i, i, i, i, i, vp, sz, vp]
+        L.ra_ring_bwd_noalloc.restype = i
+        L.ra_ring_bwd_noalloc.argtypes = [vp, vpp, vpp, i, vp, vp, vp, vp, vpp, vpp, i, i, f, i, i, i, i, i, vp]
         L.ra_ulysses_workspace_bytes.restype = sz
         L.ra_ulysses_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.ra_ulysses_bwd.restype = i
@@ -273,6 +276,34 @@ def ring_bwd(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, 
     else:
         _check(lib().ra_ring_bwd_gqa(*head, Hk, *tail))
     return workspace
+
+
+def ring_bwd_noalloc(q, k_chunks, v_chunks, o, lse, dO, dq, dk_chunks, dv_chunks, rank, causal, scale=None,
+                     stream=None):
+    """ra_ring_bwd_noalloc: ring_bwd without a workspace (the library's
+    static device scratch holds the row terms; B*H*C <= NOALLOC_MAX_ROWS).
+    Calls that overlap on one device race on that scratch."""
+    import torch
+    B, H, C, d = _bhsd(q, "q")
+    Hk = _bhsd(k_chunks[0], "k_chunks[0]")[1]
+    P = _chunks(k_chunks, (B, Hk, C, d), "k_chunks")
+    for ts, n in ((v_chunks, "v_chunks"), (dk_chunks, "dk_chunks"), (dv_chunks, "dv_chunks")):
+        if _chunks(ts, (B, Hk, C, d), n) != P:
+            raise ValueError(f"{n}: {len(ts)} chunks, expected {P}")
+    for t, n in ((o, "o"), (dO, "dO"), (dq, "dq")):
+        _shape(t, (B, H, C, d), n)
+    _shape(lse, (B, H, C), "lse")
+    _need(q, torch.bfloat16, "q"); _need(dO, torch.bfloat16, "dO")
+    _need(o, torch.float32, "o"); _need(lse, torch.float32, "lse"); _need(dq, torch.float32, "dq")
+    for n, t in enumerate(list(k_chunks) + list(v_chunks)):
+        _need(t, torch.bfloat16, f"chunk{n}")
+    for n, t in enumerate(list(dk_chunks) + list(dv_chunks)):
+        if t is not None:
+            _need(t, torch.float32, f"grad_chunk{n}")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib().ra_ring_bwd_noalloc(_ptr(q), _ptr_array(k_chunks), _ptr_array(v_chunks), P, _ptr(o), _ptr(lse),
+                                     _ptr(dO), _ptr(dq), _ptr_array(dk_chunks), _ptr_array(dv_chunks), int(rank),
+                                     int(bool(causal)), scale, B, H, Hk, C, d, _stream(stream, q)))
 
 
 def ulysses_workspace_bytes(P, B, H, C, d, bwd=False):

@@ -414,44 +414,48 @@ int ra_ring_fwd(const void* q, const void* const* k_chunks, const void* const* v
                          workspace_bytes, stream, copy_stream);
 }
 
-int ra_ring_bwd_gqa(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,
-                    const float* lse, const void* dO, float* dq, float* const* dk_chunks, float* const* dv_chunks,
-                    int rank, int causal, float scale, int B, int H, int H_kv, int C, int d, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the backward walk, other than its workspace.
+int ring_bwd_check(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,
+                   const float* lse, const void* dO, float* dq, float* const* dk_chunks, float* const* dv_chunks,
+                   int rank, int causal, int B, int H, int H_kv, int C, int d, const char* what) {
   if (!q || !k_chunks || !v_chunks || !o || !lse || !dO || !dq || !dk_chunks || !dv_chunks)
-    return fail(RA_ERR_NULL, "ra_ring_bwd: NULL pointer");
-  if (P < 1) return fail(RA_ERR_SHAPE, "ra_ring_bwd: P=%d < 1", P);
-  int st = check_dims(B, H, C, d, "ra_ring_bwd");
+    return fail(RA_ERR_NULL, "%s: NULL pointer", what);
+  if (P < 1) return fail(RA_ERR_SHAPE, "%s: P=%d < 1", what, P);
+  int st = check_dims(B, H, C, d, what);
   if (st) return st;
-  st = check_groups(H, H_kv, "ra_ring_bwd");
+  st = check_groups(H, H_kv, what);
   if (st) return st;
-  if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "ra_ring_bwd: rank=%d outside [0, %d)", rank, P);
-  const std::vector<Step> steps = visible_steps(rank, P, causal != 0);
-  for (const Step& sp : steps) {
+  if (rank < 0 || rank >= P) return fail(RA_ERR_RANK, "%s: rank=%d outside [0, %d)", what, rank, P);
+  for (const Step& sp : visible_steps(rank, P, causal != 0)) {
     const int j = sp.j;
     if (!k_chunks[j] || !v_chunks[j] || !dk_chunks[j] || !dv_chunks[j])
-      return fail(RA_ERR_NULL, "ra_ring_bwd: chunk %d pointer is NULL", j);
+      return fail(RA_ERR_NULL, "%s: chunk %d pointer is NULL", what, j);
     if (!aligned16(k_chunks[j]) || !aligned16(v_chunks[j]) || !aligned16(dk_chunks[j]) || !aligned16(dv_chunks[j]))
-      return fail(RA_ERR_ALIGN, "ra_ring_bwd: chunk %d pointer not 16-byte aligned", j);
+      return fail(RA_ERR_ALIGN, "%s: chunk %d pointer not 16-byte aligned", what, j);
   }
   if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || !aligned16(dO) || !aligned16(dq))
-    return fail(RA_ERR_ALIGN, "ra_ring_bwd: device pointers must be 16-byte aligned");
-  const size_t need = ra_ring_workspace_bytes_gqa(P, B, H, H_kv, C, d, 0, 1);
-  if (!workspace || workspace_bytes < need)
-    return fail(RA_ERR_WORKSPACE, "ra_ring_bwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
-                need);
-  if (!aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_ring_bwd: workspace not 16-byte aligned");
+    return fail(RA_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", what);
+  return RA_OK;
+}
 
-  hipStream_t cs = static_cast<hipStream_t>(stream);
-  float* Dbuf = static_cast<float*>(workspace);
+// The backward walk on validated arguments; Dbuf holds 2 * B*H*C floats (D,
+// then lse in base 2), both written by the row pre-pass before any use.
+int ring_bwd_run(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,
+                 const float* lse, const void* dO, float* dq, float* const* dk_chunks, float* const* dv_chunks,
+                 int rank, int causal, float scale, int B, int H, int H_kv, int C, int d, float* Dbuf,
+                 hipStream_t cs, const char* what) {
   const int rows = B * H * C;
   float* lse2 = Dbuf + rows;
   hipError_t e = traced(RA_TRACE_BWD_ROWDOT, cs, [&] {
     return ra::launch_bwd_rowdot(static_cast<const uint16_t*>(dO), o, lse, Dbuf, lse2, rows, d, cs);
   });
   if (e == hipSuccess) e = traced(RA_TRACE_BWD_ZERO, cs, [&] { return ra::launch_zero_f32(dq, (size_t)rows * d, cs); });
-  if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd preprocess");
-  for (const Step& sp : steps) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  for (const Step& sp : visible_steps(rank, P, causal != 0)) {
     ra::BwdStepArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_chunks[sp.j]),
                       static_cast<const uint16_t*>(v_chunks[sp.j]), static_cast<const uint16_t*>(dO), lse2, Dbuf, dq,
                       dk_chunks[sp.j], dv_chunks[sp.j], B * H, C, C, d, scale, sp.diag, H / H_kv};
@@ -459,9 +463,81 @@ int ra_ring_bwd_gqa(const void* q, const void* const* k_chunks, const void* cons
     if (e == hipSuccess)
       e = traced(sp.diag ? RA_TRACE_BWD_DKDV_DIAG : RA_TRACE_BWD_DKDV_FULL, cs,
                  [&] { return ra::launch_bwd_dkdv(a, cs); });
-    if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd step");
+    if (e != hipSuccess) return hip_fail(e, what);
   }
   return ok();
+}
+
+}  // namespace
+
+// Device scratch of ra_ring_bwd_noalloc: D and lse2 (two floats) for up to
+// RA_NOALLOC_MAX_ROWS query rows, 16 MiB.  Each device that runs the library
+// holds its own copy until the process ends.  In host code this name is a
+// host-side stand-in, not a device address: kernels and copies get the
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[2 * (size_t)RA_NOALLOC_MAX_ROWS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_on_device(float** out, const char* what) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_ERR_HIP, "%s: device %d beyond the %d supported", what, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (!p) return fail(RA_ERR_HIP, "%s: scratch address lookup returned NULL", what);
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_ring_bwd_gqa(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,
+                    const float* lse, const void* dO, float* dq, float* const* dk_chunks, float* const* dv_chunks,
+                    int rank, int causal, float scale, int B, int H, int H_kv, int C, int d, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = ring_bwd_check(q, k_chunks, v_chunks, P, o, lse, dO, dq, dk_chunks, dv_chunks, rank, causal, B, H, H_kv, C,
+                          d, "ra_ring_bwd");
+  if (st) return st;
+  const size_t need = ra_ring_workspace_bytes_gqa(P, B, H, H_kv, C, d, 0, 1);
+  if (!workspace || workspace_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "ra_ring_bwd: workspace %zu bytes, need %zu", workspace ? workspace_bytes : 0,
+                need);
+  if (!aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_ring_bwd: workspace not 16-byte aligned");
+  return ring_bwd_run(q, k_chunks, v_chunks, P, o, lse, dO, dq, dk_chunks, dv_chunks, rank, causal, scale, B, H, H_kv,
+                      C, d, static_cast<float*>(workspace), static_cast<hipStream_t>(stream), "ra_ring_bwd");
+}
+
+int ra_ring_bwd_noalloc(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P,
+                        const float* o, const float* lse, const void* dO, float* dq, float* const* dk_chunks,
+                        float* const* dv_chunks, int rank, int causal, float scale, int B, int H, int H_kv, int C,
+                        int d, void* stream) {
+  int st = ring_bwd_check(q, k_chunks, v_chunks, P, o, lse, dO, dq, dk_chunks, dv_chunks, rank, causal, B, H, H_kv, C,
+                          d, "ra_ring_bwd_noalloc");
+  if (st) return st;
+  const long long rows = (long long)B * H * C;
+  if (rows > RA_NOALLOC_MAX_ROWS)
+    return fail(RA_ERR_WORKSPACE, "ra_ring_bwd_noalloc: B*H*C=%lld query rows exceed the static scratch's %d",
+                rows, RA_NOALLOC_MAX_ROWS);
+  float* sp = nullptr;
+  st = scratch_on_device(&sp, "ra_ring_bwd_noalloc");
+  if (st) return st;
+  return ring_bwd_run(q, k_chunks, v_chunks, P, o, lse, dO, dq, dk_chunks, dv_chunks, rank, causal, scale, B, H, H_kv,
+                      C, d, sp, static_cast<hipStream_t>(stream), "ra_ring_bwd_noalloc");
 }
 
 int ra_ring_bwd(const void* q, const void* const* k_chunks, const void* const* v_chunks, int P, const float* o,

@@ -40,8 +40,8 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     # 2: grouped-query (*_gqa) entry points; 3: ra_ulysses_fwd, ra_ulysses_bwd;
-    # 4: ra_allgather_fwd, ra_allgather_bwd
-    assert L.ra_version() == 4
+    # 4: ra_allgather_fwd, ra_allgather_bwd; 5: ra_ring_bwd_noalloc
+    assert L.ra_version() == 5
     assert L.ra_status_string(RA_OK) == b"RA_OK"
     assert L.ra_status_string(RA_ERR_WORKSPACE) == b"RA_ERR_WORKSPACE"
     assert L.ra_status_string(12345) == b"RA_ERR_UNKNOWN"
@@ -113,6 +113,27 @@ def test_ring_bwd_validation(L):
     assert args(wsb=need - 4) == RA_ERR_WORKSPACE
     assert L.ra_ring_bwd(None, arr, arr, P, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), arr, arr, 0, 1, 0.1,
                          1, 2, C, d, vp(FAKE), need, None) == RA_ERR_NULL
+
+
+def test_ring_bwd_noalloc_validation(L):
+    """The no-allocation backward validates like ra_ring_bwd_gqa (before the
+    scratch lookup, which is the first device call) and rejects more query
+    rows than its static scratch holds."""
+    P, C, d = 4, 64, 128
+    arr = (ctypes.c_void_p * P)(*([FAKE] * P))
+    call = lambda q=FAKE, rank=3, B=1, H=2, Hk=2, C=C, d=d, chunks=arr: L.ra_ring_bwd_noalloc(
+        vp(q), chunks, chunks, P, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), chunks, chunks, rank, 1, 0.1,
+        B, H, Hk, C, d, None)
+    assert call(q=0) == RA_ERR_NULL
+    assert call(q=MIS) == RA_ERR_ALIGN
+    assert call(rank=4) == RA_ERR_RANK
+    assert call(d=96) == RA_ERR_UNSUPPORTED
+    assert call(H=6, Hk=4) == RA_ERR_SHAPE
+    assert call(chunks=(ctypes.c_void_p * P)(FAKE, 0, FAKE, FAKE)) == RA_ERR_NULL
+    max_rows = 1 << 21
+    assert call(B=1, H=32, C=max_rows // 32 + 1) == RA_ERR_WORKSPACE
+    assert b"scratch" in L.ra_last_error()
+    assert call(B=2, H=32, Hk=8, C=max_rows // 64 + 64) == RA_ERR_WORKSPACE
 
 
 def test_workspace_sizes(L):
