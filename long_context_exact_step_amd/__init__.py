@@ -25,7 +25,9 @@ __all__ = [
 TRACE_KINDS = {1: "fwd_diag", 2: "fwd_full", 3: "merge", 4: "bwd_rowdot", 5: "bwd_zero",
                6: "bwd_dq_diag", 7: "bwd_dq_full", 8: "bwd_dkdv_diag", 9: "bwd_dkdv_full"}
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
+# RA_LIB_PATH may name another build of the same library (the host-sanitizer
+# build the CPU tests load); by default the in-tree libra.so.
+LIB_PATH = os.environ.get("RA_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
 RING_RESIDENT = 0
 NOALLOC_MAX_ROWS = 1 << 21  # RA_NOALLOC_MAX_ROWS (include/ra.h)
 RING_DOUBLE_BUFFER = 1

@@ -5,6 +5,11 @@
 Each HIP source is compiled to an object under <repo>/_build/ in parallel and
 linked into long_context_exact_step_amd/libra.so; the plain-C client
 (csrc/ra_client.c) is then built beside it as ra_client.  Always rebuilds.
+
+build_sanitized() builds the same library with the host code instrumented by
+AddressSanitizer and UndefinedBehaviorSanitizer (device code as usual); the
+CPU tests load it with the sanitizer runtime preloaded and run the host-side
+validation and ring-walk logic against it.
 """
 
 import os
@@ -29,9 +34,24 @@ def hipcc():
     return p if os.path.exists(p) else "hipcc"
 
 
-def common_flags(extra=()):
+# Host-only sanitizers: -Xarch_host keeps them off the device code.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime():
+    """The clang ASan runtime (with the UBSan handlers) that a process must
+    preload to load the sanitized library; None if absent."""
+    import glob
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    found = sorted(glob.glob(os.path.join(rocm, "llvm", "lib", "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    return found[-1] if found else None
+
+
+def common_flags(extra=(), opt="-O3"):
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        f"--offload-arch={ARCH}", opt, "-std=c++17", "-fPIC",
         # No packed-fp32 VALU instructions in any kernel.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I" + INCLUDE, "-I" + CSRC, *extra,
@@ -47,14 +67,14 @@ def _run(cmd):
     return err
 
 
-def build(verbose=False, extra_flags=(), out=LIB):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, extra_flags=(), out=LIB, build_dir=BUILD, opt="-O3"):
+    os.makedirs(build_dir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc(), *common_flags(extra_flags), "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc(), *common_flags(extra_flags, opt), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
         for err in ex.map(_run, cmds):
             if verbose and err.strip():
@@ -69,6 +89,13 @@ def build(verbose=False, extra_flags=(), out=LIB):
         if verbose:
             print(f"built {client}", file=sys.stderr)
     return out
+
+
+def build_sanitized(out_dir, verbose=False):
+    """libra_san.so under out_dir: host code with ASan + UBSan (-O1 -g),
+    device code unchanged.  Returns its path."""
+    return build(verbose=verbose, extra_flags=("-g", *SANITIZE_HOST), out=os.path.join(out_dir, "libra_san.so"),
+                 build_dir=os.path.join(out_dir, "obj"), opt="-O1")
 
 
 def build_client():
