@@ -206,9 +206,28 @@ def walk_stats(rec, flops, steps):
                          "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}}
 
 
-def run_fwd(w, steps, warmup, ring_mode, H_kv=None):
+def untraced_steps(step_fn, steps, warmup):
+    """Runs warmup, then exactly `steps` timed steps with no per-launch
+    events (for walks of many short launches, where bracketing every launch
+    adds a gap of its own).  Returns seconds."""
+    import torch
+
+    for _ in range(warmup):
+        step_fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step_fn()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def run_fwd(w, steps, warmup, ring_mode, H_kv=None, trace=True, concurrent=False):
     """The forward walk of workload w; H_kv < H runs it with grouped-query
-    key/value chunks of H_kv heads."""
+    key/value chunks of H_kv heads.  trace=False times the steps without
+    per-launch events (no per-kernel figures then).  concurrent=True walks
+    every rank on a stream of its own, with its own staging slots, as the
+    ranks of a real ring run at once (untraced)."""
     import torch
     import long_context_exact_step_amd as ra
     from long_context_exact_step_amd import inputs
@@ -222,9 +241,19 @@ def run_fwd(w, steps, warmup, ring_mode, H_kv=None):
     vs = [inputs.chunk(w.id, inputs.V, j, B, Hk, C, d).to(dev) for j in range(P)]
     o = {r: torch.empty(B, H, C, d, device=dev) for r in w.ranks}
     lse = {r: torch.empty(B, H, C, device=dev) for r in w.ranks}
-    ws = torch.empty(max(1, ra.workspace_bytes(P, B, H, C, d, ring_mode, H_kv=Hk)), dtype=torch.uint8,
-                     device=dev)
-    copy_stream = torch.cuda.Stream(dev) if ring_mode == "double_buffer" else None
+    # "double_buffer_in_kernel": the double-buffer walk with no copy stream,
+    # each step kernel staging the next chunk itself.
+    in_kernel = ring_mode == "double_buffer_in_kernel"
+    if in_kernel:
+        ring_mode = "double_buffer"
+    nws = len(w.ranks) if concurrent else 1
+    wss = [torch.empty(max(1, ra.workspace_bytes(P, B, H, C, d, ring_mode, H_kv=Hk)), dtype=torch.uint8,
+                       device=dev) for _ in range(nws)]
+    ws = wss[0]
+    copy_stream = torch.cuda.Stream(dev) if ring_mode == "double_buffer" and not in_kernel else None
+    if concurrent and copy_stream is not None:
+        raise SystemExit("concurrent ranks: in-kernel staging or resident walks only (one copy stream per call)")
+    streams = [torch.cuda.Stream(dev) for _ in w.ranks] if concurrent else None
     # The fused mode walks a rank's chunks in one launch where the library's
     # rule allows it, else per step; the launch count and the kernel stats
     # follow what runs.
@@ -240,34 +269,55 @@ def run_fwd(w, steps, warmup, ring_mode, H_kv=None):
             ra.ring_fwd(qs[r], ks, vs, o[r], lse[r], r, w.causal, w.scale, ring_mode=ring_mode,
                         workspace=ws, copy_stream=copy_stream)
 
-    secs, rec = timed_steps(step, n_launch, steps, warmup)
+    def step_concurrent():
+        # Each rank's walk on its own stream, after the work queued so far.
+        cur = torch.cuda.current_stream(dev)
+        for n, r in enumerate(w.ranks):
+            streams[n].wait_stream(cur)
+            ra.ring_fwd(qs[r], ks, vs, o[r], lse[r], r, w.causal, w.scale, ring_mode=ring_mode,
+                        workspace=wss[n], stream=streams[n], copy_stream=None)
+        for st in streams:
+            cur.wait_stream(st)
+
+    if concurrent:
+        secs, rec = untraced_steps(step_concurrent, steps, warmup), []
+        trace = False
+    elif trace:
+        secs, rec = timed_steps(step, n_launch, steps, warmup)
+    else:
+        secs, rec = untraced_steps(step, steps, warmup), []
     flops = fwd_flops(w)
     res = {
         "secs": secs, "ms_per_step": secs / steps * 1e3,
         "tflops": flops * steps / secs / 1e12,
         "tokens_per_s": B * C * len(w.ranks) * steps / secs,
-        "kernels": (walk_stats(rec, flops, steps) if fused else kernel_stats(rec, w, lambda k: 4 * d)),
+        "launches_per_step": n_launch,
+        "kernels": ({} if not trace else
+                    walk_stats(rec, flops, steps) if fused else kernel_stats(rec, w, lambda k: 4 * d)),
         "kv_bytes_per_ring_step": 2 * B * Hk * C * d * 2,
         "rec": rec,
     }
     return res, (qs, ks, vs, o, lse)
 
 
-def config_line(w, steps, warmup, ring_mode):
+def config_line(w, steps, warmup, ring_mode, concurrent=False):
     """The forward walk of workload w (every rank it lists) as a bench line:
     ms per step, algorithmic TFLOP/s, tokens/s and the fraction of the bf16
-    peak.  Tokens are the local query tokens of every walked rank."""
+    peak.  Tokens are the local query tokens of every walked rank.  Timed
+    without per-launch events."""
     import torch
-    r, tensors = run_fwd(w, steps, warmup, ring_mode)
+    r, tensors = run_fwd(w, steps, warmup, ring_mode, trace=False, concurrent=concurrent)
     del tensors
     torch.cuda.empty_cache()
     return {
         "workload": w.name, "ring_mode": ring_mode, "ranks": list(w.ranks), "steps": steps, "warmup": warmup,
+        "ranks_walked": "concurrently, one stream each" if concurrent else "one after another, one stream",
         "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["tflops"], 2),
         "tokens_per_s": round(r["tokens_per_s"], 1),
         "frac_bf16_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
         "frac_derived_peak": round(r["tflops"] / DERIVED_PEAK_BF16_TFLOPS, 4),
-        "launches_per_step": sum(v["launches"] for v in r["kernels"].values()) // steps,
+        "launches_per_step": r["launches_per_step"],
+        "timing": "wall clock over the timed steps, no per-launch events",
     }
 
 
@@ -589,7 +639,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--ring-mode", default="double_buffer", choices=["double_buffer", "resident", "fused"])
+    ap.add_argument("--ring-mode", default="double_buffer",
+                    choices=["double_buffer", "double_buffer_in_kernel", "resident", "fused"])
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query (H_kv = H/4) measurements")
@@ -686,13 +737,19 @@ def main():
         # 32K full ring over all ranks, the 1M share; the full ring in both the
         # double-buffer walk (the ring's emulation) and the fused walk.
         cfgs = {}
-        for key, wid, mode, st in (("tiny_ring", 1, "double_buffer", args.steps),
-                                   ("full_ring_32k_double_buffer", 3, "double_buffer", args.steps),
-                                   ("full_ring_32k_fused", 3, "fused", args.steps),
-                                   ("share_1m_cp8", 4, "double_buffer", 5)):
-            if wid == w.id and mode == args.ring_mode:
+        for key, wid, mode, st, conc in (
+                ("tiny_ring", 1, "double_buffer", args.steps, False),
+                ("share_128k_cp4_double_buffer_in_kernel", 2, "double_buffer_in_kernel", args.steps, False),
+                ("full_ring_32k_double_buffer", 3, "double_buffer", args.steps, False),
+                ("full_ring_32k_double_buffer_in_kernel", 3, "double_buffer_in_kernel", args.steps, False),
+                ("full_ring_32k_double_buffer_in_kernel_ranks_concurrent", 3, "double_buffer_in_kernel",
+                 args.steps, True),
+                ("full_ring_32k_resident", 3, "resident", args.steps, False),
+                ("full_ring_32k_fused", 3, "fused", args.steps, False),
+                ("share_1m_cp8", 4, "double_buffer", 5, False)):
+            if wid == w.id and mode == args.ring_mode and not conc:
                 continue
-            c = config_line(WORKLOADS[wid], st, min(2, args.warmup), mode)
+            c = config_line(WORKLOADS[wid], st, min(2, args.warmup), mode, concurrent=conc)
             cfgs[key] = c
             print(f"[bench] {key}: {c['ms_per_step']:.3f} ms/step, {c['tflops']:.1f} TFLOP/s "
                   f"({c['frac_bf16_peak']:.3f} of peak), {c['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)

@@ -72,7 +72,8 @@ enum ra_ring_mode {
   RA_RING_RESIDENT = 0,      /* walk the resident chunks in ring order, no copies */
   RA_RING_DOUBLE_BUFFER = 1, /* stage each chunk into a 2-slot buffer first (the
                                 emulated receive), overlapped with the previous
-                                step's compute when copy_stream is given */
+                                step's compute: on copy_stream when given, else
+                                by the previous step's kernel itself */
   RA_RING_FUSED = 2          /* resident chunks walked by one launch: the
                                 online-softmax state runs on from chunk to
                                 chunk in registers and no partial crosses HBM.
@@ -151,11 +152,15 @@ size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d,
  * o [B,H,C,d] and lse [B,H,C] (fp32) are overwritten with the final result.
  *
  * ring_mode RA_RING_DOUBLE_BUFFER needs ra_ring_workspace_bytes(...) of
- * workspace: the chunk of step s >= 1 is copied into slot (s-1) & 1 on
- * copy_stream (or on stream when copy_stream is NULL) while step s-1
- * computes, with events ordering slot reuse -- the stand-in for the ring's
- * receive from the left neighbour ("Training Long-Context Models Without
- * OOM: Ring Attention", "Ring Attention Demystified", items 3-4).
+ * workspace: the chunk of step s >= 1 is copied into slot (s-1) & 1 while
+ * step s-1 computes -- the stand-in for the ring's receive from the left
+ * neighbour ("Training Long-Context Models Without OOM: Ring Attention",
+ * "Ring Attention Demystified", items 3-4).  With a copy_stream the copies
+ * run there, with events ordering slot reuse.  With copy_stream NULL the
+ * kernel of step s-1 makes the copy itself: each of its blocks copies a
+ * share of the chunk once its own tiles are done, so the walk is one
+ * stream of kernels with no copies or events elsewhere (cheaper per step
+ * for short chunks).
  * RA_RING_RESIDENT reads the chunks in place and needs no workspace.
  * When the call returns, all work is ordered on `stream` (copy_stream work
  * is joined back into it).

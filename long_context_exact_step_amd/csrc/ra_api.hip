@@ -319,7 +319,7 @@ int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks, const void* cons
   if (need > 0 && !aligned16(workspace)) return fail(RA_ERR_ALIGN, "ra_ring_fwd: workspace not 16-byte aligned");
 
   hipStream_t cs = static_cast<hipStream_t>(stream);
-  hipStream_t xs = copy_stream ? static_cast<hipStream_t>(copy_stream) : cs;
+  hipStream_t xs = static_cast<hipStream_t>(copy_stream);
   const std::vector<Step> steps = visible_steps(rank, P, causal != 0);
   const size_t chunk_bytes = (size_t)B * H_kv * C * d * 2;
   const uint16_t* qh = static_cast<const uint16_t*>(q);
@@ -363,18 +363,35 @@ int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks, const void* cons
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   auto slot_k = [&](int slot) { return ws + (size_t)slot * 2 * chunk_bytes; };
   auto slot_v = [&](int slot) { return ws + (size_t)slot * 2 * chunk_bytes + chunk_bytes; };
-  RingEvents* ev = nullptr;
-  hipError_t e = hipSuccess;
-  const bool two_streams = xs != cs;
-  if (two_streams) {
-    e = ring_events(&ev);
-    if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd events");
-    // Copies may start only after everything already queued on the compute
-    // stream (the inputs, and any earlier user of the workspace).
-    if ((e = hipEventRecord(ev->start, cs)) != hipSuccess) return hip_fail(e, "ra_ring_fwd record");
-    if ((e = hipStreamWaitEvent(xs, ev->start, 0)) != hipSuccess) return hip_fail(e, "ra_ring_fwd wait");
-  }
   const int n = (int)steps.size();
+  hipError_t e = hipSuccess;
+  if (!copy_stream) {
+    // No copy stream: step i's kernel itself copies the chunk of step i+1
+    // into slot i & 1 once its blocks have done their own work.  That slot
+    // was last read by step i-1's kernel and is next read by step i+1's,
+    // both ordered by the stream, so no copy or event goes elsewhere.
+    for (int i = 0; i < n; ++i) {
+      const Step& sp = steps[i];
+      ra::StageCopy sc{};
+      if (i + 1 < n) {
+        const int j = steps[i + 1].j;
+        sc = ra::StageCopy{{k_chunks[j], v_chunks[j]}, {slot_k(i & 1), slot_v(i & 1)}, chunk_bytes / 16};
+      }
+      ra::FwdStepArgs a = i == 0 ? step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, false)
+                                 : step_args(slot_k((i - 1) & 1), slot_v((i - 1) & 1), sp.diag, true);
+      if (i + 1 < n) a.stage = &sc;
+      if ((e = fwd_step(a, cs)) != hipSuccess) return hip_fail(e, "ra_ring_fwd step");
+    }
+    return ok();
+  }
+
+  // Copy stream: the staging copies run there, ordered by events.
+  RingEvents* ev = nullptr;
+  if ((e = ring_events(&ev)) != hipSuccess) return hip_fail(e, "ra_ring_fwd events");
+  // Copies may start only after everything already queued on the compute
+  // stream (the inputs, and any earlier user of the workspace).
+  if ((e = hipEventRecord(ev->start, cs)) != hipSuccess) return hip_fail(e, "ra_ring_fwd record");
+  if ((e = hipStreamWaitEvent(xs, ev->start, 0)) != hipSuccess) return hip_fail(e, "ra_ring_fwd wait");
   for (int i = 0; i < n; ++i) {
     // Stage the chunk for step i+1 (slot i & 1); that slot was last read by
     // step i-1 (step 0 reads the local chunk in place), so from i = 2 on the
@@ -382,25 +399,22 @@ int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks, const void* cons
     if (i + 1 < n) {
       const int slot = i & 1;
       const int j = steps[i + 1].j;
-      if (two_streams && i >= 2) {
-        if ((e = hipStreamWaitEvent(xs, ev->consumed[slot], 0)) != hipSuccess) return hip_fail(e, "ra_ring_fwd wait");
-      }
+      if (i >= 2 && (e = hipStreamWaitEvent(xs, ev->consumed[slot], 0)) != hipSuccess)
+        return hip_fail(e, "ra_ring_fwd wait");
       if ((e = hipMemcpyAsync(slot_k(slot), k_chunks[j], chunk_bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess)
         return hip_fail(e, "ra_ring_fwd stage K");
       if ((e = hipMemcpyAsync(slot_v(slot), v_chunks[j], chunk_bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess)
         return hip_fail(e, "ra_ring_fwd stage V");
-      if (two_streams && (e = hipEventRecord(ev->copied[slot], xs)) != hipSuccess)
-        return hip_fail(e, "ra_ring_fwd record");
+      if ((e = hipEventRecord(ev->copied[slot], xs)) != hipSuccess) return hip_fail(e, "ra_ring_fwd record");
     }
     const Step& sp = steps[i];
     if (i == 0) {
       e = fwd_step(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, false), cs);
     } else {
       const int slot = (i - 1) & 1;
-      if (two_streams && (e = hipStreamWaitEvent(cs, ev->copied[slot], 0)) != hipSuccess)
-        return hip_fail(e, "ra_ring_fwd wait");
+      if ((e = hipStreamWaitEvent(cs, ev->copied[slot], 0)) != hipSuccess) return hip_fail(e, "ra_ring_fwd wait");
       e = fwd_step(step_args(slot_k(slot), slot_v(slot), sp.diag, true), cs);
-      if (e == hipSuccess && two_streams) e = hipEventRecord(ev->consumed[slot], cs);
+      if (e == hipSuccess) e = hipEventRecord(ev->consumed[slot], cs);
     }
     if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd step");
   }

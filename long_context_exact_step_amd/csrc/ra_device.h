@@ -246,4 +246,28 @@ __device__ __forceinline__ void wait_vmem_but() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// This block's share of a staging copy: units [b*per, min((b+1)*per, n)) of
+// each tensor, per = ceil(n / gridDim.x), 16 bytes per unit, UNROLL loads in
+// flight per thread.  Every thread of the block calls it.
+template <int NTHREADS, int UNROLL = 4>
+__device__ __forceinline__ void stage_block_share(const void* const (&src)[2], void* const (&dst)[2], size_t n) {
+  if (n == 0) return;
+  const size_t per = (n + gridDim.x - 1) / gridDim.x;
+  const size_t u0 = (size_t)blockIdx.x * per;
+  const size_t u1 = u0 + per < n ? u0 + per : n;
+  for (int t = 0; t < 2; ++t) {
+    const u32x4* __restrict__ s = static_cast<const u32x4*>(src[t]);
+    u32x4* __restrict__ d = static_cast<u32x4*>(dst[t]);
+    for (size_t u = u0 + threadIdx.x; u < u1; u += (size_t)NTHREADS * UNROLL) {
+      u32x4 v[UNROLL];
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k)
+        if (u + (size_t)k * NTHREADS < u1) v[k] = __builtin_nontemporal_load(s + u + (size_t)k * NTHREADS);
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k)
+        if (u + (size_t)k * NTHREADS < u1) d[u + (size_t)k * NTHREADS] = v[k];
+    }
+  }
+}
+
 }  // namespace ra

@@ -135,7 +135,8 @@ template <int D, bool DIAG, bool MERGE, bool WALK>
 __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
                                          const uint16_t* __restrict__ vg, float* __restrict__ og,
                                          float* __restrict__ lseg, int Sq, int Sk, int n_qtiles, int total_tiles,
-                                         float scale_log2, int group, int qoff, const ChunkTable& tbl) {
+                                         float scale_log2, int group, int qoff, const ChunkTable& tbl,
+                                         const StageCopy& stage) {
   constexpr int NW = kFwdWaves, NQW = kFwdRowsPerWave, BR = NW * NQW, BC = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kFwdLookahead;
   constexpr int NB = kFwdBuffers;
@@ -485,6 +486,10 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
     phase_barrier();
   };
 
+  // The ring's next chunk into the idle slot (this block's share), while the
+  // block's first tile loads are in flight.
+  if constexpr (!WALK) stage_block_share<64 * NW, 8>(stage.src, stage.dst, stage.units);
+
   // Prologue: S^T(0) once K(0) has landed (computed, harmlessly, also for a
   // wave with no rows); its stream issues iteration 0's first reads.
   wait_vmem();
@@ -517,10 +522,11 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
                                                                   float* __restrict__ og,
                                                                   float* __restrict__ lseg, int Sq, int Sk,
                                                                   int n_qtiles, int total_tiles,
-                                                                  float scale_log2, int group, int qoff) {
+                                                                  float scale_log2, int group, int qoff,
+                                                                  StageCopy stage) {
   const ChunkTable none{};
   fwd_body<D, DIAG, MERGE, false>(qg, kg, vg, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group, qoff,
-                                  none);
+                                  none, stage);
 }
 
 // One pass over resident chunks (no merge: the pass sees every key).
@@ -531,8 +537,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_walk_kernel(const uint16_t
                                                                   int n_qtiles, int total_tiles,
                                                                   float scale_log2, int group, int qoff,
                                                                   ChunkTable tbl) {
+  const StageCopy none{};
   fwd_body<D, DIAG, false, true>(qg, nullptr, nullptr, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group,
-                                 qoff, tbl);
+                                 qoff, tbl, none);
 }
 
 template <int D>
@@ -548,7 +555,7 @@ hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)total), block(64 * kFwdWaves);
   if (a.walk) {
     const ChunkTable& t = *a.walk;
-    if (a.merge || t.n < 1 || t.n > kMaxWalkChunks || t.C < 1 || t.C % kTileTokens ||
+    if (a.merge || a.stage || t.n < 1 || t.n > kMaxWalkChunks || t.C < 1 || t.C % kTileTokens ||
         (long long)t.n * t.C != a.Sk)
       return hipErrorInvalidValue;
     if (a.diag)
@@ -559,9 +566,10 @@ hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
                          (int)total, sl2, a.group, a.qoff, t);
     return hipGetLastError();
   }
+  const StageCopy stage = a.stage ? *a.stage : StageCopy{};
 #define RA_FWD_LAUNCH(DIAG, MERGE)                                                                         \
   hipLaunchKernelGGL((fwd_step_kernel<D, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, a.v, a.o, \
-                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff)
+                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff, stage)
   if (a.diag) {
     if (a.merge) RA_FWD_LAUNCH(true, true);
     else RA_FWD_LAUNCH(true, false);

@@ -21,6 +21,16 @@ struct ChunkTable {
   int C;  // tokens per chunk
 };
 
+// In-kernel staging of the ring's next key/value chunk: after its own work,
+// every block of a step launch copies its share of `units` 16-byte units of
+// each of the two tensors from src[t] to dst[t] (the idle slot of the double
+// buffer).  units == 0: no copy.
+struct StageCopy {
+  const void* src[2];
+  void* dst[2];
+  size_t units;
+};
+
 struct FwdStepArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -36,6 +46,8 @@ struct FwdStepArgs {
   // Non-null: the keys are walk->n resident chunks (k, v unused; Sk =
   // n * C; merge must be false).
   const ChunkTable* walk = nullptr;
+  // Non-null: stage the next chunk from inside this launch (step kernels only).
+  const StageCopy* stage = nullptr;
 };
 hipError_t launch_fwd_step(const FwdStepArgs& a, hipStream_t stream);
 

@@ -103,10 +103,11 @@ def test_lse_merge_past_2_26_rows():
     (1, 100, 128, True), (2, 3, 64, True), (4, 100, 128, True), (3, 129, 64, False),
     (4, 64, 128, False), (2, 200, 128, True),
 ])
-@pytest.mark.parametrize("mode", ["resident", "double_buffer", "double_buffer_one_stream"])
+@pytest.mark.parametrize("mode", ["resident", "double_buffer", "double_buffer_in_kernel"])
 def test_ring_fwd_every_rank(P, C, d, causal, mode):
-    """double_buffer_one_stream: staging copies serialized on the compute
-    stream (no copy stream given)."""
+    """double_buffer_in_kernel: no copy stream given, so each step's kernel
+    stages the next chunk into the idle slot itself (a wrong or late copy
+    would show up in the next step's result)."""
     B, H = 1, 2
     q, k, v, _ = ring_tensors(102, B, H, P, C, d)
     kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))

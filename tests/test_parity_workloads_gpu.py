@@ -63,8 +63,10 @@ def gen_workload(w, ranks=None, with_do=False, H_kv=None):
 def gpu_ring_fwd(w, rank, q, kd, vd, mode="double_buffer"):
     o = torch.full((w.B, w.H, w.C, w.d), float("nan"), device=dev())
     lse = torch.full((w.B, w.H, w.C), float("nan"), device=dev())
+    # "double_buffer_in_kernel": no copy stream, each step kernel stages the next chunk.
     cs = torch.cuda.Stream(dev()) if mode == "double_buffer" else None
-    ra.ring_fwd(q.to(dev()), kd, vd, o, lse, rank, w.causal, w.scale, ring_mode=mode, copy_stream=cs)
+    ring_mode = "double_buffer" if mode == "double_buffer_in_kernel" else mode
+    ra.ring_fwd(q.to(dev()), kd, vd, o, lse, rank, w.causal, w.scale, ring_mode=ring_mode, copy_stream=cs)
     torch.cuda.synchronize()
     return o, lse
 
@@ -137,11 +139,13 @@ def test_full_ring_all_rows():
     kd = [t.to(dev()) for t in k]
     vd = [t.to(dev()) for t in v]
     for r in w.ranks:
-        say(f"full ring rank {r}: GPU walk (double buffer, and fused), then oracle on all {w.C} rows x {w.H} heads")
+        say(f"full ring rank {r}: GPU walk (double buffer with a copy stream, with in-kernel staging, and "
+            f"fused), then oracle on all {w.C} rows x {w.H} heads")
         o, lse = gpu_ring_fwd(w, r, q[r], kd, vd)
+        io, il = gpu_ring_fwd(w, r, q[r], kd, vd, "double_buffer_in_kernel")
         fo, fl = gpu_ring_fwd(w, r, q[r], kd, vd, "fused")
         check_rows(w, r, q[r], k, v, o, lse, lambda h: np.arange(w.C), f"full ring rank {r}",
-                   more=[(fo, fl, f"full ring rank {r} fused")])
+                   more=[(io, il, f"full ring rank {r} in-kernel staging"), (fo, fl, f"full ring rank {r} fused")])
 
 
 # ---------------------------------------------------------------------------
@@ -172,10 +176,11 @@ def test_local_share_sampled_rows(wid, share_inputs):
     w = WORKLOADS[wid]
     r = w.ranks[0]
     q, k, v, kd, vd = share_inputs(wid)
-    say(f"{w.name}: GPU walk")
+    say(f"{w.name}: GPU walk (copy stream, and in-kernel staging)")
     o, lse = gpu_ring_fwd(w, r, q[r], kd, vd)
+    io, il = gpu_ring_fwd(w, r, q[r], kd, vd, "double_buffer_in_kernel")
     check_rows(w, r, q[r], k, v, o, lse, lambda h: inputs.query_row_sample(w.id, h, w.C),
-               f"{w.name} sampled rows")
+               f"{w.name} sampled rows", more=[(io, il, f"{w.name} in-kernel staging sampled rows")])
 
 
 @pytest.mark.timeout(600)
