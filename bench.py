@@ -532,6 +532,58 @@ def mfma_ceiling(iters=200000):
     return out
 
 
+LADDER_LEVELS = {
+    0: "dense probe: independent accumulators, register operands",
+    1: "+ the kernel's accumulator pattern (4 P V outputs, 2 score chains restarting per tile)",
+    2: "+ A operands read from LDS (ds_read_b64_tr_b16 pairs, ds_read_b128), 3 MFMAs ahead",
+    3: "+ online softmax of the previous tile in the MFMA slots (scale, exp2, row sum, bf16 pack)",
+    4: "+ one workgroup barrier per 64-key tile",
+    5: "+ direct-to-LDS tile loads two tiles ahead, waited for before the barrier",
+}
+
+
+def fwd_ladder(iters=20000):
+    """The forward kernel's instruction stream rebuilt from the MFMA probe
+    one feature per level (ra_fwd_ladder_probe), each on random N(0,1) and
+    on all-zero data: TFLOP/s and the clock the cores ran at.  Random data
+    show what each feature costs under the power limit; zeros show what it
+    costs in the schedule at the unthrottled clock."""
+    import torch
+    import long_context_exact_step_amd as ra
+
+    dev = torch.device("cuda", 0)
+    cus, _ = ra.device_info()
+    gen = torch.Generator().manual_seed(20261203)
+    data = {"random": (torch.randn(10240, generator=gen).to(torch.bfloat16).to(dev),
+                       torch.randn(524288, generator=gen).to(torch.bfloat16).to(dev)),
+            "zero": (torch.zeros(10240, dtype=torch.bfloat16, device=dev),
+                     torch.zeros(524288, dtype=torch.bfloat16, device=dev))}
+    sink = torch.empty(cus * 512, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    flops = cus * 8 * iters * 4194304
+    c = 1.0 / math.sqrt(128) * 1.4426950408889634
+    out = {}
+    for level, what in LADDER_LEVELS.items():
+        row = {"adds": what}
+        for name, (ops, tiles) in data.items():
+            ra.fwd_ladder_probe(level, ops, tiles, sink, clocks, cus, max(1, iters // 20), c)  # warm-up
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            ra.fwd_ladder_probe(level, ops, tiles, sink, clocks, cus, iters, c)
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1)
+            cyc, ref = clocks.tolist()
+            tf = flops / (ms * 1e-3) / 1e12
+            row[name] = {"tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "clock_ghz": round(cyc / (ref / 100e6) / 1e9, 3) if ref > 0 else None,
+                         # Cycles per 32-MFMA tile per SIMD pair (the floor is 2 x 32 x 32 = 2048).
+                         "cycles_per_tile": round(cyc / (iters * 4), 1)}
+        out[f"level{level}"] = row
+    return out
+
+
 def step_on_zeros(w, launches=5):
     """One full-chunk forward step (ra_step_fwd, no mask) at the workload's
     chunk shape on its seeded N(0,1) inputs and on all-zero inputs.  The
@@ -718,6 +770,12 @@ def main():
         ce = mfma_ceiling()
         ce["kernel_frac_of_random_ceiling"] = round(achieved / ce["random"]["tflops"], 4)
         ce["step_kernel_by_input_data"] = step_on_zeros(w)
+        ce["fwd_ladder"] = fwd_ladder()
+        for lv, row in ce["fwd_ladder"].items():
+            print(f"[bench] ladder {lv}: random {row['random']['tflops']} TFLOP/s at {row['random']['clock_ghz']} GHz"
+                  f" ({row['random']['cycles_per_tile']} cyc/tile), zero {row['zero']['tflops']} at "
+                  f"{row['zero']['clock_ghz']} GHz ({row['zero']['cycles_per_tile']} cyc/tile)", file=sys.stderr,
+                  flush=True)
         out["mfma_ceiling"] = ce
         print(f"[bench] MFMA probe: random {ce['random']['tflops']} TFLOP/s at {ce['random']['clock_ghz']} GHz, "
               f"zero {ce['zero']['tflops']} TFLOP/s at {ce['zero']['clock_ghz']} GHz; derived peak "

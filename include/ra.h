@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define RA_VERSION 5
+#define RA_VERSION 6
 
 enum ra_status {
   RA_OK = 0,
@@ -413,6 +413,28 @@ int ra_trace_end(void);
  * the clock the cores ran at.  Asynchronous on `stream`; RA_ERR_NULL,
  * RA_ERR_SHAPE (blocks or iters < 1), RA_ERR_HIP.
  */
+/*
+ * ra_fwd_ladder_probe rebuilds the forward step kernel's instruction stream
+ * on synthetic data, one feature per level, to account for the distance
+ * between ra_mfma_probe's rate and the attention kernel's.  Every level has
+ * `blocks` workgroups of 8 waves (one per CU, 128 KB of LDS each, two waves
+ * per SIMD) and each wave issues iters * 4 tiles of 32 bf16 32x32x16 MFMAs:
+ * 4194304 * iters flop per wave.  Level 0: the dense probe (independent
+ * accumulators, register operands); 1: the kernel's accumulator pattern
+ * (four P V outputs, two score chains restarting every tile); 2: A operands
+ * read from LDS as the kernel reads them (ds_read_b64_tr_b16 pairs and
+ * ds_read_b128, three MFMAs ahead); 3: the online softmax of the previous
+ * tile's scores in the MFMA slots (scores times c, exp2, row sum, bf16
+ * pack into the next P V operand); 4: a workgroup barrier per tile; 5: the
+ * tile loads (direct-to-LDS buffer loads two tiles ahead, waited for before
+ * the barrier).  operands: device, >= 20480 bytes of bf16 data for the
+ * register operands; tiles: device, >= 1 MiB of bf16 data for the LDS
+ * tiles and the tile loads.  sink: blocks * 512 floats; clocks: 2 values,
+ * as for ra_mfma_probe.  RA_ERR_NULL, RA_ERR_SHAPE (level outside [0, 5],
+ * blocks or iters < 1), RA_ERR_HIP.
+ */
+int ra_fwd_ladder_probe(int level, const void* operands, const void* tiles, float* sink,
+                        unsigned long long* clocks, int blocks, int iters, float c, void* stream);
 int ra_device_info(int* cu_count, int* max_clock_khz);
 int ra_mfma_probe(const void* operands, float* sink, unsigned long long* clocks, int blocks, int iters,
                   void* stream);

@@ -18,7 +18,7 @@ __all__ = [
     "workspace_bytes", "ring_bwd_noalloc", "NOALLOC_MAX_ROWS", "RING_RESIDENT", "RING_DOUBLE_BUFFER", "LIB_PATH", "trace_begin", "trace_end",
     "ulysses_fwd", "ulysses_bwd", "ulysses_workspace_bytes",
     "allgather_fwd", "allgather_bwd", "allgather_workspace_bytes",
-    "TRACE_KINDS", "device_info", "mfma_probe",
+    "TRACE_KINDS", "device_info", "mfma_probe", "fwd_ladder_probe",
 ]
 
 # ra_trace_kind values (include/ra.h).
@@ -102,6 +102,8 @@ def lib():
         L.ra_device_info.argtypes = [ctypes.POINTER(i), ctypes.POINTER(i)]
         L.ra_mfma_probe.restype = i
         L.ra_mfma_probe.argtypes = [vp, vp, vp, i, i, vp]
+        L.ra_fwd_ladder_probe.restype = i
+        L.ra_fwd_ladder_probe.argtypes = [i, vp, vp, vp, vp, i, i, f, vp]
         _lib = L
     return _lib
 
@@ -476,3 +478,24 @@ def mfma_probe(operands, sink, clocks, blocks, iters, stream=None):
     _check(lib().ra_mfma_probe(_ptr(operands), _ptr(sink), _ptr(clocks), int(blocks), int(iters),
                                _stream(stream, sink)))
 
+
+
+def fwd_ladder_probe(level, operands, tiles, sink, clocks, blocks, iters, c, stream=None):
+    """ra_fwd_ladder_probe: the forward kernel's instruction stream rebuilt
+    on synthetic data up to `level` (0..5).  operands: >= 10240 bf16 values;
+    tiles: >= 524288 bf16 values; sink: float32, >= blocks * 512; clocks:
+    int64, >= 2.  4194304 * iters flop per wave, 8 waves per block."""
+    import torch
+    if operands.dtype != torch.bfloat16 or operands.numel() * 2 < 20480:
+        raise ValueError("operands: expected >= 10240 bf16 values")
+    if tiles.dtype != torch.bfloat16 or tiles.numel() * 2 < (1 << 20):
+        raise ValueError("tiles: expected >= 524288 bf16 values")
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 512:
+        raise ValueError(f"sink: expected >= {blocks * 512} float32 values")
+    if clocks.dtype != torch.int64 or clocks.numel() < 2:
+        raise ValueError("clocks: expected >= 2 int64 values")
+    for t, n in ((operands, "operands"), (tiles, "tiles"), (sink, "sink"), (clocks, "clocks")):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{n}: must be a contiguous GPU tensor")
+    _check(lib().ra_fwd_ladder_probe(int(level), _ptr(operands), _ptr(tiles), _ptr(sink), _ptr(clocks), int(blocks),
+                                     int(iters), float(c), _stream(stream, sink)))

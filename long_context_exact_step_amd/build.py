@@ -24,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libra.so")
 CLIENT = os.path.join(PKG, "ra_client")
-SOURCES = ["ra_api.hip", "ra_fwd.hip", "ra_merge.hip", "ra_bwd.hip", "ra_ceiling.hip"]
+SOURCES = ["ra_api.hip", "ra_fwd.hip", "ra_merge.hip", "ra_bwd.hip", "ra_ceiling.hip", "ra_ladder.hip"]
 ARCH = "gfx950"
 
 

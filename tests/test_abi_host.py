@@ -40,8 +40,8 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     # 2: grouped-query (*_gqa) entry points; 3: ra_ulysses_fwd, ra_ulysses_bwd;
-    # 4: ra_allgather_fwd, ra_allgather_bwd; 5: ra_ring_bwd_noalloc
-    assert L.ra_version() == 5
+    # 4: ra_allgather_fwd, ra_allgather_bwd; 5: ra_ring_bwd_noalloc; 6: ra_fwd_ladder_probe
+    assert L.ra_version() == 6
     assert L.ra_status_string(RA_OK) == b"RA_OK"
     assert L.ra_status_string(RA_ERR_WORKSPACE) == b"RA_ERR_WORKSPACE"
     assert L.ra_status_string(12345) == b"RA_ERR_UNKNOWN"
@@ -273,6 +273,12 @@ def test_probe_helpers_validation(L):
     assert L.ra_mfma_probe(vp(0), vp(FAKE), vp(FAKE), 1, 1, None) == RA_ERR_NULL
     assert L.ra_mfma_probe(vp(FAKE), vp(FAKE), vp(FAKE), 0, 1, None) == RA_ERR_SHAPE
     assert L.ra_mfma_probe(vp(FAKE), vp(FAKE), vp(FAKE), 4, 0, None) == RA_ERR_SHAPE
+    L.ra_fwd_ladder_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+    assert L.ra_fwd_ladder_probe(0, None, vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 0.1, None) == RA_ERR_NULL
+    assert L.ra_fwd_ladder_probe(6, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 0.1, None) == RA_ERR_SHAPE
+    assert L.ra_fwd_ladder_probe(-1, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 0.1, None) == RA_ERR_SHAPE
+    assert L.ra_fwd_ladder_probe(2, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 0, 1, 0.1, None) == RA_ERR_SHAPE
 
 
 

@@ -666,3 +666,28 @@ def test_mfma_probe_runs_within_the_derived_peak():
     rate = cus * 8 * iters * 16 * 32768 / (t0.elapsed_time(t1) * 1e-3)
     print(f"  random operands: {rate / 1e12:.0f} TFLOP/s of a derived {peak / 1e12:.0f}", flush=True)
     assert torch.isfinite(sink).all() and 0 < rate <= 1.02 * peak
+
+
+def test_fwd_ladder_probe_runs_within_the_derived_peak():
+    """Every level of the ladder probe runs, gives finite sums on random
+    operands, records a clock, and stays under the derived peak."""
+    cus, clk_khz = ra.device_info()
+    peak = cus * 4096 * clk_khz * 1e3
+    gen = torch.Generator().manual_seed(5)
+    ops = torch.randn(10240, generator=gen).to(torch.bfloat16).to(dev())
+    tiles = torch.randn(524288, generator=gen).to(torch.bfloat16).to(dev())
+    sink = torch.full((cus * 512,), float("nan"), device=dev())
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev())
+    iters = 200
+    for level in range(6):
+        print(f"ladder level {level}", flush=True)
+        ra.fwd_ladder_probe(level, ops, tiles, sink, clocks, cus, 20, 0.1275)  # warm-up
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        ra.fwd_ladder_probe(level, ops, tiles, sink, clocks, cus, iters, 0.1275)
+        t1.record()
+        torch.cuda.synchronize()
+        rate = cus * 8 * iters * 4194304 / (t0.elapsed_time(t1) * 1e-3)
+        print(f"  {rate / 1e12:.0f} TFLOP/s of a derived {peak / 1e12:.0f}", flush=True)
+        assert torch.isfinite(sink).all() and clocks[0].item() > 0 and clocks[1].item() > 0
+        assert 0 < rate <= 1.02 * peak
