@@ -539,6 +539,11 @@ LADDER_LEVELS = {
     3: "+ online softmax of the previous tile in the MFMA slots (scale, exp2, row sum, bf16 pack)",
     4: "+ one workgroup barrier per 64-key tile",
     5: "+ direct-to-LDS tile loads two tiles ahead, waited for before the barrier",
+    6: "level 2 with one wave per SIMD holding 64 rows (each LDS operand read feeds two MFMAs)",
+    7: "level 5 with one wave per SIMD holding 64 rows",
+    8: "level 6 + the softmax only",
+    9: "level 8 + one barrier per tile",
+    10: "level 7 with the barrier every second tile",
 }
 
 

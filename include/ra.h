@@ -427,10 +427,15 @@ int ra_trace_end(void);
  * tile's scores in the MFMA slots (scores times c, exp2, row sum, bf16
  * pack into the next P V operand); 4: a workgroup barrier per tile; 5: the
  * tile loads (direct-to-LDS buffer loads two tiles ahead, waited for before
- * the barrier).  operands: device, >= 20480 bytes of bf16 data for the
- * register operands; tiles: device, >= 1 MiB of bf16 data for the LDS
+ * the barrier).  Levels 6-10 take the other layout, one wave per SIMD
+ * (4 waves per block) holding 64 query rows so that each LDS operand read
+ * feeds two MFMAs (output accumulators in AGPRs, scores in VGPRs, P
+ * double-buffered): 6: operand reads only (as level 2); 7: everything (as
+ * level 5); 8: the softmax only; 9: softmax and barrier; 10: as 7 with the
+ * barrier every second tile.  operands: device, >= 20480 bytes of bf16
+ * data for the register operands; tiles: device, >= 1 MiB of bf16 data for the LDS
  * tiles and the tile loads.  sink: blocks * 512 floats; clocks: 2 values,
- * as for ra_mfma_probe.  RA_ERR_NULL, RA_ERR_SHAPE (level outside [0, 5],
+ * as for ra_mfma_probe.  RA_ERR_NULL, RA_ERR_SHAPE (level outside [0, 10],
  * blocks or iters < 1), RA_ERR_HIP.
  */
 int ra_fwd_ladder_probe(int level, const void* operands, const void* tiles, float* sink,

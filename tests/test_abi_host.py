@@ -276,7 +276,7 @@ def test_probe_helpers_validation(L):
     L.ra_fwd_ladder_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
     assert L.ra_fwd_ladder_probe(0, None, vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 0.1, None) == RA_ERR_NULL
-    assert L.ra_fwd_ladder_probe(6, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 0.1, None) == RA_ERR_SHAPE
+    assert L.ra_fwd_ladder_probe(11, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 0.1, None) == RA_ERR_SHAPE
     assert L.ra_fwd_ladder_probe(-1, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 0.1, None) == RA_ERR_SHAPE
     assert L.ra_fwd_ladder_probe(2, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 0, 1, 0.1, None) == RA_ERR_SHAPE
 

@@ -679,7 +679,7 @@ def test_fwd_ladder_probe_runs_within_the_derived_peak():
     sink = torch.full((cus * 512,), float("nan"), device=dev())
     clocks = torch.zeros(2, dtype=torch.int64, device=dev())
     iters = 200
-    for level in range(6):
+    for level in range(11):
         print(f"ladder level {level}", flush=True)
         ra.fwd_ladder_probe(level, ops, tiles, sink, clocks, cus, 20, 0.1275)  # warm-up
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
