@@ -215,6 +215,26 @@ def test_local_share_closed_forms_every_row(wid, share_inputs):
     assert torch.isfinite(lse).all()
 
 
+@pytest.mark.timeout(600)
+def test_local_share_walk_bit_repeatable(share_inputs):
+    """The 128K/CP=4 walk at full size, run twice in each staging mode: the
+    copy stream's event-ordered copies and the in-kernel staging must give
+    bit-identical O and lse from run to run (the kernels are deterministic,
+    and every staged chunk is complete before a step reads it), and the two
+    stagings must agree with each other bit for bit."""
+    w = WORKLOADS[2]
+    r = w.ranks[0]
+    q, k, v, kd, vd = share_inputs(2)
+    runs = {}
+    for mode in ("double_buffer", "double_buffer_in_kernel"):
+        for rep in range(2):
+            say(f"{w.name}: {mode} run {rep}")
+            runs[(mode, rep)] = tuple(t.cpu() for t in gpu_ring_fwd(w, r, q[r], kd, vd, mode))
+    ref = runs[("double_buffer", 0)]
+    for key, (o, lse) in runs.items():
+        assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"{key} differs from the first run"
+
+
 # ---------------------------------------------------------------------------
 # Training share: forward + backward.
 # ---------------------------------------------------------------------------
@@ -295,6 +315,28 @@ def test_train_dk_dv_sampled_key_rows(train_run):
     rel = math.sqrt(sum(x[2] for x in res) / sum(x[3] for x in res))
     say(f"  max|ddK|={e_k:.2e} max|ddV|={e_v:.2e} rel={rel:.2e}")
     assert e_k <= TOL_GRAD and e_v <= TOL_GRAD and rel <= TOL_REL
+
+
+@pytest.mark.timeout(600)
+def test_train_backward_bit_repeatable(train_run):
+    """The training share's backward walk at full size, run again on the
+    same forward output: dQ, dK and dV are bit-identical (no atomics)."""
+    t = train_run
+    w, r = t["w"], t["r"]
+    kd = [x.to(dev()) for x in t["k"]]
+    vd = [x.to(dev()) for x in t["v"]]
+    o, lse = t["o"].to(dev()), t["lse"].to(dev())
+    dq = torch.full_like(o, float("nan"))
+    dk = [torch.zeros(w.B, w.H, w.C, w.d, device=dev()) for _ in range(w.P)]
+    dv = [torch.zeros(w.B, w.H, w.C, w.d, device=dev()) for _ in range(w.P)]
+    say(f"{w.name}: second backward walk")
+    ra.ring_bwd(t["q"].to(dev()), kd, vd, o, lse, t["do"].to(dev()), dq, dk, dv, r, w.causal, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dq.cpu(), t["dq"])
+    for j in range(w.P):
+        assert torch.equal(dk[j].cpu(), t["dk"][j]) and torch.equal(dv[j].cpu(), t["dv"][j]), f"chunk {j}"
+    del kd, vd, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
 
 
 def test_train_gradient_sums_every_key(train_run):
