@@ -224,16 +224,16 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
   // Keys at or past `lim` are masked for this lane's query.
   const int lim = DIAG ? min(Sk, qq + 1 + qoff) : Sk;
 
-  // Iteration t reads K(t+1) and V(t-1) (and, in its last slots, the first
-  // operands of V(t)); step t loads V(t+2) and K(t+3), one 1 KB piece per
-  // MFMA slot in DMA_SLOT, V pieces first.  A step ends waiting for the
-  // loads of the steps before it: every tile then has a full step more to
-  // land than the barrier that precedes its first read needs.
+  // Iteration t reads K(t+1) and V(t-1); step t loads V(t+1) and K(t+3),
+  // one 1 KB piece per MFMA slot in DMA_SLOT, V pieces first.  A step ends
+  // waiting for all but its K pieces, which have one more step to land.
+  // (Loading V a step earlier as well measured the same time and 16 % more
+  // HBM traffic: the blocks of a head drift further apart in their L2 use.)
   using Dma = TileBufDma<D, NW, BC>;
   constexpr int NPIECE = Dma::kPerWave;  // pieces per tile per wave
   Dma dma;
   dma.init(wave, lane);
-  [[maybe_unused]] WalkPos vpos{}, kpos{};  // walk: tiles tt + 2 (V) and tt + 3 (K) of step tt
+  [[maybe_unused]] WalkPos vpos{}, kpos{};  // walk: tiles tt + 1 (V) and tt + 3 (K) of step tt
   if constexpr (WALK) {
 #pragma unroll
     for (int j = 0; j < 3; ++j)
@@ -241,18 +241,16 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
         const WalkPos p = walk_pos(kchunk, j);
         dma.load(kbuf(j), p.base, p.l * BC, p.n);
       }
-    const WalkPos v0 = walk_pos(vchunk, 0), v1 = walk_pos(vchunk, 1);
+    const WalkPos v0 = walk_pos(vchunk, 0);
     dma.load(vbuf(0), v0.base, 0, v0.n);
-    dma.load(vbuf(1), v1.base, v1.l * BC, v1.n);
     dma.load(vbuf(NB - 1), v0.base, 0, v0.n);  // finite data for the P = 0 product of iteration 0
-    vpos = walk_pos(vchunk, 2);
+    vpos = walk_pos(vchunk, 1);
     kpos = walk_pos(kchunk, 3);
   } else {
 #pragma unroll
     for (int j = 0; j < 3; ++j)
       if (j < ntiles) dma.load(kbuf(j), kp, j * BC, Sk);
     dma.load(vbuf(0), vp, 0, Sk);
-    dma.load(vbuf(1), vp, BC, Sk);
     dma.load(vbuf(NB - 1), vp, 0, Sk);  // finite data for the P = 0 product of iteration 0
   }
 
@@ -399,17 +397,16 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
     mref = mb;
   };
 
-  // Piece k of step tt's loads: V(tt+2) replaces V(tt-2), last read by the
-  // P V products of iteration tt - 1, and K(tt+3) replaces K(tt-1), last
-  // read in iteration tt - 2.  Loads past the last tile read zeros and are
-  // never used.
+  // Piece k of step tt's loads: V(tt+1) replaces V(tt-3) and K(tt+3)
+  // replaces K(tt-1), both last read in iteration tt - 2 or earlier.  Loads
+  // past the last tile read zeros and are never used.
   auto dma_piece = [&](int tt, auto ic, int k) __attribute__((always_inline)) {
     constexpr int I = decltype(ic)::value;
     if constexpr (WALK) {
-      if (k < NPIECE) dma.load_piece(k, vbuf((I + 2) % NB), vpos.base, vpos.l * BC, vpos.n);
+      if (k < NPIECE) dma.load_piece(k, vbuf((I + 1) % NB), vpos.base, vpos.l * BC, vpos.n);
       else dma.load_piece(k - NPIECE, kbuf((I + 3) % NB), kpos.base, kpos.l * BC, kpos.n);
     } else {
-      if (k < NPIECE) dma.load_piece(k, vbuf((I + 2) % NB), vp, (tt + 2) * BC, Sk);
+      if (k < NPIECE) dma.load_piece(k, vbuf((I + 1) % NB), vp, (tt + 1) * BC, Sk);
       else dma.load_piece(k - NPIECE, kbuf((I + 3) % NB), kp, (tt + 3) * BC, Sk);
     }
   };
@@ -487,7 +484,7 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
       walk_next(vchunk, vpos);
       walk_next(kchunk, kpos);
     }
-    wait_vmem_but<2 * NPIECE>();
+    wait_vmem_but<NPIECE>();
     phase_barrier();
   };
 
