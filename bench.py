@@ -581,10 +581,17 @@ def fwd_ladder(iters=20000):
             ms = t0.elapsed_time(t1)
             cyc, ref = clocks.tolist()
             tf = flops / (ms * 1e-3) / 1e12
+            ghz = cyc / (ref / 100e6) / 1e9 if ref > 0 else None
             row[name] = {"tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "clock_ghz": round(cyc / (ref / 100e6) / 1e9, 3) if ref > 0 else None,
-                         # Cycles per 32-MFMA tile per SIMD pair (the floor is 2 x 32 x 32 = 2048).
-                         "cycles_per_tile": round(cyc / (iters * 4), 1)}
+                         "clock_ghz": round(ghz, 3) if ghz else None,
+                         # Cycles per tile on one SIMD (two waves' 32 MFMAs, or one
+                         # wave's 64: the floor is 64 x 32 = 2048), from the launch
+                         # time and the clock.
+                         "cycles_per_tile": round(ghz * 1e9 * ms * 1e-3 / (iters * 4), 1) if ghz else None,
+                         # The same from wave 0 of block 0's own loop: without a
+                         # barrier (levels 0-3) that wave can run ahead of its SIMD
+                         # partner, and then reads less than the SIMD's figure.
+                         "wave0_cycles_per_tile": round(cyc / (iters * 4), 1)}
         out[f"level{level}"] = row
     return out
 
