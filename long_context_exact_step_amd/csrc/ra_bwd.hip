@@ -568,15 +568,20 @@ __global__ __launch_bounds__(64 * kKvfWaves) void bwd_kvf_kernel(
   // product with the previous tile is used.  The phase of tile tt also issues
   // tile tt + 2's loads, one piece every EVERY MFMAs; a wave without that
   // phase issues them all at once.  Tiles past the last one load zeros (or
-  // clamped rows) that nothing reads.
+  // clamped rows) that nothing reads.  The phase runs at a raised wave
+  // priority: the other wave of the SIMD is in its vector phase meanwhile
+  // (for waves 4..7, the exp2-heavy one of waves 0..3), and the matrix core's
+  // next instruction then issues first.
   auto mfma_tile = [&](int tt) __attribute__((always_inline)) {
     constexpr int EVERY = NOP / NPC;
     if (tt >= ws && tt <= ntq) {
+      __builtin_amdgcn_s_setprio(1);
       mfma_phase((uint32_t)(((tt + 3) & 3) * TILE), (uint32_t)((tt & 3) * TILE),
                  [&](auto mc) __attribute__((always_inline)) {
                    constexpr int m = decltype(mc)::value;
                    if constexpr (m % EVERY == EVERY / 2 && m / EVERY < NPC) load_piece(tt + 2, m / EVERY);
                  });
+      __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
       for (int k = 0; k < NPC; ++k) load_piece(tt + 2, k);
