@@ -160,8 +160,31 @@ def pairs_of_kind(kind, w):
     return 0
 
 
-def timed_steps(step_fn, n_launch_per_step, steps, warmup):
-    """Runs warmup, then exactly `steps` timed steps with per-launch tracing.
+class StepClock:
+    """Events on the current stream at every step boundary of the timed loop
+    (recorded between steps, with no synchronisation): the per-step times
+    whose median the bench lines report beside the mean."""
+
+    def __init__(self, steps):
+        import torch
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        self.n = 0
+
+    def mark(self):
+        self.ev[self.n].record()
+        self.n += 1
+
+    def median_ms(self):
+        d = sorted(self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(self.n - 1))
+        if not d:
+            return None
+        m = len(d) // 2
+        return d[m] if len(d) % 2 else 0.5 * (d[m - 1] + d[m])
+
+
+def timed_steps(step_fn, n_launch_per_step, steps, warmup, clock=None):
+    """Runs warmup, then exactly `steps` timed steps with per-launch tracing
+    (and step-boundary events into `clock`, if given).
     Returns (seconds, [(kind, ms), ...])."""
     import torch
     import long_context_exact_step_amd as ra
@@ -175,8 +198,12 @@ def timed_steps(step_fn, n_launch_per_step, steps, warmup):
     keep = ra.trace_begin(ev.start, ev.end, kinds)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if clock:
+        clock.mark()
     for _ in range(steps):
         step_fn()
+        if clock:
+            clock.mark()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     n = ra.trace_end()
@@ -206,18 +233,23 @@ def walk_stats(rec, flops, steps):
                          "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}}
 
 
-def untraced_steps(step_fn, steps, warmup):
+def untraced_steps(step_fn, steps, warmup, clock=None):
     """Runs warmup, then exactly `steps` timed steps with no per-launch
     events (for walks of many short launches, where bracketing every launch
-    adds a gap of its own).  Returns seconds."""
+    adds a gap of its own); step-boundary events into `clock`, if given.
+    Returns seconds."""
     import torch
 
     for _ in range(warmup):
         step_fn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if clock:
+        clock.mark()
     for _ in range(steps):
         step_fn()
+        if clock:
+            clock.mark()
     torch.cuda.synchronize()
     return time.perf_counter() - t0
 
@@ -279,16 +311,17 @@ def run_fwd(w, steps, warmup, ring_mode, H_kv=None, trace=True, concurrent=False
         for st in streams:
             cur.wait_stream(st)
 
+    clock = StepClock(steps)
     if concurrent:
-        secs, rec = untraced_steps(step_concurrent, steps, warmup), []
+        secs, rec = untraced_steps(step_concurrent, steps, warmup, clock), []
         trace = False
     elif trace:
-        secs, rec = timed_steps(step, n_launch, steps, warmup)
+        secs, rec = timed_steps(step, n_launch, steps, warmup, clock)
     else:
-        secs, rec = untraced_steps(step, steps, warmup), []
+        secs, rec = untraced_steps(step, steps, warmup, clock), []
     flops = fwd_flops(w)
     res = {
-        "secs": secs, "ms_per_step": secs / steps * 1e3,
+        "secs": secs, "ms_per_step": secs / steps * 1e3, "ms_per_step_median": clock.median_ms(),
         "tflops": flops * steps / secs / 1e12,
         "tokens_per_s": B * C * len(w.ranks) * steps / secs,
         "launches_per_step": n_launch,
@@ -306,6 +339,7 @@ def config_line(w, steps, warmup, ring_mode, concurrent=False):
     peak.  Tokens are the local query tokens of every walked rank.  Timed
     without per-launch events."""
     import torch
+    from long_context_exact_step_amd.workloads import fwd_flops
     r, tensors = run_fwd(w, steps, warmup, ring_mode, trace=False, concurrent=concurrent)
     del tensors
     torch.cuda.empty_cache()
@@ -313,6 +347,8 @@ def config_line(w, steps, warmup, ring_mode, concurrent=False):
         "workload": w.name, "ring_mode": ring_mode, "ranks": list(w.ranks), "steps": steps, "warmup": warmup,
         "ranks_walked": "concurrently, one stream each" if concurrent else "one after another, one stream",
         "ms_per_step": round(r["ms_per_step"], 4), "tflops": round(r["tflops"], 2),
+        "ms_per_step_median": round(r["ms_per_step_median"], 4),
+        "tflops_at_median": round(fwd_flops(w) / (r["ms_per_step_median"] * 1e-3) / 1e12, 2),
         "tokens_per_s": round(r["tokens_per_s"], 1),
         "frac_bf16_peak": round(r["tflops"] / PEAK_BF16_TFLOPS, 4),
         "frac_derived_peak": round(r["tflops"] / DERIVED_PEAK_BF16_TFLOPS, 4),
@@ -357,7 +393,8 @@ def run_train(w, steps, warmup, H_kv=None):
                     copy_stream=copy_stream)
         ra.ring_bwd(q, ks, vs, o, lse, do, dq, dk, dv, r, w.causal, w.scale, workspace=ws_b)
 
-    secs, rec = timed_steps(step, n_launch, steps, warmup)
+    clock = StepClock(steps)
+    secs, rec = timed_steps(step, n_launch, steps, warmup, clock)
     fl_f, fl_b = fwd_flops(w), bwd_flops(w)
     kf = {"fwd_diag": 4 * d, "fwd_full": 4 * d, "bwd_dq_diag": 6 * d, "bwd_dq_full": 6 * d,
           "bwd_dkdv_diag": 8 * d, "bwd_dkdv_full": 8 * d}
@@ -366,6 +403,7 @@ def run_train(w, steps, warmup, H_kv=None):
     bwd_ms = sum(m for k, m in rec if k.startswith("bwd")) / steps
     return {
         "workload": w.name, "steps": steps, "ms_per_step": secs / steps * 1e3,
+        "ms_per_step_median": round(clock.median_ms(), 4),
         "tflops_fwd_bwd": (fl_f + fl_b) * steps / secs / 1e12,
         "tokens_per_s": B * C * steps / secs,
         "fwd_kernels_ms_per_step": round(fwd_ms, 3), "bwd_kernels_ms_per_step": round(bwd_ms, 3),
@@ -651,11 +689,14 @@ def cpu_baseline(w, tensors, budget_s):
     rows_done = 0
     heads = 0
     err_o = err_l = 0.0
+    conv_secs = 0.0
     for h in range(w.H):
         rows = inputs.query_row_sample(w.id, h, C)
+        tc = time.perf_counter()
         kh = np.concatenate([f64(ks[j][:, h:h + 1]) for j in range(P)], axis=2)
         vh = np.concatenate([f64(vs[j][:, h:h + 1]) for j in range(P)], axis=2)
         qh = f64(q_cpu[:, h:h + 1, rows])
+        conv_secs += time.perf_counter() - tc
         pos = r * C + rows
         t0 = time.perf_counter()
         ro, rl = oracle.attention_fwd(qh, kh, vh, w.scale, w.causal, q_pos=pos)
@@ -679,7 +720,7 @@ def cpu_baseline(w, tensors, budget_s):
     # bias.  Extrapolated, not measured.
     extrap = {"label": "extrapolated",
               "method": "sample seconds x (visible pairs of the full forward / visible pairs of the sample)"}
-    for wid in (w.id, 5):
+    for wid in sorted(WORKLOADS):
         x = WORKLOADS[wid]
         extrap[f"{x.name} full forward"] = {"tflop_fp64": round(fwd_flops(x) / 1e12, 3),
                                            "seconds": round(fwd_flops(x) / rate, 1)}
@@ -689,6 +730,9 @@ def cpu_baseline(w, tensors, budget_s):
                   f"{'visible' if w.causal else 'whole'} key range of the unchunked sequence; fp64 NumPy",
         "blas": ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in blas})) or None,
         "seconds": round(secs, 2),
+        # Outside `seconds`: copying the sampled heads' bf16 inputs from the
+        # GPU and widening them to fp64.
+        "conversion_seconds": round(conv_secs, 2),
         # A token is one query position over all heads: the sample's rows
         # divided by the head count, per second.
         "tokens_per_s": round(rows_done / w.H / secs, 3),
@@ -768,6 +812,10 @@ def main():
     out = {
         "metric": METRIC, "value": round(fwd["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(fwd["ms_per_step"], 4),
+        # Median over the timed steps (step-boundary events on the compute
+        # stream) beside the mean that `value` is computed from.
+        "ms_per_step_median": round(fwd["ms_per_step_median"], 4),
+        "tflops_at_median": round(fwd_flops(w) / (fwd["ms_per_step_median"] * 1e-3) / 1e12, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "C": w.C, "P": w.P, "rank": list(w.ranks), "d": w.d,
