@@ -482,9 +482,11 @@ def mfma_probe(operands, sink, clocks, blocks, iters, stream=None):
 
 def fwd_ladder_probe(level, operands, tiles, sink, clocks, blocks, iters, c, stream=None):
     """ra_fwd_ladder_probe: the forward kernel's instruction stream rebuilt
-    on synthetic data up to `level` (0..5).  operands: >= 10240 bf16 values;
+    on synthetic data up to `level` (0..5: two waves per SIMD, 32 rows each;
+    6..10: one wave per SIMD with 64 rows).  operands: >= 10240 bf16 values;
     tiles: >= 524288 bf16 values; sink: float32, >= blocks * 512; clocks:
-    int64, >= 2.  4194304 * iters flop per wave, 8 waves per block."""
+    int64, >= 2.  The same matrix work at every level: 4194304 * iters flop
+    per 32 query rows (8 such row groups per block)."""
     import torch
     if operands.dtype != torch.bfloat16 or operands.numel() * 2 < 20480:
         raise ValueError("operands: expected >= 10240 bf16 values")
