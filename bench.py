@@ -31,6 +31,7 @@ fp64 CPU oracle timed on a bounded sample of the same workload.
 
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import math
@@ -714,7 +715,7 @@ def cpu_baseline(w, tensors, budget_s):
     threads = max((i.get("num_threads", 1) for i in blas), default=1)
     flops = 4 * d * pairs
     rate = flops / secs  # fp64 flop/s of the oracle on this sample
-    from long_context_exact_step_amd.workloads import WORKLOADS, fwd_flops
+    from long_context_exact_step_amd.workloads import WORKLOADS, Workload, fwd_flops
     # Whole-config times at the sample's rate: the sampled rows are uniform
     # over each head's rows, so the visible-pair ratio scales them without
     # bias.  Extrapolated, not measured.
@@ -770,7 +771,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from long_context_exact_step_amd.workloads import WORKLOADS, fwd_flops
+    from long_context_exact_step_amd.workloads import WORKLOADS, Workload, fwd_flops
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -855,8 +856,12 @@ def main():
         # 32K full ring over all ranks, the 1M share; the full ring in both the
         # double-buffer walk (the ring's emulation) and the fused walk.
         cfgs = {}
+        # The 128K share at head size 64 (H = 64: the same flops and bytes).
+        d64 = dataclasses.replace(WORKLOADS[2], H=64, d=64,
+                                  name="128K/CP=4 local share, rank 3, H=64, d=64, causal fwd")
         for key, wid, mode, st, conc in (
                 ("tiny_ring", 1, "double_buffer", args.steps, False),
+                ("share_128k_cp4_d64", d64, "double_buffer", args.steps, False),
                 ("share_128k_cp4_double_buffer_in_kernel", 2, "double_buffer_in_kernel", args.steps, False),
                 ("full_ring_32k_double_buffer", 3, "double_buffer", args.steps, False),
                 ("full_ring_32k_double_buffer_in_kernel", 3, "double_buffer_in_kernel", args.steps, False),
@@ -865,9 +870,10 @@ def main():
                 ("full_ring_32k_resident", 3, "resident", args.steps, False),
                 ("full_ring_32k_fused", 3, "fused", args.steps, False),
                 ("share_1m_cp8", 4, "double_buffer", 5, False)):
-            if wid == w.id and mode == args.ring_mode and not conc:
+            wl = wid if isinstance(wid, Workload) else WORKLOADS[wid]
+            if wl == w and mode == args.ring_mode and not conc:
                 continue
-            c = config_line(WORKLOADS[wid], st, min(2, args.warmup), mode, concurrent=conc)
+            c = config_line(wl, st, min(2, args.warmup), mode, concurrent=conc)
             cfgs[key] = c
             print(f"[bench] {key}: {c['ms_per_step']:.3f} ms/step, {c['tflops']:.1f} TFLOP/s "
                   f"({c['frac_bf16_peak']:.3f} of peak), {c['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
@@ -877,6 +883,13 @@ def main():
         out["train"] = tr
         print(f"[bench] train: {tr['ms_per_step']:.3f} ms/step, {tr['tflops_fwd_bwd']:.1f} TFLOP/s", file=sys.stderr,
               flush=True)
+        # The training share at head size 64 (H = 64).
+        w64 = dataclasses.replace(WORKLOADS[5], H=64, d=64,
+                                  name="training share C=16K, P=4, rank 3, H=64, d=64, causal fwd+bwd")
+        t64 = run_train(w64, max(3, args.steps // 2), max(1, args.warmup))
+        out["train_d64"] = t64
+        print(f"[bench] train d=64: {t64['ms_per_step']:.3f} ms/step, {t64['tflops_fwd_bwd']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
     if not args.no_gqa and w.H % 4 == 0:
         # Grouped-query attention, 4 query heads per key/value head: the same
         # attention flops, a quarter of the key/value bytes each ring step moves.
