@@ -24,11 +24,14 @@ stream).
   heads); the training share's forward and dQ on sampled rows, dK/dV on
   sampled key rows of every head over the gathered sequence, and the
   gradient sums.
+* Head size 64: the 128K/CP=4 share and the training share again at H = 64,
+  d = 64 (the same flops and bytes), with the same checks.
 
 The oracle runs on the host, fanned out over heads with one BLAS thread per
 task.
 """
 
+import dataclasses
 import math
 from concurrent.futures import ThreadPoolExecutor
 
@@ -44,6 +47,20 @@ from long_context_exact_step_amd.workloads import WORKLOADS
 from parity import TOL_GRAD, TOL_LSE, TOL_O, TOL_REL, assert_close, dev, f64, workers
 
 pytestmark = pytest.mark.gpu
+
+# The full-size shares checked below, by key: the workloads themselves and
+# their head-size-64 variants (H = 64, d = 64).
+SHARES = {
+    2: WORKLOADS[2],
+    4: WORKLOADS[4],
+    "2_d64": dataclasses.replace(WORKLOADS[2], H=64, d=64,
+                                 name="128K/CP=4 local share, rank 3, H=64, d=64, causal fwd"),
+}
+TRAINS = {
+    5: WORKLOADS[5],
+    "5_d64": dataclasses.replace(WORKLOADS[5], H=64, d=64,
+                                 name="training share C=16K, P=4, rank 3, H=64, d=64, causal fwd+bwd"),
+}
 
 
 def say(msg):
@@ -159,7 +176,7 @@ def share_inputs():
     def get(wid):
         if wid not in cache:
             cache.clear()
-            w = WORKLOADS[wid]
+            w = SHARES[wid]
             say(f"generating inputs of {w.name}")
             q, k, v, _ = gen_workload(w)
             cache[wid] = (q, k, v, [t.to(dev()) for t in k], [t.to(dev()) for t in v])
@@ -171,9 +188,9 @@ def share_inputs():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("wid", [2, 4])
+@pytest.mark.parametrize("wid", [2, 4, "2_d64"])
 def test_local_share_sampled_rows(wid, share_inputs):
-    w = WORKLOADS[wid]
+    w = SHARES[wid]
     r = w.ranks[0]
     q, k, v, kd, vd = share_inputs(wid)
     say(f"{w.name}: GPU walk (copy stream, and in-kernel staging)")
@@ -184,9 +201,9 @@ def test_local_share_sampled_rows(wid, share_inputs):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("wid", [2, 4])
+@pytest.mark.parametrize("wid", [2, 4, "2_d64"])
 def test_local_share_closed_forms_every_row(wid, share_inputs):
-    w = WORKLOADS[wid]
+    w = SHARES[wid]
     r = w.ranks[0]
     q, k, v, kd, vd = share_inputs(wid)
     pos = r * w.C + np.arange(w.C)
@@ -239,9 +256,9 @@ def test_local_share_walk_bit_repeatable(share_inputs):
 # Training share: forward + backward.
 # ---------------------------------------------------------------------------
 
-@pytest.fixture(scope="module")
-def train_run():
-    w = WORKLOADS[5]
+@pytest.fixture(scope="module", params=list(TRAINS))
+def train_run(request):
+    w = TRAINS[request.param]
     r = w.ranks[0]
     say(f"{w.name}: inputs")
     q, k, v, do = gen_workload(w, with_do=True)
