@@ -156,13 +156,41 @@ def test_full_ring_all_rows():
     kd = [t.to(dev()) for t in k]
     vd = [t.to(dev()) for t in v]
     for r in w.ranks:
-        say(f"full ring rank {r}: GPU walk (double buffer with a copy stream, with in-kernel staging, and "
-            f"fused), then oracle on all {w.C} rows x {w.H} heads")
+        say(f"full ring rank {r}: GPU walk (double buffer with a copy stream, with in-kernel staging, "
+            f"resident, and fused), then oracle on all {w.C} rows x {w.H} heads")
         o, lse = gpu_ring_fwd(w, r, q[r], kd, vd)
         io, il = gpu_ring_fwd(w, r, q[r], kd, vd, "double_buffer_in_kernel")
+        ro, rl = gpu_ring_fwd(w, r, q[r], kd, vd, "resident")
         fo, fl = gpu_ring_fwd(w, r, q[r], kd, vd, "fused")
         check_rows(w, r, q[r], k, v, o, lse, lambda h: np.arange(w.C), f"full ring rank {r}",
-                   more=[(io, il, f"full ring rank {r} in-kernel staging"), (fo, fl, f"full ring rank {r} fused")])
+                   more=[(io, il, f"full ring rank {r} in-kernel staging"), (ro, rl, f"full ring rank {r} resident"),
+                         (fo, fl, f"full ring rank {r} fused")])
+
+
+@pytest.mark.timeout(600)
+def test_full_ring_ranks_concurrent_bit_identical():
+    """Every rank of the 32K full ring walked at once, each on a stream and
+    with staging slots of its own (in-kernel staging, as the ranks of a real
+    ring run): bit-identical to the same walks run one after another."""
+    w = WORKLOADS[3]
+    q, _, _, _ = gen_workload(w)
+    k = [inputs.chunk(w.id, inputs.K, j, w.B, w.H, w.C, w.d).to(dev()) for j in range(w.P)]
+    v = [inputs.chunk(w.id, inputs.V, j, w.B, w.H, w.C, w.d).to(dev()) for j in range(w.P)]
+    qd = {r: q[r].to(dev()) for r in w.ranks}
+    seq = {r: gpu_ring_fwd(w, r, qd[r], k, v, "double_buffer_in_kernel") for r in w.ranks}
+    need = ra.workspace_bytes(w.P, w.B, w.H, w.C, w.d, "double_buffer")
+    wss = {r: torch.empty(need, dtype=torch.uint8, device=dev()) for r in w.ranks}
+    streams = {r: torch.cuda.Stream(dev()) for r in w.ranks}
+    out = {r: (torch.full((w.B, w.H, w.C, w.d), float("nan"), device=dev()),
+               torch.full((w.B, w.H, w.C), float("nan"), device=dev())) for r in w.ranks}
+    torch.cuda.synchronize()
+    say(f"full ring: {len(w.ranks)} ranks walked concurrently")
+    for r in w.ranks:
+        ra.ring_fwd(qd[r], k, v, out[r][0], out[r][1], r, w.causal, w.scale, ring_mode="double_buffer",
+                    workspace=wss[r], stream=streams[r], copy_stream=None)
+    torch.cuda.synchronize()
+    for r in w.ranks:
+        assert torch.equal(out[r][0], seq[r][0]) and torch.equal(out[r][1], seq[r][1]), f"rank {r}"
 
 
 # ---------------------------------------------------------------------------
