@@ -28,7 +28,6 @@
 namespace ra {
 namespace {
 
-constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 
 // One ds_write_b128 of v at LDS byte address addr + OFF, as inline assembly
@@ -379,6 +378,8 @@ __global__ __launch_bounds__(64 * kKvfWaves) void bwd_kvf_kernel(
     const int row = min(j * BQ + lane, Sq - 1);
     if (wave == 0) __builtin_amdgcn_global_load_lds(lp + row, (lds_void*)(smem + LOFF + (j & 3) * BQ * 4), 4, 0, 0);
     if (wave == 1) __builtin_amdgcn_global_load_lds(Dp + row, (lds_void*)(smem + DLOFF + (j & 3) * BQ * 4), 4, 0, 0);
+#else
+    (void)j, (void)lp, (void)Dp;
 #endif
   };
   auto load_tile = [&](int j) __attribute__((always_inline)) {

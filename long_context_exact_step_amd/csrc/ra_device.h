@@ -165,6 +165,8 @@ struct TileBufDma {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(mat) + (size_t)t0 * D, 0, rows * (D * 2), kBufWord3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + (piece0 + i) * 1024), 16, off[i], 0, 0, 0);
+#else
+    (void)i, (void)tile, (void)mat, (void)t0, (void)n;
 #endif
   }
 

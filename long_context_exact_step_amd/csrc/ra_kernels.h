@@ -42,7 +42,7 @@ struct FwdStepArgs {
   bool diag;   // causal mask: query t sees keys <= t + qoff
   bool merge;  // fold into the running (o, lse) instead of overwriting
   int group;   // query heads per key/value head (>= 1, divides BH)
-  int qoff;    // causal offset of the query rows against the keys (>= 0; 0 on the ring's diagonal chunk)
+  int qoff = 0;  // causal offset of the query rows against the keys (>= 0; 0 on the ring's diagonal chunk)
   // Non-null: the keys are walk->n resident chunks (k, v unused; Sk =
   // n * C; merge must be false).
   const ChunkTable* walk = nullptr;
@@ -77,7 +77,7 @@ struct BwdStepArgs {
   float scale;
   bool diag;  // causal mask: query t sees keys <= t + qoff
   int group;  // query heads per key/value head (>= 1, divides BH)
-  int qoff;   // causal offset of the query rows against the keys (>= 0)
+  int qoff = 0;  // causal offset of the query rows against the keys (>= 0)
 };
 hipError_t launch_bwd_dq(const BwdStepArgs& a, hipStream_t stream);    // dq += ...
 hipError_t launch_bwd_dkdv(const BwdStepArgs& a, hipStream_t stream);  // dk, dv += ...
