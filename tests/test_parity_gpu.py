@@ -524,6 +524,53 @@ def test_ring_bwd_gqa_matches_oracle(P, C, d, H, Hk):
             assert_close(f64(dv[j]), rv[:, :, sl], TOL_GRAD, f"dv chunk {j}")
 
 
+
+@pytest.mark.parametrize("P,C,d,H,Hk,causal", [(3, 130, 128, 4, 4, True), (3, 130, 128, 4, 2, True),
+                                               (2, 192, 64, 4, 1, False)])
+def test_ring_batch_of_two_every_rank(P, C, d, H, Hk, causal):
+    """B = 2: the batch index enters every kernel's row and chunk offsets
+    (queries, running output, lse, D, dq, and each key chunk of H_kv heads).
+    Ragged chunks (130) and whole tiles (192, where the fused walk runs rather
+    than falling back to the per-step walk).  Every forward walk (resident, double-buffered with a copy stream and with
+    in-kernel staging, fused) and the backward walk, every rank, against the
+    oracle."""
+    B = 2
+    q, k, v, do = ring_tensors(118, B, H, P, C, d, with_do=True, H_kv=Hk)
+    kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    scale = 1 / math.sqrt(d)
+    copy_stream = torch.cuda.Stream()
+    modes = [("resident", None), ("double_buffer", copy_stream), ("double_buffer", None), ("fused", None)]
+    for rank in range(P):
+        pos = rank * C + np.arange(C)
+        qd, dod = q[rank].to(dev()), do[rank].to(dev())
+        ro, rl = oracle.attention_fwd(f64(q[rank]), kf, vf, scale, causal, q_pos=pos)
+        for mode, cs in modes:
+            print(f"ring B=2 P={P} C={C} d={d} H={H} Hk={Hk} causal={causal} rank={rank} "
+                  f"fwd {mode} copy_stream={cs is not None}", flush=True)
+            o = torch.full((B, H, C, d), float("nan"), device=dev())
+            lse = torch.full((B, H, C), float("nan"), device=dev())
+            ra.ring_fwd(qd, kd, vd, o, lse, rank, causal, scale, ring_mode=mode, copy_stream=cs)
+            torch.cuda.synchronize()
+            assert_close(f64(o), ro, TOL_O, f"o {mode}")
+            assert_close(f64(lse), rl, TOL_LSE, f"lse {mode}", rel=None)
+        print(f"ring B=2 P={P} C={C} d={d} H={H} Hk={Hk} causal={causal} rank={rank} bwd", flush=True)
+        dq = torch.full((B, H, C, d), float("nan"), device=dev())
+        dk = [torch.zeros(B, Hk, C, d, device=dev()) for _ in range(P)]
+        dv = [torch.zeros(B, Hk, C, d, device=dev()) for _ in range(P)]
+        ra.ring_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, rank, causal, scale)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.attention_bwd(f64(q[rank]), kf, vf, f64(do[rank]), scale, causal, q_pos=pos)
+        assert_close(f64(dq), rq, TOL_GRAD, "dq")
+        for j in range(P):
+            if causal and j > rank:
+                assert not dk[j].any() and not dv[j].any(), "skipped chunk was touched"
+                continue
+            sl = slice(j * C, (j + 1) * C)
+            assert_close(f64(dk[j]), rk[:, :, sl], TOL_GRAD, f"dk chunk {j}")
+            assert_close(f64(dv[j]), rv[:, :, sl], TOL_GRAD, f"dv chunk {j}")
+
 # ---------------------------------------------------------------------------
 # Head-partitioned (Ulysses) share: regroup by head, full-sequence attention.
 # ---------------------------------------------------------------------------
