@@ -131,9 +131,9 @@ int ra_lse_merge(float* o, float* lse, const float* o_partial,
 /*
  * Device workspace bytes ra_ring_fwd (bwd == 0) or ra_ring_bwd (bwd != 0)
  * needs for these sizes.  Double-buffer forward: two slots of one K and one
- * V chunk, 4 * B*H*C*d * 2 bytes.  Resident forward: 0.  Backward: two fp32
- * values per row, rowsum(dO * O) and lse * log2(e), 2 * B*H*C * 4 bytes.
- * Returns 0 for invalid sizes.
+ * V chunk, 4 * B*H*C*d * 2 bytes, then 1024 bytes of work-queue counters.
+ * Resident forward: 0.  Backward: two fp32 values per row, rowsum(dO * O)
+ * and lse * log2(e), 2 * B*H*C * 4 bytes.  Returns 0 for invalid sizes.
  */
 size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d,
                                int ring_mode, int bwd);
@@ -160,7 +160,12 @@ size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d,
  * kernel of step s-1 makes the copy itself: each of its blocks copies a
  * share of the chunk once its own tiles are done, so the walk is one
  * stream of kernels with no copies or events elsewhere (cheaper per step
- * for short chunks).
+ * for short chunks).  The workspace also holds the work-queue counters of
+ * the full-chunk steps: with more (head, query tile) units than compute
+ * units, such a step runs one persistent block per compute unit, taking
+ * units from its XCD's queue first and then from the other XCDs', so that
+ * a slower XCD does not set the step's length.  Results are the same bits
+ * as with one block per unit.
  * RA_RING_RESIDENT reads the chunks in place and needs no workspace.
  * When the call returns, all work is ordered on `stream` (copy_stream work
  * is joined back into it).
@@ -209,7 +214,7 @@ int ra_ring_bwd(const void* q, const void* const* k_chunks,
  *   - dk_chunks[j], dv_chunks[j] are [B,H_kv,C,d] fp32 accumulators; each
  *     key/value head's gradient sums over the query heads of its group.
  *   - The double-buffer workspace holds H_kv-head chunks:
- *     4 * B*H_kv*C*d * 2 bytes.  The backward workspace is unchanged
+ *     4 * B*H_kv*C*d * 2 + 1024 bytes.  The backward workspace is unchanged
  *     (2 * B*H*C * 4 bytes).
  *   - H_kv < 1, or H not a multiple of H_kv, is RA_ERR_SHAPE (and 0 bytes
  *     from ra_ring_workspace_bytes_gqa).  Every other contract (ownership,

@@ -285,7 +285,8 @@ size_t ra_ring_workspace_bytes_gqa(int P, int B, int H, int H_kv, int C, int d, 
   if (P < 1 || B < 1 || H < 1 || H_kv < 1 || H % H_kv || C < 1 || (d != 64 && d != 128)) return 0;
   const size_t kv_elems = (size_t)B * H_kv * C * d;
   if (bwd) return 2 * (size_t)B * H * C * sizeof(float);  // D and lse2 per query row
-  if (ring_mode == RA_RING_DOUBLE_BUFFER) return 4 * kv_elems * 2;  // 2 slots x (K, V) bf16
+  // 2 slots x (K, V) bf16, then two blocks of unit-queue counters.
+  if (ring_mode == RA_RING_DOUBLE_BUFFER) return 4 * kv_elems * 2 + 2 * ra::kFwdQueueBytes;
   return 0;
 }
 
@@ -360,10 +361,19 @@ int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks, const void* cons
 
   // Double buffer: step 0 reads the local chunk in place; the chunk of
   // visible step i >= 1 is staged into slot (i-1) & 1 while step i-1 runs.
+  // Steps i >= 1 (full chunks) run persistent blocks on the unit queue in
+  // counter block i & 1, which step i-1 zeroed (step 0, static, zeroes
+  // block 1), so the counters need no launch of their own.
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   auto slot_k = [&](int slot) { return ws + (size_t)slot * 2 * chunk_bytes; };
   auto slot_v = [&](int slot) { return ws + (size_t)slot * 2 * chunk_bytes + chunk_bytes; };
+  int* queues = reinterpret_cast<int*>(ws + 4 * chunk_bytes);
   const int n = (int)steps.size();
+  auto with_queues = [&](ra::FwdStepArgs a, int i) {
+    if (i > 0) a.queue = queues + (i & 1) * ra::kFwdQueueInts;
+    if (i + 1 < n) a.queue_next = queues + ((i + 1) & 1) * ra::kFwdQueueInts;
+    return a;
+  };
   hipError_t e = hipSuccess;
   if (!copy_stream) {
     // No copy stream: step i's kernel itself copies the chunk of step i+1
@@ -377,8 +387,9 @@ int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks, const void* cons
         const int j = steps[i + 1].j;
         sc = ra::StageCopy{{k_chunks[j], v_chunks[j]}, {slot_k(i & 1), slot_v(i & 1)}, chunk_bytes / 16};
       }
-      ra::FwdStepArgs a = i == 0 ? step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, false)
-                                 : step_args(slot_k((i - 1) & 1), slot_v((i - 1) & 1), sp.diag, true);
+      ra::FwdStepArgs a = with_queues(i == 0 ? step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, false)
+                                             : step_args(slot_k((i - 1) & 1), slot_v((i - 1) & 1), sp.diag, true),
+                                      i);
       if (i + 1 < n) a.stage = &sc;
       if ((e = fwd_step(a, cs)) != hipSuccess) return hip_fail(e, "ra_ring_fwd step");
     }
@@ -409,11 +420,11 @@ int ra_ring_fwd_gqa(const void* q, const void* const* k_chunks, const void* cons
     }
     const Step& sp = steps[i];
     if (i == 0) {
-      e = fwd_step(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, false), cs);
+      e = fwd_step(with_queues(step_args(k_chunks[sp.j], v_chunks[sp.j], sp.diag, false), i), cs);
     } else {
       const int slot = (i - 1) & 1;
       if ((e = hipStreamWaitEvent(cs, ev->copied[slot], 0)) != hipSuccess) return hip_fail(e, "ra_ring_fwd wait");
-      e = fwd_step(step_args(slot_k(slot), slot_v(slot), sp.diag, true), cs);
+      e = fwd_step(with_queues(step_args(slot_k(slot), slot_v(slot), sp.diag, true), i), cs);
       if (e == hipSuccess) e = hipEventRecord(ev->consumed[slot], cs);
     }
     if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd step");

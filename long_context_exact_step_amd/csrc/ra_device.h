@@ -17,6 +17,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;  // MI355X: 8 XCDs x 32 CUs; workgroups go round-robin over XCDs
+// s_getreg operand for the XCC_ID hardware register (id 20, all 32 bits):
+// the XCD the wave runs on.
+constexpr int kHwRegXccId = 20 | (31 << 11);
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -41,6 +41,8 @@
 //    diagonal chunk the longest query tiles of every head go first.
 #include <type_traits>
 
+#include <atomic>
+
 #include "ra_device.h"
 #include "ra_kernels.h"
 
@@ -136,7 +138,7 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
                                          const uint16_t* __restrict__ vg, float* __restrict__ og,
                                          float* __restrict__ lseg, int Sq, int Sk, int n_qtiles, int total_tiles,
                                          float scale_log2, int group, int qoff, const ChunkTable& tbl,
-                                         const StageCopy& stage) {
+                                         const StageCopy& stage, int unit, bool stage_now) {
   constexpr int NW = kFwdWaves, NQW = kFwdRowsPerWave, BR = NW * NQW, BC = kTileTokens;
   constexpr int NKS = D / 16, NDB = D / 32, NKB = BC / 32, TILE = BC * D * 2, LA = kFwdLookahead;
   constexpr int NB = kFwdBuffers;
@@ -160,15 +162,16 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
   const int l32 = lane & 31, g = lane >> 5;
+  // The block's unit: the (head row, query tile) pair, numbered as the
+  // launch maps them (see fwd_step_kernel).
   int bh, qt;
   if constexpr (DIAG) {
     // Causal: the last query tiles see the most keys; they go first.
-    longest_first(blockIdx.x, total_tiles / n_qtiles, bh, qt);
+    longest_first(unit, total_tiles / n_qtiles, bh, qt);
     qt = n_qtiles - 1 - qt;
   } else {
-    const int t = xcd_remap(blockIdx.x, total_tiles);
-    bh = t / n_qtiles;
-    qt = t - bh * n_qtiles;
+    bh = unit / n_qtiles;
+    qt = unit - bh * n_qtiles;
   }
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * NQW;
@@ -490,7 +493,9 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
 
   // The ring's next chunk into the idle slot (this block's share), while the
   // block's first tile loads are in flight.
-  if constexpr (!WALK) stage_block_share<64 * NW, 8>(stage.src, stage.dst, stage.units);
+  if constexpr (!WALK) {
+    if (stage_now) stage_block_share<64 * NW, 8>(stage.src, stage.dst, stage.units);
+  }
 
   // Prologue: S^T(0) once K(0) has landed (computed, harmlessly, also for a
   // wave with no rows); its stream issues iteration 0's first reads.
@@ -519,6 +524,13 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
   fwd_epilogue<D, MERGE>(oacc, mrow, lrow - lcomp, og, lseg, bh, Sq, qq, g);
 }
 
+// One ring step.  Static (queue null): block b takes unit xcd_remap(b) of a
+// full chunk, or level-ordered unit b of the diagonal.  Persistent (queue
+// non-null, full chunks): one block per compute unit; thread 0 takes the
+// next unit of its XCD's queue -- XCD x's queue holds the units xcd_remap
+// gives XCD x, in the same order -- and, once that queue is empty, of the
+// next XCDs' in turn.  The units are equal work, but the XCDs do not run at
+// equal speed, and a static split ends with the slowest one.
 template <int D, bool DIAG, bool MERGE>
 __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t* __restrict__ qg,
                                                                   const uint16_t* __restrict__ kg,
@@ -527,10 +539,48 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
                                                                   float* __restrict__ lseg, int Sq, int Sk,
                                                                   int n_qtiles, int total_tiles,
                                                                   float scale_log2, int group, int qoff,
-                                                                  StageCopy stage) {
+                                                                  StageCopy stage, int* queue, int* queue_next) {
+  static_assert(16 * kXcds <= kFwdQueueInts, "one counter per XCD, 64 bytes apart");
   const ChunkTable none{};
-  fwd_body<D, DIAG, MERGE, false>(qg, kg, vg, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group, qoff,
-                                  none, stage);
+  if (queue_next && blockIdx.x == 0 && threadIdx.x < kFwdQueueInts) queue_next[threadIdx.x] = 0;
+  if (DIAG || !queue) {
+    const int unit = DIAG ? (int)blockIdx.x : xcd_remap(blockIdx.x, total_tiles);
+    fwd_body<D, DIAG, MERGE, false>(qg, kg, vg, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group, qoff,
+                                    none, stage, unit, true);
+    return;
+  }
+  if constexpr (!DIAG) {
+    __shared__ int unit_s;
+    // This wave's XCD (hardware register XCC_ID).
+    const int xcd = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) % kXcds);
+    const int q = total_tiles / kXcds, r = total_tiles % kXcds;
+    int from = 0;  // queues xcd, xcd+1, ... before `from` are empty (thread 0)
+    for (bool first = true;; first = false) {
+      if (threadIdx.x == 0) {
+        int t = -1;
+        for (; from < kXcds; ++from) {
+          const int y = (xcd + from) % kXcds;
+          const int u = __hip_atomic_fetch_add(queue + 16 * y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (u < q + (y < r ? 1 : 0)) {
+            t = y * q + (y < r ? y : r) + u;
+            break;
+          }
+        }
+        unit_s = t;
+      }
+      __syncthreads();
+      const int t = unit_s;
+      __syncthreads();  // every thread has read unit_s before thread 0 writes it again
+      if (t < 0) {
+        // A block that started after the queues ran dry (the grid need not
+        // be resident all at once) still copies its share of the next chunk.
+        if (first) stage_block_share<64 * kFwdWaves, 8>(stage.src, stage.dst, stage.units);
+        break;
+      }
+      fwd_body<D, false, MERGE, false>(qg, kg, vg, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group,
+                                       qoff, none, stage, t, first);
+    }
+  }
 }
 
 // One pass over resident chunks (no merge: the pass sees every key).
@@ -542,8 +592,23 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_walk_kernel(const uint16_t
                                                                   float scale_log2, int group, int qoff,
                                                                   ChunkTable tbl) {
   const StageCopy none{};
+  const int unit = DIAG ? (int)blockIdx.x : xcd_remap(blockIdx.x, total_tiles);
   fwd_body<D, DIAG, false, true>(qg, nullptr, nullptr, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group,
-                                 qoff, tbl, none);
+                                 qoff, tbl, none, unit, true);
+}
+
+// Compute units of the current device, looked up once per device.
+int compute_units() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return -1;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 template <int D>
@@ -571,9 +636,19 @@ hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const StageCopy stage = a.stage ? *a.stage : StageCopy{};
+  // Persistent blocks only where there are more units than compute units.
+  int* queue = nullptr;
+  if (a.queue && !a.diag) {
+    const int ncu = compute_units();
+    if (ncu <= 0) return hipErrorInvalidDevice;
+    if (total > ncu) {
+      queue = a.queue;
+      grid = dim3((unsigned)ncu);
+    }
+  }
 #define RA_FWD_LAUNCH(DIAG, MERGE)                                                                         \
   hipLaunchKernelGGL((fwd_step_kernel<D, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, a.v, a.o, \
-                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff, stage)
+                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff, stage, queue, a.queue_next)
   if (a.diag) {
     if (a.merge) RA_FWD_LAUNCH(true, true);
     else RA_FWD_LAUNCH(true, false);

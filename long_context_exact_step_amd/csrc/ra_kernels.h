@@ -31,6 +31,10 @@ struct StageCopy {
   size_t units;
 };
 
+// Unit counters of a persistent step launch: one per XCD, 64 bytes apart.
+constexpr int kFwdQueueInts = 128;
+constexpr size_t kFwdQueueBytes = kFwdQueueInts * sizeof(int);
+
 struct FwdStepArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -48,6 +52,16 @@ struct FwdStepArgs {
   const ChunkTable* walk = nullptr;
   // Non-null: stage the next chunk from inside this launch (step kernels only).
   const StageCopy* stage = nullptr;
+  // Non-null (full-chunk steps): kFwdQueueInts zeroed counters this launch
+  // owns while it runs.  The launch then runs one persistent block per
+  // compute unit; a block takes (head, query tile) units from its XCD's
+  // queue, the same units in the same order as the static mapping, and once
+  // that queue is empty from the other XCDs' queues, so that faster XCDs
+  // take more units.  Null: one block per unit, statically mapped.
+  int* queue = nullptr;
+  // Non-null: kFwdQueueInts counters the launch sets to zero for the next
+  // launch on the stream (which cannot start before this one ends).
+  int* queue_next = nullptr;
 };
 hipError_t launch_fwd_step(const FwdStepArgs& a, hipStream_t stream);
 

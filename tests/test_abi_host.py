@@ -137,8 +137,8 @@ def test_ring_bwd_noalloc_validation(L):
 
 
 def test_workspace_sizes(L):
-    # Double buffer: 2 slots x (K + V) x B*H*C*d bf16.
-    assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 1, 0) == 2 * 2 * 32 * 32768 * 128 * 2
+    # Double buffer: 2 slots x (K + V) x B*H*C*d bf16, then 2 x 512 bytes of queue counters.
+    assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 1, 0) == 2 * 2 * 32 * 32768 * 128 * 2 + 1024
     assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 0, 0) == 0
     assert L.ra_ring_workspace_bytes(4, 1, 32, 32768, 128, 2, 0) == 0  # fused walk: no staging
     assert L.ra_ring_workspace_bytes(4, 1, 32, 16384, 128, 0, 1) == 2 * 32 * 16384 * 4
@@ -147,7 +147,7 @@ def test_workspace_sizes(L):
 
 def test_gqa_workspace_sizes(L):
     # Double buffer holds H_kv-head chunks; the backward's per-row values keep H heads.
-    assert L.ra_ring_workspace_bytes_gqa(4, 1, 32, 8, 32768, 128, 1, 0) == 2 * 2 * 8 * 32768 * 128 * 2
+    assert L.ra_ring_workspace_bytes_gqa(4, 1, 32, 8, 32768, 128, 1, 0) == 2 * 2 * 8 * 32768 * 128 * 2 + 1024
     assert L.ra_ring_workspace_bytes_gqa(4, 1, 32, 8, 16384, 128, 0, 1) == 2 * 32 * 16384 * 4
     assert L.ra_ring_workspace_bytes_gqa(4, 1, 32, 32, 32768, 128, 1, 0) == L.ra_ring_workspace_bytes(
         4, 1, 32, 32768, 128, 1, 0)

@@ -157,6 +157,44 @@ def test_ring_fwd_fused_every_rank(P, C, d, causal, H_kv, B, H):
         assert_close(outs["fused"][1], outs["resident"][1], 1e-4, "fused vs resident lse", rel=None)
 
 
+@pytest.mark.parametrize("P,C,d,H,Hk,causal", [(3, 2304, 64, 32, 32, True), (3, 2304, 128, 32, 8, True),
+                                               (2, 2340, 64, 32, 32, False)])
+def test_ring_fwd_persistent_steps_match_static(P, C, d, H, Hk, causal):
+    """The double-buffer walk's full-chunk steps, with more (head, query tile)
+    units than compute units, run persistent blocks that take units from
+    per-XCD work queues; the resident walk runs one block per unit.  Each
+    unit is computed the same way whichever block takes it, so the two are
+    bit-identical: every rank, both stagings (C = 2340 has ragged query and
+    key tiles).  Sampled rows against the oracle."""
+    B = 1
+    ncu, _ = ra.device_info()
+    assert B * H * -(-C // 256) > ncu, "the case needs more units than compute units"
+    q, k, v, _ = ring_tensors(117, B, H, P, C, d, H_kv=Hk)
+    kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
+    kd = [t.to(dev()) for t in k]
+    vd = [t.to(dev()) for t in v]
+    scale = 1 / math.sqrt(d)
+    rows = np.array([0, 37, 255, 256, C // 2, C - 1])
+    copy_stream = torch.cuda.Stream()
+    for rank in range(P):
+        qd = q[rank].to(dev())
+        outs = {}
+        for mode, cs in (("resident", None), ("double_buffer", copy_stream), ("double_buffer", None)):
+            print(f"persistent steps P={P} C={C} d={d} H={H} Hk={Hk} causal={causal} rank={rank} {mode} "
+                  f"copy_stream={cs is not None}", flush=True)
+            o = torch.full((B, H, C, d), float("nan"), device=dev())
+            lse = torch.full((B, H, C), float("nan"), device=dev())
+            ra.ring_fwd(qd, kd, vd, o, lse, rank, causal, scale, ring_mode=mode, copy_stream=cs)
+            torch.cuda.synchronize()
+            outs[(mode, cs is not None)] = (o.cpu(), lse.cpu())
+        ro, rl = outs[("resident", False)]
+        for key, (o, lse) in outs.items():
+            assert torch.equal(o, ro) and torch.equal(lse, rl), f"{key} differs from the resident walk"
+        po, pl = oracle.attention_fwd(f64(q[rank][:, :, rows]), kf, vf, scale, causal, q_pos=rank * C + rows)
+        assert_close(f64(ro[:, :, rows]), po, TOL_O, f"o rank {rank}")
+        assert_close(f64(rl[:, :, rows]), pl, TOL_LSE, f"lse rank {rank}", rel=None)
+
+
 @pytest.mark.parametrize("P,C", [(3, 100), (17, 64)])
 def test_ring_fwd_fused_falls_back(P, C):
     """Chunk lengths that are not a multiple of 64, or more than 16 visible
