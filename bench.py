@@ -60,7 +60,10 @@ def fwd_kernel_sha():
     return h.hexdigest()[:16]
 
 
-COUNTER_KERNEL = "fwd_step_kernel<128, false, true>"  # the full-chunk step with the fused merge
+# The full-chunk merge step of the 128K share's double-buffer walk, on
+# persistent blocks (the step kernel of the static schedule is
+# fwd_step_kernel<128, false, true>).
+COUNTER_KERNEL = "fwd_queue_kernel<128, true>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -715,7 +718,7 @@ def cpu_baseline(w, tensors, budget_s):
     threads = max((i.get("num_threads", 1) for i in blas), default=1)
     flops = 4 * d * pairs
     rate = flops / secs  # fp64 flop/s of the oracle on this sample
-    from long_context_exact_step_amd.workloads import WORKLOADS, Workload, fwd_flops
+    from long_context_exact_step_amd.workloads import WORKLOADS, Workload, fwd_flops, queue_steps_apply
     # Whole-config times at the sample's rate: the sampled rows are uniform
     # over each head's rows, so the visible-pair ratio scales them without
     # bias.  Extrapolated, not measured.
@@ -771,7 +774,8 @@ def main():
         sys.exit(2)
 
     import torch
-    from long_context_exact_step_amd.workloads import WORKLOADS, Workload, fwd_flops
+    import long_context_exact_step_amd as ra
+    from long_context_exact_step_amd.workloads import WORKLOADS, Workload, fwd_flops, queue_steps_apply
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -790,13 +794,19 @@ def main():
         dom = "fwd_full" if "fwd_full" in fwd["kernels"] else "fwd_diag"
         dk = fwd["kernels"][dom]
         dom_flops = 4 * w.d * pairs_of_kind(dom, w)
+    # The kernel those launches ran: full-chunk steps of a double-buffer walk
+    # large enough for persistent blocks run fwd_queue_kernel.
+    cus, _ = ra.device_info()
+    queued = args.ring_mode.startswith("double_buffer") and queue_steps_apply(w, "double_buffer", cus)
+    full_kernel = "fwd_queue_kernel" if dom == "fwd_full" and queued else "fwd_step_kernel"
     achieved = dom_flops / (dk["avg_ms"] * 1e-3) / 1e12
     traffic = None
     try:
         with open(PROFILE_COUNTERS) as f:
             prof = json.load(f)
-        # The counters cover the full-chunk step kernel, not the fused walk.
-        if prof.get("source_sha") == fwd_kernel_sha() and prof.get("workload_id") == w.id and dom != "fwd_walk":
+        # The counters cover one kernel of one workload (not the fused walk).
+        if (prof.get("source_sha") == fwd_kernel_sha() and prof.get("workload_id") == w.id and dom != "fwd_walk"
+                and prof.get("kernel", "").startswith(full_kernel)):
             traffic = prof.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
@@ -806,7 +816,7 @@ def main():
         # HBM bytes per launch (counters) over the live launch time: achieved HBM bandwidth.
         "traffic_gbps": None if traffic is None else round(traffic / (dk["avg_ms"] * 1e-3) / 1e9, 1),
         "kernel": (f"fwd_walk_kernel (fused walk), {dk['launches']} launches, {dk['avg_ms']} ms per step"
-                   if dom == "fwd_walk" else f"fwd_step_kernel ({dom}), {dk['launches']} launches, avg {dk['avg_ms']} ms"),
+                   if dom == "fwd_walk" else f"{full_kernel} ({dom}), {dk['launches']} launches, avg {dk['avg_ms']} ms"),
         "flops_per_launch": dom_flops,  # fused walk: per step (all its launches)
     }
 

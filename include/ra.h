@@ -161,8 +161,8 @@ size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d,
  * share of the chunk once its own tiles are done, so the walk is one
  * stream of kernels with no copies or events elsewhere (cheaper per step
  * for short chunks).  The workspace also holds the work-queue counters of
- * the full-chunk steps: with more (head, query tile) units than compute
- * units, such a step runs one persistent block per compute unit, taking
+ * the full-chunk steps: with at least four (head, query tile) units per
+ * compute unit, such a step runs one persistent block per compute unit, taking
  * units from its XCD's queue first and then from the other XCDs', so that
  * a slower XCD does not set the step's length.  Results are the same bits
  * as with one block per unit.

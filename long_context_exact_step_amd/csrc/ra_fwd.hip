@@ -524,13 +524,9 @@ __device__ __forceinline__ void fwd_body(const uint16_t* __restrict__ qg, const 
   fwd_epilogue<D, MERGE>(oacc, mrow, lrow - lcomp, og, lseg, bh, Sq, qq, g);
 }
 
-// One ring step.  Static (queue null): block b takes unit xcd_remap(b) of a
-// full chunk, or level-ordered unit b of the diagonal.  Persistent (queue
-// non-null, full chunks): one block per compute unit; thread 0 takes the
-// next unit of its XCD's queue -- XCD x's queue holds the units xcd_remap
-// gives XCD x, in the same order -- and, once that queue is empty, of the
-// next XCDs' in turn.  The units are equal work, but the XCDs do not run at
-// equal speed, and a static split ends with the slowest one.
+// One ring step: block b takes unit xcd_remap(b) of a full chunk, or
+// level-ordered unit b of the diagonal.  Block 0 first zeroes the work-queue
+// counters of the next step launch (queue_next), if any.
 template <int D, bool DIAG, bool MERGE>
 __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t* __restrict__ qg,
                                                                   const uint16_t* __restrict__ kg,
@@ -539,47 +535,62 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_step_kernel(const uint16_t
                                                                   float* __restrict__ lseg, int Sq, int Sk,
                                                                   int n_qtiles, int total_tiles,
                                                                   float scale_log2, int group, int qoff,
-                                                                  StageCopy stage, int* queue, int* queue_next) {
-  static_assert(16 * kXcds <= kFwdQueueInts, "one counter per XCD, 64 bytes apart");
-  const ChunkTable none{};
+                                                                  StageCopy stage, int* queue_next) {
   if (queue_next && blockIdx.x == 0 && threadIdx.x < kFwdQueueInts) queue_next[threadIdx.x] = 0;
-  if (DIAG || !queue) {
-    const int unit = DIAG ? (int)blockIdx.x : xcd_remap(blockIdx.x, total_tiles);
-    fwd_body<D, DIAG, MERGE, false>(qg, kg, vg, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group, qoff,
-                                    none, stage, unit, true);
-    return;
-  }
-  if constexpr (!DIAG) {
-    __shared__ int unit_s;
-    // This wave's XCD (hardware register XCC_ID).
-    const int xcd = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) % kXcds);
-    const int q = total_tiles / kXcds, r = total_tiles % kXcds;
-    int from = 0;  // queues xcd, xcd+1, ... before `from` are empty (thread 0)
-    for (bool first = true;; first = false) {
-      if (threadIdx.x == 0) {
-        int t = -1;
-        for (; from < kXcds; ++from) {
-          const int y = (xcd + from) % kXcds;
-          const int u = __hip_atomic_fetch_add(queue + 16 * y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (u < q + (y < r ? 1 : 0)) {
-            t = y * q + (y < r ? y : r) + u;
-            break;
-          }
+  const ChunkTable none{};
+  const int unit = DIAG ? (int)blockIdx.x : xcd_remap(blockIdx.x, total_tiles);
+  fwd_body<D, DIAG, MERGE, false>(qg, kg, vg, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group, qoff,
+                                  none, stage, unit, true);
+}
+
+// One full-chunk ring step on persistent blocks (one per compute unit).
+// Thread 0 takes the next unit of its XCD's queue -- XCD x's queue holds the
+// units that xcd_remap gives XCD x, in the same order -- and, once that
+// queue is empty, of the next XCDs' in turn.  The units are equal work, but
+// the XCDs do not run at equal speed, and a static split ends with the
+// slowest one.  queue: kFwdQueueInts zeroed counters, one per XCD 64 bytes
+// apart; queue_next as in fwd_step_kernel.
+template <int D, bool MERGE>
+__global__ __launch_bounds__(64 * kFwdWaves) void fwd_queue_kernel(const uint16_t* __restrict__ qg,
+                                                                   const uint16_t* __restrict__ kg,
+                                                                   const uint16_t* __restrict__ vg,
+                                                                   float* __restrict__ og,
+                                                                   float* __restrict__ lseg, int Sq, int Sk,
+                                                                   int n_qtiles, int total_tiles,
+                                                                   float scale_log2, int group, int qoff,
+                                                                   StageCopy stage, int* queue, int* queue_next) {
+  static_assert(16 * kXcds <= kFwdQueueInts, "one counter per XCD, 64 bytes apart");
+  if (queue_next && blockIdx.x == 0 && threadIdx.x < kFwdQueueInts) queue_next[threadIdx.x] = 0;
+  const ChunkTable none{};
+  __shared__ int unit_s;
+  // This wave's XCD (hardware register XCC_ID).
+  const int xcd = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) % kXcds);
+  const int q = total_tiles / kXcds, r = total_tiles % kXcds;
+  int from = 0;  // queues xcd, xcd+1, ... before `from` are empty (thread 0)
+  for (bool first = true;; first = false) {
+    if (threadIdx.x == 0) {
+      int t = -1;
+      for (; from < kXcds; ++from) {
+        const int y = (xcd + from) % kXcds;
+        const int n = __hip_atomic_fetch_add(queue + 16 * y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n < q + (y < r ? 1 : 0)) {
+          t = y * q + (y < r ? y : r) + n;
+          break;
         }
-        unit_s = t;
       }
-      __syncthreads();
-      const int t = unit_s;
-      __syncthreads();  // every thread has read unit_s before thread 0 writes it again
-      if (t < 0) {
-        // A block that started after the queues ran dry (the grid need not
-        // be resident all at once) still copies its share of the next chunk.
-        if (first) stage_block_share<64 * kFwdWaves, 8>(stage.src, stage.dst, stage.units);
-        break;
-      }
-      fwd_body<D, false, MERGE, false>(qg, kg, vg, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group,
-                                       qoff, none, stage, t, first);
+      unit_s = t;
     }
+    __syncthreads();
+    const int t = unit_s;
+    __syncthreads();  // every thread has read unit_s before thread 0 writes it again
+    if (t < 0) {
+      // A block that started after the queues ran dry (the grid need not
+      // be resident all at once) still copies its share of the next chunk.
+      if (first) stage_block_share<64 * kFwdWaves, 8>(stage.src, stage.dst, stage.units);
+      break;
+    }
+    fwd_body<D, false, MERGE, false>(qg, kg, vg, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group, qoff,
+                                     none, stage, t, first);
   }
 }
 
@@ -596,6 +607,8 @@ __global__ __launch_bounds__(64 * kFwdWaves) void fwd_walk_kernel(const uint16_t
   fwd_body<D, DIAG, false, true>(qg, nullptr, nullptr, og, lseg, Sq, Sk, n_qtiles, total_tiles, scale_log2, group,
                                  qoff, tbl, none, unit, true);
 }
+
+constexpr int kPersistentUnitsPerCu = 4;
 
 // Compute units of the current device, looked up once per device.
 int compute_units() {
@@ -636,19 +649,27 @@ hipError_t launch_cfg(const FwdStepArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const StageCopy stage = a.stage ? *a.stage : StageCopy{};
-  // Persistent blocks only where there are more units than compute units.
-  int* queue = nullptr;
+  // Persistent blocks only where each compute unit has several units to
+  // take (kPersistentUnitsPerCu or more): with fewer, the last unit of each
+  // block sets the step's length anyway, and a staging copy queued on
+  // another stream would wait for CUs that the step holds throughout.
   if (a.queue && !a.diag) {
     const int ncu = compute_units();
     if (ncu <= 0) return hipErrorInvalidDevice;
-    if (total > ncu) {
-      queue = a.queue;
-      grid = dim3((unsigned)ncu);
+    if (total >= (long long)kPersistentUnitsPerCu * ncu) {
+      const dim3 pgrid((unsigned)ncu);
+      if (a.merge)
+        hipLaunchKernelGGL((fwd_queue_kernel<D, true>), pgrid, block, 0, stream, a.q, a.k, a.v, a.o, a.lse, a.Sq,
+                           a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff, stage, a.queue, a.queue_next);
+      else
+        hipLaunchKernelGGL((fwd_queue_kernel<D, false>), pgrid, block, 0, stream, a.q, a.k, a.v, a.o, a.lse, a.Sq,
+                           a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff, stage, a.queue, a.queue_next);
+      return hipGetLastError();
     }
   }
 #define RA_FWD_LAUNCH(DIAG, MERGE)                                                                         \
   hipLaunchKernelGGL((fwd_step_kernel<D, DIAG, MERGE>), grid, block, 0, stream, a.q, a.k, a.v, a.o, \
-                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff, stage, queue, a.queue_next)
+                     a.lse, a.Sq, a.Sk, n_qtiles, (int)total, sl2, a.group, a.qoff, stage, a.queue_next)
   if (a.diag) {
     if (a.merge) RA_FWD_LAUNCH(true, true);
     else RA_FWD_LAUNCH(true, false);

@@ -53,8 +53,9 @@ struct FwdStepArgs {
   // Non-null: stage the next chunk from inside this launch (step kernels only).
   const StageCopy* stage = nullptr;
   // Non-null (full-chunk steps): kFwdQueueInts zeroed counters this launch
-  // owns while it runs.  The launch then runs one persistent block per
-  // compute unit; a block takes (head, query tile) units from its XCD's
+  // owns while it runs.  With at least four (head, query tile) units per
+  // compute unit, the launch then runs one persistent block per compute
+  // unit; a block takes units from its XCD's
   // queue, the same units in the same order as the static mapping, and once
   // that queue is empty from the other XCDs' queues, so that faster XCDs
   // take more units.  Null: one block per unit, statically mapped.

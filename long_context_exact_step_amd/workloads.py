@@ -72,6 +72,15 @@ def fused_walk_applies(w, rank):
     return w.C % 64 == 0 and nvis <= MAX_WALK_CHUNKS and nvis * w.C < 2 ** 30
 
 
+def queue_steps_apply(w, ring_mode, cus):
+    """Whether ra_ring_fwd runs the walk's full-chunk steps on persistent
+    blocks with per-XCD work queues (the library's rule: the double-buffer
+    walk, whose workspace holds the queue counters, with at least four
+    (head, query tile) units of 256 query rows per compute unit)."""
+    units = w.B * w.H * -(-w.C // 256)
+    return ring_mode == "double_buffer" and units >= 4 * cus
+
+
 def visible_pairs_per_head(w, rank):
     """(query, key) pairs a rank's walk evaluates per (batch, head)."""
     n = 0

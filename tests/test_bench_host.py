@@ -13,7 +13,7 @@ sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
 
-KERNEL = "void ra::(anonymous namespace)::fwd_step_kernel<128, false, true>(unsigned short const*, float*)"
+KERNEL = "void ra::(anonymous namespace)::fwd_queue_kernel<128, true>(unsigned short const*, float*)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -51,6 +51,24 @@ def test_counter_ingestion(tmp_path):
     assert rec["hbm_bytes_per_launch"] == (2200.0 + 600.0) * 1024
     assert rec["source_sha"] == bench.fwd_kernel_sha()
     assert json.loads(out.read_text()) == rec
+
+
+def test_queue_rule():
+    """bench.py names the kernel of the full-chunk launches by the library's
+    rule for persistent steps: the double-buffer walk with at least four
+    units of 256 query rows per compute unit."""
+    from dataclasses import replace
+
+    from long_context_exact_step_amd.workloads import WORKLOADS, queue_steps_apply
+
+    assert queue_steps_apply(WORKLOADS[2], "double_buffer", 256)      # 32 heads x 128 query tiles
+    assert queue_steps_apply(WORKLOADS[5], "double_buffer", 256)      # 32 x 64
+    assert not queue_steps_apply(WORKLOADS[3], "double_buffer", 256)  # 32 x 16: 2 per CU
+    assert not queue_steps_apply(WORKLOADS[2], "resident", 256)
+    assert not queue_steps_apply(WORKLOADS[2], "fused", 256)
+    w = replace(WORKLOADS[3], C=8192)
+    assert queue_steps_apply(w, "double_buffer", 256)                 # 32 x 32 = 4 per CU
+    assert not queue_steps_apply(replace(w, C=8192 - 256), "double_buffer", 256)
 
 
 def test_fused_walk_rule_mirrors_the_library():

@@ -157,18 +157,18 @@ def test_ring_fwd_fused_every_rank(P, C, d, causal, H_kv, B, H):
         assert_close(outs["fused"][1], outs["resident"][1], 1e-4, "fused vs resident lse", rel=None)
 
 
-@pytest.mark.parametrize("P,C,d,H,Hk,causal", [(3, 2304, 64, 32, 32, True), (3, 2304, 128, 32, 8, True),
-                                               (2, 2340, 64, 32, 32, False)])
+@pytest.mark.parametrize("P,C,d,H,Hk,causal", [(3, 8192, 64, 32, 32, True), (3, 8192, 128, 32, 8, True),
+                                               (2, 8212, 64, 32, 32, False)])
 def test_ring_fwd_persistent_steps_match_static(P, C, d, H, Hk, causal):
-    """The double-buffer walk's full-chunk steps, with more (head, query tile)
-    units than compute units, run persistent blocks that take units from
-    per-XCD work queues; the resident walk runs one block per unit.  Each
-    unit is computed the same way whichever block takes it, so the two are
-    bit-identical: every rank, both stagings (C = 2340 has ragged query and
-    key tiles).  Sampled rows against the oracle."""
+    """The double-buffer walk's full-chunk steps, with at least four (head,
+    query tile) units per compute unit, run persistent blocks that take
+    units from per-XCD work queues; the resident walk runs one block per
+    unit.  Each unit is computed the same way whichever block takes it, so
+    the two are bit-identical: every rank, both stagings (C = 8212 has
+    ragged query and key tiles).  Sampled rows against the oracle."""
     B = 1
     ncu, _ = ra.device_info()
-    assert B * H * -(-C // 256) > ncu, "the case needs more units than compute units"
+    assert B * H * -(-C // 256) >= 4 * ncu, "the case needs four units per compute unit"
     q, k, v, _ = ring_tensors(117, B, H, P, C, d, H_kv=Hk)
     kf, vf = f64(torch.cat(k, dim=2)), f64(torch.cat(v, dim=2))
     kd = [t.to(dev()) for t in k]
