@@ -48,7 +48,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak (the roofline
 # 256 CUs x 4096 flop per CU per clock x 2.4 GHz: the same peak derived from
 # the chip's unit counts and clock, reported beside the published figure.
 DERIVED_PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fwd_step_full_128k_cp4_counters.json")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fwd_full_step_128k_cp4_counters.json")
 FWD_KERNEL_SOURCES = ["long_context_exact_step_amd/csrc/ra_fwd.hip", "long_context_exact_step_amd/csrc/ra_device.h"]
 
 
