@@ -157,16 +157,16 @@ def test_ring_fwd_fused_every_rank(P, C, d, causal, H_kv, B, H):
         assert_close(outs["fused"][1], outs["resident"][1], 1e-4, "fused vs resident lse", rel=None)
 
 
-@pytest.mark.parametrize("P,C,d,H,Hk,causal", [(3, 8192, 64, 32, 32, True), (3, 8192, 128, 32, 8, True),
-                                               (2, 8212, 64, 32, 32, False)])
-def test_ring_fwd_persistent_steps_match_static(P, C, d, H, Hk, causal):
+@pytest.mark.parametrize("P,C,d,H,Hk,causal,B", [(3, 8192, 64, 32, 32, True, 1), (3, 8192, 128, 32, 8, True, 1),
+                                                 (2, 8212, 64, 32, 32, False, 1), (2, 8192, 64, 16, 4, True, 2)])
+def test_ring_fwd_persistent_steps_match_static(P, C, d, H, Hk, causal, B):
     """The double-buffer walk's full-chunk steps, with at least four (head,
     query tile) units per compute unit, run persistent blocks that take
     units from per-XCD work queues; the resident walk runs one block per
     unit.  Each unit is computed the same way whichever block takes it, so
     the two are bit-identical: every rank, both stagings (C = 8212 has
-    ragged query and key tiles).  Sampled rows against the oracle."""
-    B = 1
+    ragged query and key tiles; B = 2 puts the batch index in the units).
+    Sampled rows against the oracle."""
     ncu, _ = ra.device_info()
     assert B * H * -(-C // 256) >= 4 * ncu, "the case needs four units per compute unit"
     q, k, v, _ = ring_tensors(117, B, H, P, C, d, H_kv=Hk)
@@ -180,7 +180,7 @@ def test_ring_fwd_persistent_steps_match_static(P, C, d, H, Hk, causal):
         qd = q[rank].to(dev())
         outs = {}
         for mode, cs in (("resident", None), ("double_buffer", copy_stream), ("double_buffer", None)):
-            print(f"persistent steps P={P} C={C} d={d} H={H} Hk={Hk} causal={causal} rank={rank} {mode} "
+            print(f"persistent steps B={B} P={P} C={C} d={d} H={H} Hk={Hk} causal={causal} rank={rank} {mode} "
                   f"copy_stream={cs is not None}", flush=True)
             o = torch.full((B, H, C, d), float("nan"), device=dev())
             lse = torch.full((B, H, C), float("nan"), device=dev())
