@@ -186,10 +186,81 @@ class StepClock:
         return d[m] if len(d) % 2 else 0.5 * (d[m - 1] + d[m])
 
 
-def timed_steps(step_fn, n_launch_per_step, steps, warmup, clock=None):
+class ClockSampler:
+    """The GPU's current engine clock as its driver reports it (the level
+    marked '*' in pp_dpm_sclk), read by a thread every `period` seconds
+    between start() and stop(): the clock the timed steps ran at, for the
+    fraction of the peak at that clock.  The file is that of cuda:0's PCI
+    device (or the only one present); samples stay empty where it cannot be
+    read."""
+
+    def __init__(self, period=0.01):
+        import glob
+        import threading
+        import torch
+        self.path = None
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        try:
+            p = torch.cuda.get_device_properties(0)
+            bus = "%04x:%02x:%02x" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+            mine = [x for x in paths if os.path.basename(os.path.realpath(os.path.dirname(x))).startswith(bus)]
+        except (AttributeError, RuntimeError, AssertionError):
+            mine = []
+        if len(mine) == 1:
+            self.path = mine[0]
+        elif len(paths) == 1:
+            self.path = paths[0]
+        self.period, self.samples = period, []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def parse(text):
+        """MHz of the level marked '*' in pp_dpm_sclk text ("1: 1650Mhz *"), or None."""
+        for line in text.splitlines():
+            line = line.strip()
+            if line.endswith("*"):
+                try:
+                    return float(line.split(":")[1].rstrip("*").strip().lower().rstrip("mhz"))
+                except (IndexError, ValueError):
+                    return None
+        return None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                return self.parse(f.read())
+        except OSError:
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.path:
+            self._thread.start()
+
+    def stop(self):
+        if self.path:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"mean_mhz": round(sum(v) / len(v), 1), "median_mhz": v[len(v) // 2], "min_mhz": v[0],
+                "max_mhz": v[-1], "samples": len(v), "source": self.path}
+
+
+def timed_steps(step_fn, n_launch_per_step, steps, warmup, clock=None, sampler=None):
     """Runs warmup, then exactly `steps` timed steps with per-launch tracing
-    (and step-boundary events into `clock`, if given).
-    Returns (seconds, [(kind, ms), ...])."""
+    (and step-boundary events into `clock`, the engine clock into `sampler`,
+    if given).  Returns (seconds, [(kind, ms), ...])."""
     import torch
     import long_context_exact_step_amd as ra
 
@@ -201,6 +272,8 @@ def timed_steps(step_fn, n_launch_per_step, steps, warmup, clock=None):
     kinds = (ctypes.c_int * cap)()
     keep = ra.trace_begin(ev.start, ev.end, kinds)
     torch.cuda.synchronize()
+    if sampler:
+        sampler.start()
     t0 = time.perf_counter()
     if clock:
         clock.mark()
@@ -210,6 +283,8 @@ def timed_steps(step_fn, n_launch_per_step, steps, warmup, clock=None):
             clock.mark()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if sampler:
+        sampler.stop()
     n = ra.trace_end()
     del keep
     rec = [(ra.TRACE_KINDS[kinds[i]], ev.elapsed_ms(i)) for i in range(min(n, cap))]
@@ -258,7 +333,7 @@ def untraced_steps(step_fn, steps, warmup, clock=None):
     return time.perf_counter() - t0
 
 
-def run_fwd(w, steps, warmup, ring_mode, H_kv=None, trace=True, concurrent=False):
+def run_fwd(w, steps, warmup, ring_mode, H_kv=None, trace=True, concurrent=False, sampler=None):
     """The forward walk of workload w; H_kv < H runs it with grouped-query
     key/value chunks of H_kv heads.  trace=False times the steps without
     per-launch events (no per-kernel figures then).  concurrent=True walks
@@ -320,7 +395,7 @@ def run_fwd(w, steps, warmup, ring_mode, H_kv=None, trace=True, concurrent=False
         secs, rec = untraced_steps(step_concurrent, steps, warmup, clock), []
         trace = False
     elif trace:
-        secs, rec = timed_steps(step, n_launch, steps, warmup, clock)
+        secs, rec = timed_steps(step, n_launch, steps, warmup, clock, sampler)
     else:
         secs, rec = untraced_steps(step, steps, warmup, clock), []
     flops = fwd_flops(w)
@@ -781,7 +856,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     w = WORKLOADS[args.workload]
-    fwd, tensors = run_fwd(w, args.steps, args.warmup, args.ring_mode)
+    sampler = ClockSampler()
+    fwd, tensors = run_fwd(w, args.steps, args.warmup, args.ring_mode, sampler=sampler)
+    sclk = sampler.summary()
     print(f"[bench] fwd {w.name}: {fwd['ms_per_step']:.3f} ms/step, {fwd['tflops']:.1f} TFLOP/s", file=sys.stderr,
           flush=True)
 
@@ -818,6 +895,12 @@ def main():
         "kernel": (f"fwd_walk_kernel (fused walk), {dk['launches']} launches, {dk['avg_ms']} ms per step"
                    if dom == "fwd_walk" else f"{full_kernel} ({dom}), {dk['launches']} launches, avg {dk['avg_ms']} ms"),
         "flops_per_launch": dom_flops,  # fused walk: per step (all its launches)
+        # The engine clock the driver reported during the timed steps, and
+        # `achieved` over the peak at that clock (CUs x 4096 flop per clock;
+        # the median sample, which the full-chunk launches dominate).
+        "engine_clock_sampled": sclk,
+        "frac_of_peak_at_sampled_clock": (None if not sclk else
+                                          round(achieved / (cus * 4096 * sclk["median_mhz"] * 1e6 / 1e12), 4)),
     }
 
     out = {

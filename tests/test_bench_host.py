@@ -53,6 +53,14 @@ def test_counter_ingestion(tmp_path):
     assert json.loads(out.read_text()) == rec
 
 
+def test_engine_clock_parse():
+    """The sampled engine clock is the level marked '*' in pp_dpm_sclk."""
+    assert bench.ClockSampler.parse("0: 500Mhz\n1: 1652Mhz *\n2: 2400Mhz\n") == 1652.0
+    assert bench.ClockSampler.parse("0: 500Mhz *\n1: 2400Mhz\n") == 500.0
+    assert bench.ClockSampler.parse("0: 500Mhz\n1: 2400Mhz\n") is None
+    assert bench.ClockSampler.parse("") is None
+
+
 def test_queue_rule():
     """bench.py names the kernel of the full-chunk launches by the library's
     rule for persistent steps: the double-buffer walk with at least four
