@@ -473,13 +473,17 @@ def run_train(w, steps, warmup, H_kv=None):
         ra.ring_bwd(q, ks, vs, o, lse, do, dq, dk, dv, r, w.causal, w.scale, workspace=ws_b)
 
     clock = StepClock(steps)
-    secs, rec = timed_steps(step, n_launch, steps, warmup, clock)
+    sampler = ClockSampler()
+    secs, rec = timed_steps(step, n_launch, steps, warmup, clock, sampler)
+    sclk = sampler.summary()
+    cus, _ = ra.device_info()
     fl_f, fl_b = fwd_flops(w), bwd_flops(w)
     kf = {"fwd_diag": 4 * d, "fwd_full": 4 * d, "bwd_dq_diag": 6 * d, "bwd_dq_full": 6 * d,
           "bwd_dkdv_diag": 8 * d, "bwd_dkdv_full": 8 * d}
     ks_ = kernel_stats(rec, w, lambda k: kf.get(k, 0))
     fwd_ms = sum(m for k, m in rec if k.startswith("fwd")) / steps
     bwd_ms = sum(m for k, m in rec if k.startswith("bwd")) / steps
+    bwd_mm_ms = sum(m for k, m in rec if k.startswith(("bwd_dq", "bwd_dkdv"))) / steps
     return {
         "workload": w.name, "steps": steps, "ms_per_step": secs / steps * 1e3,
         "ms_per_step_median": round(clock.median_ms(), 4),
@@ -488,6 +492,15 @@ def run_train(w, steps, warmup, H_kv=None):
         "fwd_kernels_ms_per_step": round(fwd_ms, 3), "bwd_kernels_ms_per_step": round(bwd_ms, 3),
         "fwd_tflops_kernels": round(fl_f / (fwd_ms * 1e-3) / 1e12, 1),
         "bwd_tflops_kernels_algorithmic": round(fl_b / (bwd_ms * 1e-3) / 1e12, 1),
+        # The dQ and dK/dV kernels execute 14 d flop per pair (6 d + 8 d) for
+        # the 10 d of the gradient: their executed rate, and that rate over the
+        # peak at the engine clock the driver reported during the timed steps
+        # (forward and backward together).
+        "bwd_tflops_matmul_kernels_executed": round(1.4 * fl_b / (bwd_mm_ms * 1e-3) / 1e12, 1),
+        "engine_clock_sampled": sclk,
+        "bwd_executed_frac_of_peak_at_sampled_clock": (
+            None if not sclk else
+            round(1.4 * fl_b / (bwd_mm_ms * 1e-3) / (cus * 4096 * sclk["median_mhz"] * 1e6), 4)),
         "kernels": ks_,
     }
 
