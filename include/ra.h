@@ -132,7 +132,7 @@ int ra_lse_merge(float* o, float* lse, const float* o_partial,
  * Device workspace bytes ra_ring_fwd (bwd == 0) or ra_ring_bwd (bwd != 0)
  * needs for these sizes.  Double-buffer forward: two slots of one K and one
  * V chunk, 4 * B*H*C*d * 2 bytes, then 1024 bytes of work-queue counters.
- * Resident forward: 0.  Backward: two fp32 values per row, rowsum(dO * O)
+ * Resident forward: 0.  Backward: two fp32 values per row, -rowsum(dO * O)
  * and lse * log2(e), 2 * B*H*C * 4 bytes.  Returns 0 for invalid sizes.
  */
 size_t ra_ring_workspace_bytes(int P, int B, int H, int C, int d,
@@ -245,7 +245,7 @@ int ra_ring_bwd_gqa(const void* q, const void* const* k_chunks,
  * device memory: code under HIP graph capture, tight serving loops, or
  * harnesses that forbid hipMalloc.  Same arguments, results and contracts as
  * ra_ring_bwd_gqa (H_kv == H for multi-head attention), minus the workspace:
- * the row terms the backward needs (rowsum(dO * o) and lse in base 2, two
+ * the row terms the backward needs (-rowsum(dO * o) and lse in base 2, two
  * floats per query row) live in a static device array of the library,
  * sized for RA_NOALLOC_MAX_ROWS query rows (16 MiB), of which each device
  * keeps its own copy until the process ends.  The call allocates and frees

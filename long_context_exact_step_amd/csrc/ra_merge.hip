@@ -52,8 +52,10 @@ __global__ __launch_bounds__(kRowThreads) void lse_merge_kernel(float* __restric
   }
 }
 
-// D[row] = sum_d dO[row, d] * O[row, d]; 32 lanes per row (D = 128: 4 values
-// per lane; D = 64: 2), butterfly sum over the 32 lanes.  Also the row's lse
+// out[row] = -D[row], D[row] = sum_d dO[row, d] * O[row, d]; 32 lanes per row
+// (D = 128: 4 values per lane; D = 64: 2), butterfly sum over the 32 lanes.
+// The key kernel starts its dP accumulators at -D, which yields dP - D with
+// no vector work; the dq kernel negates it back.  Also the row's lse
 // in base 2, lse * log2(e), with -inf (a row that saw no key) mapped to +inf
 // so that exp2(s - lse2) is 0 for it.
 template <int D>
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(kRowThreads) void rowdot_kernel(const uint16_t* __r
 #pragma unroll
     for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
     if (ok && c == 0) {
-      out[row] = acc;
+      out[row] = -acc;
       const float l2 = lse[row] * kLog2e;
       lse2[row] = (l2 == -__builtin_inff()) ? __builtin_inff() : l2;
     }
