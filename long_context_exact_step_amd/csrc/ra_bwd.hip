@@ -425,8 +425,11 @@ struct KvReads {
 static_assert(KvReads{8, kKvLookahead<128>, 2}.valid() && KvReads{4, kKvLookahead<64>, 1}.valid(),
               "key kernel read schedule");
 
-// dv^T += dO^T P and dk^T += scale Q^T dS for one ring step in one launch,
-// with one wave per SIMD.  A block holds 128 keys, 32 per wave; a wave keeps
+// dv^T += dO^T P and dk^T += scale Q^T dS for one ring step in one launch.
+// A block holds 128 keys, 32 per wave, 4 waves; at d = 128 a block takes a
+// CU (one wave per SIMD: a wave's state needs 428 registers), at d = 64 two
+// blocks share one (246 registers, 66 KB of LDS each), so that one wave's
+// vector work runs beside the other's MFMAs.  A wave keeps
 // its keys' K and V rows (the B operands of S = Q K^T and dP = dO V^T) and
 // the dk^T and dv^T accumulators in AGPRs.  It walks the chunk's queries in
 // units of 32 (half a 64-query LDS tile).  Step u, one unit's worth of
@@ -446,7 +449,7 @@ static_assert(KvReads{8, kKvLookahead<128>, 2}.valid() && KvReads{4, kKvLookahea
 // tile, and the tile loop is unrolled four times so that every LDS offset is
 // an immediate.
 template <int D, bool DIAG>
-__global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_kernel(
+__global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1))) void bwd_kv_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
     const uint16_t* __restrict__ dog, const float* __restrict__ lse2g, const float* __restrict__ Dg,
     float* __restrict__ dkg, float* __restrict__ dvg, int Sq, int Sk, int n_ktiles, int total_tiles,
