@@ -320,7 +320,11 @@ def _bwd_case(P, C, d, causal, rank, B=1, H=2, wid=105):
 @pytest.mark.parametrize("P,C,d,causal", [(3, 100, 128, True), (2, 129, 64, True), (3, 64, 128, False),
                                           (1, 200, 128, True),
                                           # several 256-row blocks and 64-row tiles, ragged tails
-                                          (2, 600, 128, True), (2, 300, 64, True), (2, 520, 128, False)])
+                                          (2, 600, 128, True), (2, 300, 64, True), (2, 520, 128, False),
+                                          # chunks shorter than a 32-query unit or a 32-key wave: one
+                                          # tile, most units and keys masked or absent
+                                          (3, 1, 128, True), (3, 1, 64, False), (2, 5, 64, True),
+                                          (3, 31, 128, True), (2, 33, 64, False), (4, 17, 128, True)])
 def test_ring_bwd_matches_oracle(P, C, d, causal):
     for rank in range(P):
         print(f"ring_bwd P={P} C={C} d={d} causal={causal} rank={rank}", flush=True)
