@@ -289,10 +289,10 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dk/dv kernel, one wave per SIMD: each wave holds 32 keys and all of their
-// work.
+// dk/dv kernel: each wave holds 32 keys and all of their work (one wave per
+// SIMD at d = 128, two at d = 64).
 // ---------------------------------------------------------------------------
-constexpr int kKvWaves = 4;      // one per SIMD
+constexpr int kKvWaves = 4;  // waves per block, 32 keys each
 // MFMAs whose LDS operands are read ahead: 3 at d = 128 (a step's stream
 // then covers the reads' latency; 2 left it exposed), 2 at d = 64.
 template <int D>
@@ -305,9 +305,9 @@ constexpr int kKvLookahead = D == 128 ? 3 : 2;
 // AGPRs in AGPRs and copies each score out.  Inline assembly carries no
 // hazard tracking, so every use keeps its distance from the instructions
 // that feed it: an accumulator recurs every second MFMA or later, a score is
-// read by the vector unit one step (16 or more MFMAs) after it is written,
-// and the packed P and dS are read by the products one step after they are
-// written.  A result that does not accumulate in place is early-clobber: the
+// read by the vector unit in the next step (two or more MFMAs after it is
+// written) or, by the mask pass, after 20 wait states, and the packed P and
+// dS are read by the products one step after they are written.  A result that does not accumulate in place is early-clobber: the
 // MFMA reads its sources over several passes while it writes, so its
 // destination may overlap none of them.
 __device__ __forceinline__ void mfma_score_first(f32x16& d, const u32x4& a, const u32x4& b) {
