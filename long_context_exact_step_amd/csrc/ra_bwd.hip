@@ -114,11 +114,15 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
       df[s] = (qq < Sq) ? ld16(drow + s * 16 + g * 8) : u32x4{0, 0, 0, 0};
     }
   }
-  float lse2 = kPosInf, Dq = 0.f;
+  float lse2 = kPosInf, nDq = 0.f;
   if (qq < Sq) {
     lse2 = lse2g[(size_t)bh * Sq + qq];  // +inf for a row that saw no key: P = 0
-    Dq = -Dg[(size_t)bh * Sq + qq];  // the row pre-pass stores -D
+    nDq = Dg[(size_t)bh * Sq + qq];      // the row pre-pass stores -D
   }
+  // At d = 64 the dP^T chain starts at the lane's -D, so it yields dP^T - D
+  // and the vector phase saves a subtraction per element (the vector unit
+  // bounds that kernel); at d = 128 the 16 extra registers are not there.
+  constexpr bool kFoldD = D == 64;
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -188,8 +192,16 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
           if constexpr (s == 0) sacc[kb] = mfma32(rq[b], qf[0], f32x16{});
           else sacc[kb] = mfma32(rq[b], qf[s], sacc[kb]);
         } else {
-          if constexpr (s == 0) pacc[kb] = mfma32(rq[b], df[0], f32x16{});
-          else pacc[kb] = mfma32(rq[b], df[s], pacc[kb]);
+          if constexpr (s == 0 && kFoldD) {
+            f32x16 c;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = nDq;
+            pacc[kb] = mfma32(rq[b], df[0], c);
+          } else if constexpr (s == 0) {
+            pacc[kb] = mfma32(rq[b], df[0], f32x16{});
+          } else {
+            pacc[kb] = mfma32(rq[b], df[s], pacc[kb]);
+          }
         }
       }
       hook(mc);
@@ -206,7 +218,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, -lse2));
-        sacc[kb][i] = p * (pacc[kb][i] - Dq);
+        sacc[kb][i] = kFoldD ? p * pacc[kb][i] : p * (pacc[kb][i] + nDq);
       }
     // Masked tiles (the diagonal band, the ragged tail) zero the entries of
     // keys at or past the lane's limit, whatever was computed for them, in a
