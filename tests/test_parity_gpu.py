@@ -537,7 +537,9 @@ def test_ring_fwd_gqa_every_rank(mode):
         assert_close(f64(lse), rl, TOL_LSE, f"lse rank {rank}", rel=None)
 
 
-@pytest.mark.parametrize("P,C,d,H,Hk", [(2, 300, 128, 4, 2), (3, 100, 64, 6, 3), (2, 130, 128, 4, 1)])
+@pytest.mark.parametrize("P,C,d,H,Hk", [(2, 300, 128, 4, 2), (3, 100, 64, 6, 3), (2, 130, 128, 4, 1),
+                                        # several key blocks per head, grouped heads, d = 64
+                                        (2, 600, 64, 8, 2), (2, 520, 128, 8, 2)])
 def test_ring_bwd_gqa_matches_oracle(P, C, d, H, Hk):
     q, k, v, do = ring_tensors(110, 1, H, P, C, d, with_do=True, H_kv=Hk)
     kd, vd = [t.to(dev()) for t in k], [t.to(dev()) for t in v]
